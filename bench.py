@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one whole ``moe_layer_forward`` (align, gate+up+SiLU, down, blend)
+of the decode workload: M=8 tokens, hidden 2048, 128 experts, top-8, expert
+inter 768, BS 16, FP8 e4m3 weights with float32 128x128 block scales, bf16
+activations, softmax top-k routing of N(0,1) logits.  Inputs are resident in
+HBM before the timed region.  Consecutive steps cycle over 4 copies of the
+expert weights and 4 seeded routings, so no step finds its weights in the
+256 MB last-level cache.  Each (copy, routing) pair is one captured HIP graph;
+the timed region replays exactly K graphs, bracketed by device syncs.
+
+Printed (one JSON line): layer rows/s (the value), weight-stream GB/s and its
+fraction of the 8 TB/s HBM peak, per-kernel times from HIP events, the
+roofline of the dominant kernel (gate+up), the align latency on the
+prefill-scale align workload (n = 32768 int64 ids, 256 experts, BS 64), and the
+float64 CPU oracle timed on the host as a reference baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer rows/s + weight-stream HBM GB/s (% of peak) at M=8; align latency us"
+HBM_PEAK_GBPS = 8000.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "grouped_gate_up_decode_pmc.txt")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies / routings cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown-reps", type=int, default=50)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device copy 8 times (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def graph_of(fn, stream):
+    import torch
+
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(graphs, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("grouped.hip",):
+        with open(os.path.join(ROOT, "mixture_experts_routing_align_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(digest):
+    """HBM bytes per gate+up launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    fields = {}
+    for line in open(PROFILE_PMC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_digest") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, routings):
+    """The float64 oracle on the same routings, BLAS limited to one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads
+
+    x = workloads.x_bf16(cfg)
+    needed = sorted({int(e) for ids, _ in routings for e in np.unique(ids)})
+    host = {}
+    for which in ("gate", "up", "down"):
+        for e in needed:
+            host[(which, e)] = workloads.expert_matrix(cfg, which, e)
+    rows = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for ids, w in routings:
+            oracle.moe_layer(x, ids, w, cfg.E, cfg.BS, cfg.wdt, lambda which, e: host[(which, e)])
+            rows += ids.shape[0]
+        dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle moe_layer (align + dequant + SwiGLU FFN + blend) on {len(routings)} "
+                      f"seeded decode routings = {rows} rows, {dt:.2f} s, numpy BLAS limited to 1 thread",
+            "seconds": dt, "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_align_amd as moe
+    import workloads
+    from workloads.device import DeviceWeights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 8}))
+        return
+
+    cfg = workloads.CONFIGS["decode"]
+    G = args.copies
+    log(f"generating decode weights ({cfg.E} experts, FP8) and {G} copies")
+    w0 = DeviceWeights(cfg, device=dev, threads=16)
+    copies = [w0] + [w0.clone() for _ in range(G - 1)]
+    routings = [workloads.routing(cfg.replace(seed=cfg.seed + r)) for r in range(G)]
+    x = workloads.x_bf16(cfg)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids_d = [torch.from_numpy(ids).to(dev) for ids, _ in routings]
+    w_d = [torch.from_numpy(w).to(dev) for _, w in routings]
+    layers = [moe.MoeLayer(c.weight("gate"), c.weight("up"), c.weight("down"), cfg.top_k, cfg.BS) for c in copies]
+    outs = [torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device=dev) for _ in range(G)]
+    wss = [layers[i].alloc_workspace(cfg.M) for i in range(G)]
+    bytes_per = [w0.algorithmic_bytes(ids) for ids, _ in routings]
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream(device=dev)
+    graphs = [graph_of(lambda i=i: layers[i].forward(xt, ids_d[i], w_d[i], out=outs[i], workspace=wss[i]), stream)
+              for i in range(G)]
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    elapsed = time_graphs(graphs, args.steps, args.warmup)
+    ms_per_step = elapsed / args.steps * 1e3
+    rows_per_s = cfg.M * args.steps / elapsed
+    weight_bytes = sum(bytes_per[i % G]["total"] for i in range(args.steps))
+    weight_gbps = weight_bytes / elapsed / 1e9
+
+    # per-kernel durations: the four steps launched one by one, HIP events between them
+    log("per-kernel breakdown")
+    names = ("align", "gate_up", "down", "blend")
+    acc = {k: 0.0 for k in names}
+    gu_bytes = 0.0
+    down_bytes = 0.0
+    count = 0
+    with torch.cuda.stream(stream):
+        for rep in range(args.breakdown_reps):
+            for i in range(G):
+                L = layers[i]
+                v = L.workspace_views(wss[i], cfg.M)
+                tables = moe.AlignTables(**{k: v[k] for k in moe.TABLE_FIELDS})
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                ev[0].record(stream)
+                moe.moe_align(ids_d[i], cfg.E, cfg.BS, tables, stream=stream)
+                ev[1].record(stream)
+                moe.moe_grouped_gate_up_silu(xt, L.gate, L.up, tables, v["act"], cfg.top_k, cfg.BS, stream=stream)
+                ev[2].record(stream)
+                moe.moe_grouped_down(v["act"], L.down, tables, v["expert_out"], cfg.M, cfg.top_k, cfg.BS,
+                                     stream=stream)
+                ev[3].record(stream)
+                moe.moe_blend(outs[i], v["expert_out"], w_d[i], tables.token_to_perm, stream=stream)
+                ev[4].record(stream)
+                ev[4].synchronize()
+                if rep == 0:
+                    continue  # first pass warms up
+                for j, k in enumerate(names):
+                    acc[k] += ev[j].elapsed_time(ev[j + 1]) * 1e3
+                gu_bytes += bytes_per[i]["gate_up"]
+                down_bytes += bytes_per[i]["down"]
+                count += 1
+    kernels_us = {k: acc[k] / count for k in names}
+    gu_gbps = gu_bytes / count / (kernels_us["gate_up"] * 1e-6) / 1e9
+    down_gbps = down_bytes / count / (kernels_us["down"] * 1e-6) / 1e9
+
+    # align latency on the prefill-scale align workload, graph-replayed
+    log("align latency (n=32768, E=256, BS=64)")
+    acfg = workloads.CONFIGS["align"]
+    aids, _ = workloads.routing(acfg)
+    aids_d = torch.from_numpy(aids).to(dev)
+    atab = moe.AlignTables.allocate(acfg.M, acfg.top_k, acfg.E, acfg.BS, dev)
+    ag = graph_of(lambda: moe.moe_align(aids_d, acfg.E, acfg.BS, atab), stream)
+    areps = 200
+    align_s = time_graphs([ag], areps, 20)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(areps):
+            moe.moe_align(aids_d, acfg.E, acfg.BS, atab, stream=stream)
+        ev1.record(stream)
+    ev1.synchronize()
+    align_ev_us = ev0.elapsed_time(ev1) * 1e3 / areps
+    z = torch.zeros(1, device=dev)
+    fg = graph_of(lambda: z.add_(1.0), stream)
+    floor_s = time_graphs([fg], areps, 20)
+
+    # plain streaming-read ceiling measured in the same run (context for % of peak)
+    big = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
+    big.sum()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        big.sum()
+    torch.cuda.synchronize()
+    read_gbps = 5 * big.numel() * 4 / (time.perf_counter() - t0) / 1e9
+    del big
+
+    digest = source_digest()
+    gu_bytes_per_launch = gu_bytes / count
+    traffic = traffic_from_profile(digest)
+    result = {
+        "metric": METRIC,
+        "value": rows_per_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode MoE layer: M=8, hidden 2048, 128 experts, top-8, inter 768, BS 16, no shared "
+                        "expert; FP8 e4m3 weights with fp32 128x128 block scales; bf16 activations",
+            "M": cfg.M, "H": cfg.H, "E": cfg.E, "top_k": cfg.top_k, "I": cfg.I, "BS": cfg.BS,
+            "weights": "fp8_e4m3 + fp32 128x128 scales (bf16 MFMA, fp32 accumulate)",
+            "weight_copies": G, "routings": G, "replay": "one HIP graph per (copy, routing), K replays",
+        },
+        "weight_gbps": weight_gbps,
+        "weight_frac_of_peak": weight_gbps / HBM_PEAK_GBPS,
+        "active_experts_mean": float(np.mean([b["active"] for b in bytes_per])),
+        "weight_bytes_per_step_mean": float(np.mean([b["total"] for b in bytes_per])),
+        "kernels_us": kernels_us,
+        "kernel_gbps": {"gate_up": gu_gbps, "down": down_gbps},
+        "roofline": {
+            "kernel": "grouped_kernel<fp8, gate_up> (moe_grouped_gate_up_silu)",
+            "bound": "hbm",
+            "achieved": gu_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": gu_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": gu_bytes_per_launch,
+            "source_digest": digest,
+        },
+        "align_us": align_s / areps * 1e6,
+        "align_us_events": align_ev_us,
+        "align_workload": "n = 4096 x 8 int64 ids, Zipf(1.1), 256 experts, BS 64 (graph replay, wall clock)",
+        "launch_floor_us": floor_s / areps * 1e6,
+        "read_ceiling_gbps": read_gbps,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: float64 oracle")
+        result["cpu_baseline"] = cpu_baseline(cfg, routings)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

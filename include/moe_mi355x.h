@@ -1,0 +1,209 @@
+/*
+ * moe_mi355x.h - C ABI of the MI355X (gfx950) MoE routing-align + grouped
+ * expert FFN library (libmoe_mi355x.so).
+ *
+ * The path, restated from the pages that define it:
+ *   1. align  - a deterministic on-device sort of the (token, k) slots by
+ *      expert: per-expert counts, padding to a block size BS, the exclusive
+ *      prefix of the padded counts, a stable within-expert rank, the
+ *      block->expert map, token_to_perm and the ascending active-expert list
+ *      (nbxtensor 0.0.1 wheel page, moe_align.py: module docstring and the
+ *      three stage kernels; metrale fp8_moe_grouped.rs: moe_fp8_grouped_sort
+ *      and Fp8GroupedSortOut);
+ *   2. gate+up with SiLU and 3. down over the sorted slots, one workgroup
+ *      column per active expert, each weight row streamed once for every row
+ *      routed to that expert (fp8_moe_grouped.rs: module doc and the gate+up
+ *      and down launchers);
+ *   4. blend - each token's router-weighted sum of its slots' expert outputs,
+ *      looked up through token_to_perm, in a fixed k order, plus the shared
+ *      expert (fp8_moe_grouped.rs: moe_weighted_sum_blend_fp8_grouped;
+ *      moe_decode_vec.py: moe_part_reduce_kernel's fixed-order sum).
+ *
+ * Conventions for every entry point:
+ *   - All buffers are device memory owned by the caller.  The library never
+ *     allocates, never synchronises and never reads device data on the host,
+ *     so every call can be captured in a HIP graph and replayed for any routing.
+ *   - Work is enqueued on `stream` (0 = the null stream) in call order.
+ *   - Host-side argument checks come first: on failure the call returns a
+ *     negative moe_status, records a message for moe_last_error() and
+ *     launches nothing.  MOE_ERR_HIP reports a failed kernel launch.
+ *   - M == 0 returns MOE_OK and launches nothing.
+ *   - Slot ids outside [0, E) are dropped on the device: they are in no count
+ *     or table, get token_to_perm = -1 and add nothing to the blend (the
+ *     stage-3 kernel of moe_align.py skips them the same way).
+ *   - Weight matrices are row-major [N, K] per expert (N output rows, K input
+ *     columns) stacked over experts: gate/up [E, I, H], down [E, H, I]; the
+ *     shared expert's are [S, H] and [H, S].  FP8 weights are OCP E4M3
+ *     (e4m3fn) codes with one float32 scale per 128x128 block, row-major
+ *     [E, N/128, K/128] (fp8_moe_grouped.rs, fp8_grouped_tc_shape_ok: FP8
+ *     projections come in whole 128 blocks, the scale blocks).  BF16 weights
+ *     take no scale.
+ *   - Activations x are bf16 [M, H]; intermediates are float32; the output is
+ *     bf16 [M, H], one round-to-nearest-even of the float32 blend sum.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  MOE_ERR_SHAPE = -2,     /* a size is negative, zero where it must not be, or
+                             not a whole number of the blocks the kernels need   */
+  MOE_ERR_LIMIT = -3,     /* E > MOE_MAX_EXPERTS, or a table would need >= 2^31
+                             entries                                             */
+  MOE_ERR_WORKSPACE = -4, /* workspace smaller than moe_layer_workspace_bytes()  */
+  MOE_ERR_HIP = -5        /* the HIP runtime reported a launch failure           */
+} moe_status;
+
+typedef enum { MOE_IDX_I32 = 0, MOE_IDX_I64 = 1 } moe_index_dtype;
+typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1 } moe_weight_dtype;
+
+/* Experts one align launch handles (fp8_moe_grouped.rs: the one-launch sort's
+ * 1024-expert limit, FP8_GROUPED_SORT_MAX_EXPERTS). */
+#define MOE_MAX_EXPERTS 1024
+
+/* ---------------------------------------------------------------- sizing --
+ * Pure host functions; no GPU needed.                                       */
+
+/* Worst-case length of sorted_token_ids for n = M*top_k slots:
+ * min(n*BS, n + E*(BS-1)) rounded up to a multiple of BS (moe_align.py,
+ * module docstring).  block_expert_ids has moe_align_max_total(...)/BS
+ * entries.  Returns -1 for a negative n or a non-positive E or BS. */
+int64_t moe_align_max_total(int64_t n, int32_t E, int32_t BS);
+
+/* Length of active_experts: min(n, E), the most distinct experts n slots can
+ * reach; it does not depend on the routing (fp8_moe_grouped.rs,
+ * fp8_grouped_active_cap).  Returns -1 for a negative n or E. */
+int32_t moe_active_cap(int64_t n, int32_t E);
+
+/* Text of the last failure on the calling thread ("" if none).  The pointer
+ * stays valid until the thread's next failing call. */
+const char* moe_last_error(void);
+
+/* ABI version of this header (increases on any change). */
+int32_t moe_abi_version(void);
+
+/* ------------------------------------------------------------- align -- */
+
+/* Alignment tables; all int32 device arrays allocated by the caller. */
+typedef struct {
+  int32_t* sorted_token_ids; /* [max_total]  flat slot i = t*top_k + k; the
+                                sentinel n = M*top_k at every padding position */
+  int32_t* block_expert_ids; /* [max_total/BS] owning expert of each BS block,
+                                -1 for blocks at or past the total            */
+  int32_t* expert_offsets;   /* [E+1] exclusive prefix of the padded counts;
+                                expert_offsets[E] = total                     */
+  int32_t* expert_counts;    /* [E] in-range slots per expert (unpadded)      */
+  int32_t* token_to_perm;    /* [n] sorted position of slot i, -1 if dropped  */
+  int32_t* active_experts;   /* [cap] experts with a slot, ascending, then -1 */
+  int32_t* active_count;     /* [1] number of active experts                  */
+  int32_t* total;            /* [1] padded total; lives only on the device    */
+} moe_align_tables;
+
+/* Sort the n = M*top_k slots of topk_ids ([M, top_k] row-major, int32 or
+ * int64 per idt) by expert, stably (a slot's rank within its expert is the
+ * number of earlier slots with the same id), with no atomics: the tables are
+ * bit-identical run to run and equal to a host stable sort's.
+ * Errors: MOE_ERR_NULL (topk_ids or a table pointer NULL with M > 0),
+ * MOE_ERR_SHAPE (M < 0, top_k < 1, E < 1, BS < 1), MOE_ERR_LIMIT
+ * (E > MOE_MAX_EXPERTS, n or max_total >= 2^31). */
+int moe_align(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k,
+              int32_t E, int32_t BS, const moe_align_tables* out, hipStream_t stream);
+
+/* ---------------------------------------------------- grouped expert FFN -- */
+
+/* One projection's weights: w is [E, N, K] (bf16 or e4m3fn codes); scale is
+ * [E, N/128, K/128] float32 for FP8 and ignored (may be NULL) for BF16. */
+typedef struct {
+  const void* w;
+  const float* scale;
+} moe_weight;
+
+/* act[p, :] = silu(g) * u with g = W_gate[e] x[t], u = W_up[e] x[t] for every
+ * sorted position p holding a slot of active expert e (t = slot / top_k);
+ * act is float32 [max_total, I], rows indexed by sorted position; padding rows
+ * are not written.  With a shared expert (sh_gate and sh_up non-NULL, S > 0)
+ * the same launch writes sh_act[t, :] (float32 [M, S]) for every token.
+ * `t` are the tables moe_align wrote for the same topk_ids.
+ * Shapes: FP8 needs H, I, S multiples of 128; BF16 needs H multiple of 32 and
+ * I, S multiples of 16.  Errors as for moe_align, plus MOE_ERR_SHAPE for the
+ * block rules above. */
+int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe_weight* gate,
+                             const moe_weight* up, const moe_align_tables* t, float* act,
+                             const moe_weight* sh_gate, const moe_weight* sh_up, float* sh_act,
+                             int64_t M, int32_t H, int32_t I, int32_t S, int32_t E,
+                             int32_t top_k, int32_t BS, hipStream_t stream);
+
+/* expert_out[p, :] = W_down[e] act[p, :] for every slot position p of active
+ * expert e (float32 [max_total, H]; padding rows not written); with a shared
+ * expert (sh_down non-NULL, S > 0) also sh_out[t, :] = W_sh_down sh_act[t, :]
+ * (float32 [M, H]).  Shapes: FP8 needs H, I, S multiples of 128; BF16 needs
+ * I, S multiples of 32 and H a multiple of 16. */
+int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down,
+                     const moe_align_tables* t, float* expert_out, const moe_weight* sh_down,
+                     const float* sh_act, float* sh_out, int64_t M, int32_t H, int32_t I,
+                     int32_t S, int32_t E, int32_t top_k, int32_t BS, hipStream_t stream);
+
+/* out[t, :] = bf16( (sum over k = 0..top_k-1 in that order of
+ * w[t*top_k+k] * expert_out[token_to_perm[t*top_k+k], :]) + sh_out[t, :] ),
+ * float32 fused multiply-adds, a slot with token_to_perm < 0 skipped, sh_out
+ * NULL for no shared expert; one round-to-nearest-even at the end.  A row's
+ * bits depend only on that token's inputs (not on M).  H must be a multiple
+ * of 4. */
+int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights,
+              const int32_t* token_to_perm, const float* sh_out, int64_t M, int32_t H,
+              int32_t top_k, hipStream_t stream);
+
+/* ------------------------------------------------------------ whole layer -- */
+
+typedef struct {
+  int64_t M;          /* tokens                                       */
+  int32_t H;          /* hidden size                                  */
+  int32_t I;          /* routed expert intermediate size              */
+  int32_t S;          /* shared expert intermediate size (0: none)    */
+  int32_t E;          /* routed experts                               */
+  int32_t top_k;
+  int32_t BS;         /* alignment block size                         */
+  moe_weight_dtype wdt;
+  moe_index_dtype idt;
+  moe_weight gate, up, down;            /* routed experts                  */
+  moe_weight sh_gate, sh_up, sh_down;   /* shared expert (.w NULL if none) */
+} moe_layer_desc;
+
+/* Bytes of workspace moe_layer_forward needs for `d` (tables, act,
+ * expert_out, and the shared expert's sh_act and sh_out), each region
+ * 256-byte aligned.  Depends on the shapes only, never on the routing.
+ * Returns 0 for an invalid descriptor (moe_last_error says why). */
+size_t moe_layer_workspace_bytes(const moe_layer_desc* d);
+
+/* The whole layer on `stream`: align, gate+up+SiLU, down, blend, with no host
+ * synchronisation.  x is bf16 [M, H], topk_ids [M, top_k] (d->idt),
+ * topk_weights float32 [M, top_k], out bf16 [M, H].  The workspace (device,
+ * >= moe_layer_workspace_bytes(d), 256-byte aligned) holds the tables and
+ * intermediates afterwards, laid out as moe_layer_workspace_layout says.
+ * Errors: as for the four steps, plus MOE_ERR_WORKSPACE. */
+int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids,
+                      const float* topk_weights, void* out_bf16, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Byte offsets of the workspace regions moe_layer_forward uses, in this order:
+ * sorted_token_ids, block_expert_ids, expert_offsets, expert_counts,
+ * token_to_perm, active_experts, active_count, total, act, expert_out,
+ * sh_act, sh_out (the last two are 0 without a shared expert); offsets[12] is
+ * the total size.  Returns MOE_OK or an error for an invalid descriptor. */
+int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[13]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

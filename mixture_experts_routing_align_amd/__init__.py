@@ -1,0 +1,292 @@
+"""MI355X (gfx950) MoE routing-align + grouped expert FFN.
+
+Thin Python binding of ``libmoe_mi355x.so`` (C ABI in ``include/moe_mi355x.h``).
+Every function here only marshals arguments: torch tensors supply device
+memory and the current HIP stream, and each step runs in the library's HIP
+kernels.  There is no fallback: if the library is not built, importing the
+binding's entry points raises.
+
+Entry points (same names as the C ABI): ``moe_align``,
+``moe_grouped_gate_up_silu``, ``moe_grouped_down``, ``moe_blend``,
+``moe_layer_forward`` (via :class:`MoeLayer`), ``moe_layer_workspace_bytes``,
+``moe_align_max_total``, ``moe_active_cap``.
+
+Weights are passed as ``(w, scale)`` pairs: ``w`` is ``[E, N, K]`` (one expert:
+``[N, K]``) ``torch.uint8`` e4m3fn codes with ``scale`` float32
+``[E, N/128, K/128]``, or ``torch.bfloat16`` with ``scale`` None.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import _ffi
+from ._ffi import (  # noqa: F401
+    MOE_ERR_HIP,
+    MOE_ERR_LIMIT,
+    MOE_ERR_NULL,
+    MOE_ERR_SHAPE,
+    MOE_ERR_WORKSPACE,
+    MOE_IDX_I32,
+    MOE_IDX_I64,
+    MOE_MAX_EXPERTS,
+    MOE_OK,
+    MOE_W_BF16,
+    MOE_W_FP8_E4M3,
+    TABLE_FIELDS,
+    MoeAlignTables,
+    MoeLayerDesc,
+    MoeWeight,
+)
+
+Weight = Tuple[torch.Tensor, Optional[torch.Tensor]]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def lib():
+    return _ffi.load()
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+# ------------------------------------------------------------------ sizing --
+
+def moe_align_max_total(n: int, E: int, BS: int) -> int:
+    return int(lib().moe_align_max_total(n, E, BS))
+
+
+def moe_active_cap(n: int, E: int) -> int:
+    return int(lib().moe_active_cap(n, E))
+
+
+# ------------------------------------------------------------------- align --
+
+@dataclass
+class AlignTables:
+    sorted_token_ids: torch.Tensor
+    block_expert_ids: torch.Tensor
+    expert_offsets: torch.Tensor
+    expert_counts: torch.Tensor
+    token_to_perm: torch.Tensor
+    active_experts: torch.Tensor
+    active_count: torch.Tensor
+    total: torch.Tensor
+
+    @classmethod
+    def allocate(cls, M: int, top_k: int, E: int, BS: int, device="cuda") -> "AlignTables":
+        n = M * top_k
+        mt = moe_align_max_total(n, E, BS)
+        cap = moe_active_cap(n, E)
+        _need(mt >= 0 and cap >= 0, "invalid alignment shape")
+
+        def mk(k):
+            return torch.empty(k, dtype=torch.int32, device=device)
+
+        return cls(mk(mt), mk(mt // BS), mk(E + 1), mk(E), mk(n), mk(cap), mk(1), mk(1))
+
+    def as_c(self) -> MoeAlignTables:
+        return MoeAlignTables(*[getattr(self, f).data_ptr() for f in TABLE_FIELDS])
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, BS: int, tables: Optional[AlignTables] = None,
+              stream=None) -> AlignTables:
+    """Align the [M, top_k] ids (int32 or int64, device); returns the tables."""
+    _need(topk_ids.dim() == 2 and topk_ids.is_contiguous(), "topk_ids must be a contiguous [M, top_k] tensor")
+    _need(topk_ids.dtype in (torch.int32, torch.int64), "topk_ids must be int32 or int64")
+    M, top_k = topk_ids.shape
+    if tables is None:
+        tables = AlignTables.allocate(M, top_k, E, BS, topk_ids.device)
+    idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
+    c = tables.as_c()
+    _check(lib().moe_align(topk_ids.data_ptr(), idt, M, top_k, E, BS, ctypes.byref(c), _stream(stream)))
+    return tables
+
+
+# ------------------------------------------------------------ grouped FFN --
+
+def weight_dtype(w: torch.Tensor) -> int:
+    if w.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MOE_W_FP8_E4M3
+    if w.dtype == torch.bfloat16:
+        return MOE_W_BF16
+    raise ValueError(f"unsupported weight dtype {w.dtype}")
+
+
+def _weight(wt: Optional[Weight]) -> Optional[MoeWeight]:
+    if wt is None:
+        return None
+    w, s = wt
+    _need(w.is_contiguous() and (s is None or s.is_contiguous()), "weights must be contiguous")
+    if weight_dtype(w) == MOE_W_FP8_E4M3:
+        _need(s is not None and s.dtype == torch.float32, "FP8 weights need float32 block scales")
+    return MoeWeight(w.data_ptr(), _ptr(s))
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+def moe_grouped_gate_up_silu(x: torch.Tensor, gate: Weight, up: Weight, tables: AlignTables, act: torch.Tensor,
+                             top_k: int, BS: int, sh_gate: Optional[Weight] = None, sh_up: Optional[Weight] = None,
+                             sh_act: Optional[torch.Tensor] = None, stream=None) -> None:
+    """act[p] = silu(Wg x) * (Wu x) per sorted slot position (+ the shared expert into sh_act)."""
+    M, H = x.shape
+    E, I, H2 = gate[0].shape
+    _need(H2 == H and x.dtype == torch.bfloat16, "x must be bf16 [M, H] matching the weights")
+    _need(act.dtype == torch.float32 and act.shape[1] == I, "act must be float32 [max_total, I]")
+    S = 0 if sh_gate is None else sh_gate[0].shape[0]
+    c = tables.as_c()
+    wdt = weight_dtype(gate[0])
+    _check(lib().moe_grouped_gate_up_silu(
+        x.data_ptr(), wdt, ctypes.byref(_weight(gate)), ctypes.byref(_weight(up)), ctypes.byref(c),
+        act.data_ptr(), _ref(_weight(sh_gate)), _ref(_weight(sh_up)), _ptr(sh_act),
+        M, H, I, S, E, top_k, BS, _stream(stream)))
+
+
+def moe_grouped_down(act: torch.Tensor, down: Weight, tables: AlignTables, expert_out: torch.Tensor, M: int,
+                     top_k: int, BS: int, sh_down: Optional[Weight] = None, sh_act: Optional[torch.Tensor] = None,
+                     sh_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """expert_out[p] = Wd act[p] per sorted slot position (+ the shared expert into sh_out)."""
+    E, H, I = down[0].shape
+    _need(act.dtype == torch.float32 and act.shape[1] == I, "act must be float32 [max_total, I]")
+    _need(expert_out.dtype == torch.float32 and expert_out.shape[1] == H, "expert_out must be float32 [max_total, H]")
+    S = 0 if sh_down is None else sh_down[0].shape[1]
+    c = tables.as_c()
+    _check(lib().moe_grouped_down(
+        act.data_ptr(), weight_dtype(down[0]), ctypes.byref(_weight(down)), ctypes.byref(c),
+        expert_out.data_ptr(), _ref(_weight(sh_down)), _ptr(sh_act), _ptr(sh_out),
+        M, H, I, S, E, top_k, BS, _stream(stream)))
+
+
+def moe_blend(out: torch.Tensor, expert_out: torch.Tensor, topk_weights: torch.Tensor, token_to_perm: torch.Tensor,
+              sh_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[t] = bf16(sum_k w[t,k] expert_out[token_to_perm[t*top_k+k]] + sh_out[t])."""
+    M, top_k = topk_weights.shape
+    H = out.shape[1]
+    _need(out.dtype == torch.bfloat16 and out.shape[0] == M, "out must be bf16 [M, H]")
+    _need(topk_weights.dtype == torch.float32 and topk_weights.is_contiguous(), "topk_weights must be float32")
+    _need(token_to_perm.dtype == torch.int32, "token_to_perm must be int32")
+    _check(lib().moe_blend(out.data_ptr(), expert_out.data_ptr(), topk_weights.data_ptr(), token_to_perm.data_ptr(),
+                           _ptr(sh_out), M, H, top_k, _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------- whole layer --
+
+WORKSPACE_REGIONS = TABLE_FIELDS + ("act", "expert_out", "sh_act", "sh_out")
+
+
+class MoeLayer:
+    """Expert weights of one MoE layer plus the fused ``moe_layer_forward`` call."""
+
+    def __init__(self, gate: Weight, up: Weight, down: Weight, top_k: int, BS: int,
+                 sh_gate: Optional[Weight] = None, sh_up: Optional[Weight] = None, sh_down: Optional[Weight] = None):
+        self.gate, self.up, self.down = gate, up, down
+        self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
+        self.top_k, self.BS = top_k, BS
+        self.E, self.I, self.H = gate[0].shape
+        self.S = 0 if sh_gate is None else sh_gate[0].shape[0]
+        self.wdt = weight_dtype(gate[0])
+        self._keep = None
+
+    def desc(self, M: int, idt: int = MOE_IDX_I64) -> MoeLayerDesc:
+        none = MoeWeight(None, None)
+        d = MoeLayerDesc(M, self.H, self.I, self.S, self.E, self.top_k, self.BS, self.wdt, idt,
+                         _weight(self.gate), _weight(self.up), _weight(self.down),
+                         _weight(self.sh_gate) or none, _weight(self.sh_up) or none, _weight(self.sh_down) or none)
+        return d
+
+    def workspace_bytes(self, M: int, idt: int = MOE_IDX_I64) -> int:
+        d = self.desc(M, idt)
+        n = int(lib().moe_layer_workspace_bytes(ctypes.byref(d)))
+        if n == 0:
+            raise MoeError(MOE_ERR_SHAPE, lib().moe_last_error().decode())
+        return n
+
+    def workspace_layout(self, M: int, idt: int = MOE_IDX_I64):
+        d = self.desc(M, idt)
+        off = (ctypes.c_size_t * 13)()
+        _check(lib().moe_layer_workspace_layout(ctypes.byref(d), off))
+        return list(off)
+
+    def alloc_workspace(self, M: int, idt: int = MOE_IDX_I64, device="cuda") -> torch.Tensor:
+        return torch.empty(self.workspace_bytes(M, idt), dtype=torch.uint8, device=device)
+
+    def workspace_views(self, ws: torch.Tensor, M: int, idt: int = MOE_IDX_I64) -> dict:
+        """Typed views of the tables and intermediates inside a used workspace."""
+        off = self.workspace_layout(M, idt)
+        n = M * self.top_k
+        mt = moe_align_max_total(n, self.E, self.BS)
+        sizes = {
+            "sorted_token_ids": (mt,), "block_expert_ids": (mt // self.BS,), "expert_offsets": (self.E + 1,),
+            "expert_counts": (self.E,), "token_to_perm": (n,), "active_experts": (moe_active_cap(n, self.E),),
+            "active_count": (1,), "total": (1,), "act": (mt, self.I), "expert_out": (mt, self.H),
+            "sh_act": (M, self.S), "sh_out": (M, self.H),
+        }
+        views = {}
+        for i, name in enumerate(WORKSPACE_REGIONS):
+            if name.startswith("sh_") and self.S == 0:
+                continue
+            shape = sizes[name]
+            dt = torch.int32 if i < 8 else torch.float32
+            numel = 1
+            for s in shape:
+                numel *= s
+            views[name] = ws[off[i]:off[i] + 4 * numel].view(dt).view(*shape)
+        return views
+
+    def forward(self, x: torch.Tensor, topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+        """moe_layer_forward: align, gate+up+SiLU, down, blend on one stream, no host sync."""
+        M = x.shape[0]
+        _need(x.dtype == torch.bfloat16 and x.shape[1] == self.H and x.is_contiguous(), "x must be bf16 [M, H]")
+        _need(topk_ids.shape == (M, self.top_k) and topk_ids.is_contiguous(), "topk_ids must be [M, top_k]")
+        _need(topk_weights.shape == (M, self.top_k) and topk_weights.dtype == torch.float32
+              and topk_weights.is_contiguous(), "topk_weights must be float32 [M, top_k]")
+        idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
+        if out is None:
+            out = torch.empty(M, self.H, dtype=torch.bfloat16, device=x.device)
+        if workspace is None:
+            workspace = self.alloc_workspace(M, idt, x.device)
+        d = self.desc(M, idt)
+        _check(lib().moe_layer_forward(ctypes.byref(d), x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(),
+                                       out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+        return out
+
+
+def moe_layer_workspace_bytes(layer: MoeLayer, M: int, idt: int = MOE_IDX_I64) -> int:
+    return layer.workspace_bytes(M, idt)
+
+
+def moe_layer_forward(layer: MoeLayer, x, topk_ids, topk_weights, out=None, workspace=None, stream=None):
+    return layer.forward(x, topk_ids, topk_weights, out, workspace, stream)

@@ -1,0 +1,356 @@
+// C ABI of libmoe_mi355x.so: argument checks, workspace layout, and the launch
+// order of the layer.  See include/moe_mi355x.h for the contract of each call.
+//
+// Every entry point checks all host arguments before touching the HIP runtime,
+// so a refused call launches nothing (the layer forward of metrale
+// forward_nvfp4_grouped_decode.rs launches nothing when its admission predicate
+// fails; the one-launch sort of fp8_moe_grouped.rs refuses more than 1024
+// experts).  Nothing here allocates, synchronises or reads device memory.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "moe_internal.h"
+#include "moe_mi355x.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kInt32Limit = (int64_t)1 << 31;
+
+struct AlignShape {
+  int64_t n = 0, max_total = 0;
+  int32_t cap = 0;
+};
+
+// Shape rules shared by every call that takes (M, top_k, E, BS).
+int check_routing_shape(const char* fn, int64_t M, int32_t top_k, int32_t E, int32_t BS, AlignShape* s) {
+  if (M < 0) return fail(MOE_ERR_SHAPE, "%s: M=%lld is negative", fn, (long long)M);
+  if (top_k < 1) return fail(MOE_ERR_SHAPE, "%s: top_k=%d must be >= 1", fn, top_k);
+  if (E < 1) return fail(MOE_ERR_SHAPE, "%s: E=%d must be >= 1", fn, E);
+  if (BS < 1) return fail(MOE_ERR_SHAPE, "%s: BS=%d must be >= 1", fn, BS);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_LIMIT, "%s: E=%d exceeds the %d experts one align launch handles", fn, E,
+                MOE_MAX_EXPERTS);
+  if (M >= kInt32Limit / top_k)
+    return fail(MOE_ERR_LIMIT, "%s: M*top_k = %lld*%d slots reach 2^31", fn, (long long)M, top_k);
+  s->n = M * top_k;
+  s->max_total = moe_align_max_total(s->n, E, BS);
+  if (s->max_total >= kInt32Limit)
+    return fail(MOE_ERR_LIMIT, "%s: worst-case table length %lld reaches 2^31", fn, (long long)s->max_total);
+  s->cap = moe_active_cap(s->n, E);
+  return MOE_OK;
+}
+
+int check_tables(const char* fn, const moe_align_tables* t, bool all) {
+  if (t == nullptr) return fail(MOE_ERR_NULL, "%s: tables pointer is NULL", fn);
+  if (!t->sorted_token_ids || !t->expert_offsets || !t->expert_counts || !t->active_experts ||
+      !t->active_count)
+    return fail(MOE_ERR_NULL, "%s: a required table pointer is NULL", fn);
+  if (all && (!t->block_expert_ids || !t->token_to_perm || !t->total))
+    return fail(MOE_ERR_NULL, "%s: a table pointer is NULL", fn);
+  return MOE_OK;
+}
+
+int check_weight(const char* fn, const char* name, const moe_weight* w, moe_weight_dtype wdt) {
+  if (w == nullptr || w->w == nullptr) return fail(MOE_ERR_NULL, "%s: %s weights are NULL", fn, name);
+  if (wdt == MOE_W_FP8_E4M3 && w->scale == nullptr)
+    return fail(MOE_ERR_NULL, "%s: %s FP8 block scales are NULL", fn, name);
+  return MOE_OK;
+}
+
+int check_wdt(const char* fn, moe_weight_dtype wdt) {
+  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3)
+    return fail(MOE_ERR_SHAPE, "%s: unknown weight dtype %d", fn, (int)wdt);
+  return MOE_OK;
+}
+
+// A projection with N output rows and depth K: FP8 needs whole 128x128 scale
+// blocks; BF16 needs K in whole 32-deep MFMA steps and N in whole 16-row tiles.
+int check_projection(const char* fn, const char* name, moe_weight_dtype wdt, int32_t N, int32_t K) {
+  if (N < 1 || K < 1) return fail(MOE_ERR_SHAPE, "%s: %s is %dx%d", fn, name, N, K);
+  if (wdt == MOE_W_FP8_E4M3) {
+    if (N % moe::kFp8Block || K % moe::kFp8Block)
+      return fail(MOE_ERR_SHAPE, "%s: FP8 %s is %dx%d, not whole 128x128 scale blocks", fn, name, N, K);
+  } else if (N % 16 || K % 32) {
+    return fail(MOE_ERR_SHAPE, "%s: BF16 %s is %dx%d; needs N %% 16 == 0 and K %% 32 == 0", fn, name, N, K);
+  }
+  return MOE_OK;
+}
+
+moe::AlignOut to_align_out(const moe_align_tables& t) {
+  return moe::AlignOut{t.sorted_token_ids, t.block_expert_ids, t.expert_offsets, t.expert_counts,
+                       t.token_to_perm,    t.active_experts,   t.active_count,   t.total};
+}
+
+void fill_tables(moe::GroupedArgs& a, const moe_align_tables* t) {
+  a.sorted_token_ids = t->sorted_token_ids;
+  a.expert_offsets = t->expert_offsets;
+  a.expert_counts = t->expert_counts;
+  a.active_experts = t->active_experts;
+  a.active_count = t->active_count;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int layout(const moe_layer_desc* d, size_t off[13]) {
+  const char* fn = "moe_layer_workspace";
+  if (d == nullptr) return fail(MOE_ERR_NULL, "%s: descriptor is NULL", fn);
+  AlignShape s;
+  int rc = check_routing_shape(fn, d->M, d->top_k, d->E, d->BS, &s);
+  if (rc) return rc;
+  if ((rc = check_wdt(fn, d->wdt))) return rc;
+  if (d->idt != MOE_IDX_I32 && d->idt != MOE_IDX_I64)
+    return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)d->idt);
+  if (d->S < 0) return fail(MOE_ERR_SHAPE, "%s: S=%d is negative", fn, d->S);
+  if ((rc = check_projection(fn, "gate/up", d->wdt, d->I, d->H))) return rc;
+  if ((rc = check_projection(fn, "down", d->wdt, d->H, d->I))) return rc;
+  if (d->S > 0) {
+    if ((rc = check_projection(fn, "shared gate/up", d->wdt, d->S, d->H))) return rc;
+    if ((rc = check_projection(fn, "shared down", d->wdt, d->H, d->S))) return rc;
+  }
+  const size_t mt = (size_t)s.max_total, n = (size_t)s.n, M = (size_t)d->M;
+  size_t cur = 0;
+  auto take = [&](int i, size_t bytes) {
+    off[i] = cur;
+    cur = align256(cur + bytes);
+  };
+  take(0, mt * 4);                            // sorted_token_ids
+  take(1, (mt / d->BS) * 4);                  // block_expert_ids
+  take(2, ((size_t)d->E + 1) * 4);            // expert_offsets
+  take(3, (size_t)d->E * 4);                  // expert_counts
+  take(4, n * 4);                             // token_to_perm
+  take(5, (size_t)s.cap * 4);                 // active_experts
+  take(6, 4);                                 // active_count
+  take(7, 4);                                 // total
+  take(8, mt * (size_t)d->I * 4);             // act
+  take(9, mt * (size_t)d->H * 4);             // expert_out
+  if (d->S > 0) {
+    take(10, M * (size_t)d->S * 4);           // sh_act
+    take(11, M * (size_t)d->H * 4);           // sh_out
+  } else {
+    off[10] = off[11] = 0;
+  }
+  off[12] = cur;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return 1; }
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int64_t moe_align_max_total(int64_t n, int32_t E, int32_t BS) {
+  if (n < 0 || E < 1 || BS < 1) return -1;
+  const int64_t bound = std::min(n * (int64_t)BS, n + (int64_t)E * (BS - 1));
+  return (bound + BS - 1) / BS * BS;
+}
+
+int32_t moe_active_cap(int64_t n, int32_t E) {
+  if (n < 0 || E < 0) return -1;
+  return (int32_t)std::min<int64_t>(n, E);
+}
+
+int moe_align(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k, int32_t E, int32_t BS,
+              const moe_align_tables* out, hipStream_t stream) {
+  const char* fn = "moe_align";
+  AlignShape s;
+  int rc = check_routing_shape(fn, M, top_k, E, BS, &s);
+  if (rc) return rc;
+  if (idt != MOE_IDX_I32 && idt != MOE_IDX_I64)
+    return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)idt);
+  if (M == 0) return MOE_OK;
+  if (topk_ids == nullptr) return fail(MOE_ERR_NULL, "%s: topk_ids is NULL", fn);
+  if ((rc = check_tables(fn, out, true))) return rc;
+  return hip_status(moe::launch_align(topk_ids, idt == MOE_IDX_I64, (int)s.n, E, BS, (int)s.max_total,
+                                      s.cap, to_align_out(*out), stream),
+                    fn);
+}
+
+int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe_weight* gate,
+                             const moe_weight* up, const moe_align_tables* t, float* act,
+                             const moe_weight* sh_gate, const moe_weight* sh_up, float* sh_act, int64_t M,
+                             int32_t H, int32_t I, int32_t S, int32_t E, int32_t top_k, int32_t BS,
+                             hipStream_t stream) {
+  const char* fn = "moe_grouped_gate_up_silu";
+  AlignShape s;
+  int rc = check_routing_shape(fn, M, top_k, E, BS, &s);
+  if (rc) return rc;
+  if ((rc = check_wdt(fn, wdt))) return rc;
+  if (S < 0) return fail(MOE_ERR_SHAPE, "%s: S=%d is negative", fn, S);
+  if ((rc = check_projection(fn, "gate/up", wdt, I, H))) return rc;
+  if (S > 0 && (rc = check_projection(fn, "shared gate/up", wdt, S, H))) return rc;
+  if (M == 0) return MOE_OK;
+  if (x_bf16 == nullptr || act == nullptr) return fail(MOE_ERR_NULL, "%s: x or act is NULL", fn);
+  if ((rc = check_weight(fn, "gate", gate, wdt)) || (rc = check_weight(fn, "up", up, wdt))) return rc;
+  if ((rc = check_tables(fn, t, false))) return rc;
+  if (S > 0) {
+    if ((rc = check_weight(fn, "shared gate", sh_gate, wdt)) || (rc = check_weight(fn, "shared up", sh_up, wdt)))
+      return rc;
+    if (sh_act == nullptr) return fail(MOE_ERR_NULL, "%s: sh_act is NULL with S > 0", fn);
+  }
+  moe::GroupedArgs a{};
+  a.x = x_bf16;
+  a.w0 = gate->w;
+  a.s0 = gate->scale;
+  a.w1 = up->w;
+  a.s1 = up->scale;
+  a.out = act;
+  a.N = I;
+  a.K = H;
+  if (S > 0) {
+    a.sx = x_bf16;
+    a.sw0 = sh_gate->w;
+    a.ss0 = sh_gate->scale;
+    a.sw1 = sh_up->w;
+    a.ss1 = sh_up->scale;
+    a.sout = sh_act;
+    a.sN = S;
+    a.sK = H;
+  }
+  fill_tables(a, t);
+  a.M = (int)M;
+  a.top_k = top_k;
+  a.cap = s.cap;
+  return hip_status(moe::launch_grouped_gate_up(a, wdt == MOE_W_FP8_E4M3, moe::grouped_row_tiles(M, top_k), stream),
+                    fn);
+}
+
+int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down, const moe_align_tables* t,
+                     float* expert_out, const moe_weight* sh_down, const float* sh_act, float* sh_out, int64_t M,
+                     int32_t H, int32_t I, int32_t S, int32_t E, int32_t top_k, int32_t BS, hipStream_t stream) {
+  const char* fn = "moe_grouped_down";
+  AlignShape s;
+  int rc = check_routing_shape(fn, M, top_k, E, BS, &s);
+  if (rc) return rc;
+  if ((rc = check_wdt(fn, wdt))) return rc;
+  if (S < 0) return fail(MOE_ERR_SHAPE, "%s: S=%d is negative", fn, S);
+  if ((rc = check_projection(fn, "down", wdt, H, I))) return rc;
+  if (S > 0 && (rc = check_projection(fn, "shared down", wdt, H, S))) return rc;
+  if (M == 0) return MOE_OK;
+  if (act == nullptr || expert_out == nullptr) return fail(MOE_ERR_NULL, "%s: act or expert_out is NULL", fn);
+  if ((rc = check_weight(fn, "down", down, wdt))) return rc;
+  if ((rc = check_tables(fn, t, false))) return rc;
+  if (S > 0) {
+    if ((rc = check_weight(fn, "shared down", sh_down, wdt))) return rc;
+    if (sh_act == nullptr || sh_out == nullptr)
+      return fail(MOE_ERR_NULL, "%s: sh_act or sh_out is NULL with S > 0", fn);
+  }
+  moe::GroupedArgs a{};
+  a.x = act;
+  a.w0 = down->w;
+  a.s0 = down->scale;
+  a.out = expert_out;
+  a.N = H;
+  a.K = I;
+  if (S > 0) {
+    a.sx = sh_act;
+    a.sw0 = sh_down->w;
+    a.ss0 = sh_down->scale;
+    a.sout = sh_out;
+    a.sN = H;
+    a.sK = S;
+  }
+  fill_tables(a, t);
+  a.M = (int)M;
+  a.top_k = top_k;
+  a.cap = s.cap;
+  return hip_status(moe::launch_grouped_down(a, wdt == MOE_W_FP8_E4M3, moe::grouped_row_tiles(M, top_k), stream), fn);
+}
+
+int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights, const int32_t* token_to_perm,
+              const float* sh_out, int64_t M, int32_t H, int32_t top_k, hipStream_t stream) {
+  const char* fn = "moe_blend";
+  if (M < 0 || H < 1 || top_k < 1) return fail(MOE_ERR_SHAPE, "%s: M=%lld H=%d top_k=%d", fn, (long long)M, H, top_k);
+  if (H % 4) return fail(MOE_ERR_SHAPE, "%s: H=%d must be a multiple of 4", fn, H);
+  if (M >= kInt32Limit / top_k) return fail(MOE_ERR_LIMIT, "%s: M*top_k reaches 2^31", fn);
+  if (M == 0) return MOE_OK;
+  if (!out_bf16 || !expert_out || !topk_weights || !token_to_perm)
+    return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  return hip_status(moe::launch_blend(static_cast<uint16_t*>(out_bf16), expert_out, topk_weights, token_to_perm,
+                                      sh_out, (int)M, H, top_k, stream),
+                    fn);
+}
+
+int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[13]) {
+  if (offsets == nullptr) return fail(MOE_ERR_NULL, "moe_layer_workspace_layout: offsets is NULL");
+  return layout(d, offsets);
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc* d) {
+  size_t off[13];
+  if (layout(d, off) != MOE_OK) return 0;
+  return off[12];
+}
+
+int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids, const float* topk_weights,
+                      void* out_bf16, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_layer_forward";
+  size_t off[13];
+  int rc = layout(d, off);
+  if (rc) return rc;
+  if (d->M == 0) return MOE_OK;
+  if (!x_bf16 || !topk_ids || !topk_weights || !out_bf16)
+    return fail(MOE_ERR_NULL, "%s: x, topk_ids, topk_weights or out is NULL", fn);
+  if (workspace == nullptr) return fail(MOE_ERR_NULL, "%s: workspace is NULL", fn);
+  if (workspace_bytes < off[12])
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, off[12]);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", fn);
+  const bool shared = d->S > 0;
+  if ((rc = check_weight(fn, "gate", &d->gate, d->wdt)) || (rc = check_weight(fn, "up", &d->up, d->wdt)) ||
+      (rc = check_weight(fn, "down", &d->down, d->wdt)))
+    return rc;
+  if (shared && ((rc = check_weight(fn, "shared gate", &d->sh_gate, d->wdt)) ||
+                 (rc = check_weight(fn, "shared up", &d->sh_up, d->wdt)) ||
+                 (rc = check_weight(fn, "shared down", &d->sh_down, d->wdt))))
+    return rc;
+
+  char* ws = static_cast<char*>(workspace);
+  moe_align_tables t;
+  t.sorted_token_ids = reinterpret_cast<int32_t*>(ws + off[0]);
+  t.block_expert_ids = reinterpret_cast<int32_t*>(ws + off[1]);
+  t.expert_offsets = reinterpret_cast<int32_t*>(ws + off[2]);
+  t.expert_counts = reinterpret_cast<int32_t*>(ws + off[3]);
+  t.token_to_perm = reinterpret_cast<int32_t*>(ws + off[4]);
+  t.active_experts = reinterpret_cast<int32_t*>(ws + off[5]);
+  t.active_count = reinterpret_cast<int32_t*>(ws + off[6]);
+  t.total = reinterpret_cast<int32_t*>(ws + off[7]);
+  float* act = reinterpret_cast<float*>(ws + off[8]);
+  float* expert_out = reinterpret_cast<float*>(ws + off[9]);
+  float* sh_act = shared ? reinterpret_cast<float*>(ws + off[10]) : nullptr;
+  float* sh_out = shared ? reinterpret_cast<float*>(ws + off[11]) : nullptr;
+
+  if ((rc = moe_align(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, stream))) return rc;
+  if ((rc = moe_grouped_gate_up_silu(x_bf16, d->wdt, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,
+                                     shared ? &d->sh_up : nullptr, sh_act, d->M, d->H, d->I, d->S, d->E, d->top_k,
+                                     d->BS, stream)))
+    return rc;
+  if ((rc = moe_grouped_down(act, d->wdt, &d->down, &t, expert_out, shared ? &d->sh_down : nullptr, sh_act, sh_out,
+                             d->M, d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))
+    return rc;
+  return moe_blend(out_bf16, expert_out, topk_weights, t.token_to_perm, sh_out, d->M, d->H, d->top_k, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,73 @@
+// Top-k blend for gfx950.
+//
+// out[t, h] = bf16( sum_{k=0..top_k-1, in order} w[t,k] * expert_out[token_to_perm[t*top_k+k], h]
+//                   + sh_out[t, h] )
+// Restated from metrale fp8_moe_grouped.rs (moe_weighted_sum_blend_fp8_grouped:
+// expert outputs are rows of sorted positions reached through token_to_perm; the
+// shared expert's output is added ungated when no gate is given) and nbxtensor
+// moe_decode_vec.py (moe_part_reduce_kernel: the top-k sum in a constant order so
+// the combine is deterministic).  The accumulation is a float32 fused
+// multiply-add chain over k starting from 0, then + sh_out, then one
+// round-to-nearest-even to bf16.  A token's bits depend only on its own inputs.
+//
+// Layout: one thread owns 4 consecutive hidden columns (16-byte loads of each
+// expert row, an 8-byte store); grid = (ceil(H / 1024), min(M, 65535)), the
+// y blocks striding over the tokens.  The expert rows a
+// token reads are each contiguous, so every load is coalesced.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays a quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ __launch_bounds__(256) void blend_kernel(uint16_t* __restrict__ out,
+                                                    const float* __restrict__ expert_out,
+                                                    const float* __restrict__ w,
+                                                    const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ sh_out, int M, int H, int top_k) {
+  const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (h >= H) return;
+  for (int t = blockIdx.y; t < M; t += gridDim.y) {
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  const size_t slot0 = (size_t)t * top_k;
+  for (int k = 0; k < top_k; ++k) {
+    const int p = perm[slot0 + k];
+    if (p < 0) continue;
+    const float wk = w[slot0 + k];
+    const float4 y = *reinterpret_cast<const float4*>(expert_out + (size_t)p * H + h);
+    a0 = fmaf(wk, y.x, a0);
+    a1 = fmaf(wk, y.y, a1);
+    a2 = fmaf(wk, y.z, a2);
+    a3 = fmaf(wk, y.w, a3);
+  }
+  if (sh_out != nullptr) {
+    const float4 s = *reinterpret_cast<const float4*>(sh_out + (size_t)t * H + h);
+    a0 += s.x;
+    a1 += s.y;
+    a2 += s.z;
+    a3 += s.w;
+  }
+  uint2 packed;
+  packed.x = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+  packed.y = f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16);
+  *reinterpret_cast<uint2*>(out + (size_t)t * H + h) = packed;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,
+                        const float* sh_out, int M, int H, int top_k, hipStream_t s) {
+  const dim3 grid((H / 4 + 255) / 256, M < 65535 ? M : 65535);
+  hipLaunchKernelGGL(blend_kernel, grid, dim3(256), 0, s, out, expert_out, w, perm, sh_out, M, H, top_k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

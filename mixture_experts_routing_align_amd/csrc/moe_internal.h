@@ -1,0 +1,66 @@
+// Internal interface between the C ABI layer (api.cpp) and the gfx950 kernels.
+// Launchers validate nothing: api.cpp has checked every argument before calling.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace moe {
+
+constexpr int kFp8Block = 128;   // FP8 scale block edge (both N and K)
+
+struct AlignOut {
+  int32_t* sorted_token_ids;
+  int32_t* block_expert_ids;
+  int32_t* expert_offsets;
+  int32_t* expert_counts;
+  int32_t* token_to_perm;
+  int32_t* active_experts;
+  int32_t* active_count;
+  int32_t* total;
+};
+
+// One launch, one workgroup: the whole alignment.
+hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap,
+                        const AlignOut& o, hipStream_t s);
+
+// Operands of one grouped projection launch (routed experts + optional shared expert).
+struct GroupedArgs {
+  // routed experts
+  const void* x;        // gate+up: bf16 [M, K] token rows; down: float32 [max_total, K] by position
+  const void* w0;       // gate (gate+up) or down weights [E, N, K]
+  const float* s0;      // its FP8 scales [E, N/128, K/128] (unused for bf16)
+  const void* w1;       // up weights (gate+up only)
+  const float* s1;
+  float* out;           // gate+up: act [max_total, N]; down: expert_out [max_total, N]
+  int N, K;
+  // shared expert (sw0 == nullptr: none)
+  const void* sx;       // gate+up: bf16 [M, sK] (the same x); down: float32 sh_act [M, sK]
+  const void* sw0;
+  const float* ss0;
+  const void* sw1;
+  const float* ss1;
+  float* sout;          // [M, sN]
+  int sN, sK;
+  // alignment tables
+  const int32_t* sorted_token_ids;
+  const int32_t* expert_offsets;
+  const int32_t* expert_counts;
+  const int32_t* active_experts;
+  const int32_t* active_count;
+  int M, top_k, cap;
+};
+
+// Row tiles (16 rows each) one workgroup keeps in registers per pass over the
+// weights; chosen from the shape class (the most rows an expert can hold), never
+// from the routing.
+int grouped_row_tiles(int64_t M, int top_k);
+
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, int row_tiles, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, int row_tiles, hipStream_t s);
+
+hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,
+                        const float* sh_out, int M, int H, int top_k, hipStream_t s);
+
+}  // namespace moe

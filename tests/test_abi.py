@@ -1,0 +1,168 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, its
+pure sizing functions agree with the oracle, and every host-side check refuses
+bad arguments before touching the GPU (no compute call runs here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_routing_align_amd import _ffi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mi355x.h")
+FAKE = 0x1000  # a non-NULL address no call may dereference: every case below fails before any launch
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _ffi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in _ffi.SIGNATURES, name
+    assert set(_ffi.SIGNATURES) == set(names)
+
+
+def test_abi_version(lib):
+    assert lib.moe_abi_version() == 1
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_sizing_matches_oracle(lib, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        n = int(rng.integers(0, 100000))
+        E = int(rng.integers(1, 1025))
+        BS = int(rng.integers(1, 129))
+        assert lib.moe_align_max_total(n, E, BS) == oracle.max_total(n, E, BS)
+        assert lib.moe_active_cap(n, E) == oracle.active_cap(n, E)
+    assert lib.moe_align_max_total(-1, 4, 4) == -1
+    assert lib.moe_align_max_total(4, 0, 4) == -1
+    assert lib.moe_active_cap(-1, 4) == -1
+
+
+def _tables(ptr=FAKE):
+    return _ffi.MoeAlignTables(*([ptr] * 8))
+
+
+def _err(lib):
+    return lib.moe_last_error().decode()
+
+
+def test_align_refusals(lib):
+    t = _tables()
+    assert lib.moe_align(FAKE, 1, 4, 2, 1025, 16, ctypes.byref(t), None) == _ffi.MOE_ERR_LIMIT
+    assert "1024" in _err(lib)
+    assert lib.moe_align(FAKE, 1, 4, 0, 8, 16, ctypes.byref(t), None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_align(FAKE, 1, 4, 2, 8, 0, ctypes.byref(t), None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_align(FAKE, 1, -1, 2, 8, 16, ctypes.byref(t), None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_align(FAKE, 7, 4, 2, 8, 16, ctypes.byref(t), None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_align(None, 1, 4, 2, 8, 16, ctypes.byref(t), None) == _ffi.MOE_ERR_NULL
+    bad = _tables()
+    bad.token_to_perm = None
+    assert lib.moe_align(FAKE, 1, 4, 2, 8, 16, ctypes.byref(bad), None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_align(FAKE, 1, 2 ** 30, 4, 8, 16, ctypes.byref(t), None) == _ffi.MOE_ERR_LIMIT
+    # worst-case table past 2^31 entries: n = 2^20 slots, 1024 experts, BS = 2^21
+    assert oracle.max_total(2 ** 20, 1024, 2 ** 21) >= 2 ** 31
+    assert lib.moe_align(FAKE, 1, 2 ** 17, 8, 1024, 2 ** 21, ctypes.byref(t), None) == _ffi.MOE_ERR_LIMIT
+    # M = 0: nothing to do, nothing launched
+    assert lib.moe_align(None, 1, 0, 2, 8, 16, None, None) == _ffi.MOE_OK
+
+
+def _w(scale=True):
+    return _ffi.MoeWeight(FAKE, FAKE if scale else None)
+
+
+def test_grouped_refusals(lib):
+    t = _tables()
+    g, u = _w(), _w()
+    args = dict(M=4, H=256, I=128, S=0, E=8, top_k=2, BS=16)
+
+    def gu(wdt=1, **kw):
+        a = {**args, **kw}
+        return lib.moe_grouped_gate_up_silu(FAKE, wdt, ctypes.byref(g), ctypes.byref(u), ctypes.byref(t), FAKE,
+                                            None, None, None, a["M"], a["H"], a["I"], a["S"], a["E"], a["top_k"],
+                                            a["BS"], None)
+
+    assert gu(H=200) == _ffi.MOE_ERR_SHAPE          # FP8 needs whole 128 blocks
+    assert gu(I=64) == _ffi.MOE_ERR_SHAPE
+    assert gu(wdt=0, H=48) == _ffi.MOE_ERR_SHAPE    # BF16 needs K % 32
+    assert gu(wdt=0, I=24) == _ffi.MOE_ERR_SHAPE    # and N % 16
+    assert gu(wdt=5) == _ffi.MOE_ERR_SHAPE
+    assert gu(S=128) == _ffi.MOE_ERR_NULL           # shared expert without weights
+    assert gu(E=2000) == _ffi.MOE_ERR_LIMIT
+    assert gu(M=0) == _ffi.MOE_OK
+    nos = _w(scale=False)
+    assert lib.moe_grouped_gate_up_silu(FAKE, 1, ctypes.byref(nos), ctypes.byref(u), ctypes.byref(t), FAKE, None,
+                                        None, None, 4, 256, 128, 0, 8, 2, 16, None) == _ffi.MOE_ERR_NULL
+    d = _w()
+    assert lib.moe_grouped_down(FAKE, 1, ctypes.byref(d), ctypes.byref(t), FAKE, None, None, None,
+                                4, 256, 100, 0, 8, 2, 16, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_grouped_down(FAKE, 1, ctypes.byref(d), ctypes.byref(t), FAKE, None, None, None,
+                                4, 256, 128, 128, 8, 2, 16, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_blend(FAKE, FAKE, FAKE, FAKE, None, 4, 6, 2, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_blend(None, FAKE, FAKE, FAKE, None, 4, 8, 2, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_blend(None, None, None, None, None, 0, 8, 2, None) == _ffi.MOE_OK
+
+
+def _desc(M=8, H=2048, I=768, S=0, E=128, top_k=8, BS=16, wdt=1, idt=1):
+    w = _w(wdt == 1)
+    none = _ffi.MoeWeight(None, None)
+    sh = w if S else none
+    return _ffi.MoeLayerDesc(M, H, I, S, E, top_k, BS, wdt, idt, w, w, w, sh, sh, sh)
+
+
+def test_workspace_layout(lib):
+    for kw in (dict(), dict(M=128, S=2048), dict(M=64, H=7168, E=256, I=2048, S=2048, BS=64),
+               dict(M=4, H=256, E=8, top_k=2, I=128, wdt=0)):
+        d = _desc(**kw)
+        off = (ctypes.c_size_t * 13)()
+        assert lib.moe_layer_workspace_layout(ctypes.byref(d), off) == _ffi.MOE_OK
+        a = {k: v for k, v in dict(M=8, H=2048, I=768, S=0, E=128, top_k=8, BS=16).items()}
+        a.update({k: v for k, v in kw.items() if k in a})
+        n = a["M"] * a["top_k"]
+        mt = oracle.max_total(n, a["E"], a["BS"])
+        sizes = [mt * 4, mt // a["BS"] * 4, (a["E"] + 1) * 4, a["E"] * 4, n * 4, min(n, a["E"]) * 4, 4, 4,
+                 mt * a["I"] * 4, mt * a["H"] * 4]
+        for i, s in enumerate(sizes):
+            assert off[i] % 256 == 0
+            assert off[i + 1] >= off[i] + s if i + 1 < 10 else True
+        total = lib.moe_layer_workspace_bytes(ctypes.byref(d))
+        assert total == off[12] and total >= off[9] + sizes[9]
+        if a["S"]:
+            assert off[10] >= off[9] + sizes[9] and off[11] >= off[10] + a["M"] * a["S"] * 4
+            assert total >= off[11] + a["M"] * a["H"] * 4
+
+
+def test_layer_refusals(lib):
+    d = _desc()
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    rc = lib.moe_layer_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0x100000, need - 1, None)
+    assert rc == _ffi.MOE_ERR_WORKSPACE
+    rc = lib.moe_layer_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0x100010, need, None)
+    assert rc == _ffi.MOE_ERR_WORKSPACE              # not 256-byte aligned
+    rc = lib.moe_layer_forward(ctypes.byref(d), None, FAKE, FAKE, FAKE, 0x100000, need, None)
+    assert rc == _ffi.MOE_ERR_NULL
+    bad = _desc(H=1000)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(bad)) == 0
+    assert "128" in _err(lib)
+    bad = _desc(S=2048)
+    bad.sh_down = _ffi.MoeWeight(None, None)
+    rc = lib.moe_layer_forward(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 0x100000, 1 << 40, None)
+    assert rc == _ffi.MOE_ERR_NULL
+    d0 = _desc(M=0)
+    assert lib.moe_layer_forward(ctypes.byref(d0), None, None, None, None, None, 0, None) == _ffi.MOE_OK

@@ -1,0 +1,80 @@
+"""GPU parity of moe_align: every table bit-exact against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from moe_testlib import compare_tables, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_align(ids_np, E, BS, dtype=torch.int64):
+    import mixture_experts_routing_align_amd as moe
+
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np)).to(dtype).cuda()
+    t = moe.moe_align(ids, E, BS)
+    torch.cuda.synchronize()
+    return {k: getattr(t, k) for k in moe.TABLE_FIELDS}
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "verify", "align", "large"])
+@pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
+def test_align_configs_bit_exact(name, dtype):
+    cfg = workloads.CONFIGS[name]
+    log(f"align parity: config {name} n={cfg.n} E={cfg.E} BS={cfg.BS} ids {dtype}")
+    ids, _ = workloads.routing(cfg)
+    compare_tables(_gpu_align(ids, cfg.E, cfg.BS, dtype), oracle.align(ids, cfg.E, cfg.BS))
+
+
+ADVERSARIAL = [
+    ("one_expert_all_slots", lambda r: np.full((300, 4), 5), 8, 16),
+    ("all_distinct", lambda r: r.permutation(1024)[:1000].reshape(250, 4), 1024, 16),
+    ("out_of_range", lambda r: r.integers(-3, 11, size=(77, 3)), 8, 4),
+    ("bs1", lambda r: r.integers(0, 64, size=(100, 8)), 64, 1),
+    ("single_expert_E1", lambda r: np.zeros((13, 1)), 1, 16),
+    ("max_experts", lambda r: r.integers(0, 1024, size=(500, 8)), 1024, 64),
+    ("ragged_n", lambda r: r.integers(0, 7, size=(37, 3)), 7, 3),
+    ("single_slot", lambda r: np.array([[2]]), 4, 8),
+    ("large_bs", lambda r: r.integers(0, 32, size=(64, 2)), 32, 256),
+    ("all_invalid", lambda r: np.full((20, 2), -1), 8, 4),
+    ("skewed_big", lambda r: np.minimum(r.geometric(0.05, size=(8192, 4)), 300), 300, 32),
+]
+
+
+@pytest.mark.parametrize("case", ADVERSARIAL, ids=lambda c: c[0])
+def test_align_adversarial(case):
+    name, make, E, BS = case
+    ids = make(np.random.default_rng(99)).astype(np.int64)
+    log(f"align adversarial: {name} shape={ids.shape} E={E} BS={BS}")
+    compare_tables(_gpu_align(ids, E, BS), oracle.align(ids, E, BS))
+
+
+def test_align_int64_ids_beyond_int32():
+    """int64 ids that would alias a valid expert if truncated to 32 bits are dropped."""
+    ids = np.array([[2 ** 32 + 1, 1], [3, -(2 ** 40)], [2 ** 33, 0]], dtype=np.int64)
+    compare_tables(_gpu_align(ids, 4, 2), oracle.align(ids, 4, 2))
+
+
+def test_align_deterministic_repeats():
+    cfg = workloads.CONFIGS["align"]
+    ids, _ = workloads.routing(cfg)
+    first = _gpu_align(ids, cfg.E, cfg.BS)
+    for _ in range(10):
+        again = _gpu_align(ids, cfg.E, cfg.BS)
+        for k in first:
+            assert torch.equal(first[k], again[k]), k
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_align_random_shapes(seed):
+    rng = np.random.default_rng(1000 + seed)
+    E = int(rng.integers(1, 1025))
+    BS = int(rng.choice([1, 2, 4, 16, 64, 128]))
+    M = int(rng.integers(1, 3000))
+    top_k = int(rng.integers(1, 9))
+    ids = rng.integers(-1, E + 1, size=(M, top_k))
+    log(f"align random: seed={seed} M={M} top_k={top_k} E={E} BS={BS}")
+    compare_tables(_gpu_align(ids, E, BS, torch.int32 if seed % 2 else torch.int64), oracle.align(ids, E, BS))

@@ -1,0 +1,269 @@
+"""GPU parity of the grouped expert FFN, the blend and the fused layer against
+the float64 oracle, plus the bit-exact properties (row invariance, run-to-run
+determinism, blend invariants, exact FP8 decode)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from moe_testlib import (DeviceModel, bf16_to_np, compare_tables, device_inputs, log, oracle_layer,
+                         tolerance_ok)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import mixture_experts_routing_align_amd as m
+
+    return m
+
+
+_MODELS = {}
+
+
+def model_for(name, **kw):
+    if name not in _MODELS:
+        cfg = workloads.CONFIGS[name]
+        log(f"generating weights for {name}")
+        _MODELS[name] = DeviceModel(cfg, keep_host=(name != "large"), threads=16)
+    return _MODELS[name]
+
+
+def _run_layer(moe, model, xt, it, wt):
+    layer = model.layer()
+    ws = layer.alloc_workspace(xt.shape[0], moe.MOE_IDX_I64 if it.dtype == torch.int64 else moe.MOE_IDX_I32)
+    out = layer.forward(xt, it, wt, workspace=ws)
+    torch.cuda.synchronize()
+    return out, layer.workspace_views(ws, xt.shape[0], moe.MOE_IDX_I64 if it.dtype == torch.int64 else
+                                      moe.MOE_IDX_I32)
+
+
+# ------------------------------------------------------------ FP8 decode --
+
+@pytest.mark.parametrize("scale", [1.0, 0.375])
+def test_fp8_decode_exhaustive_through_down(moe, scale):
+    """Row c of a one-expert down projection holds code c at input column j and
+    zeros elsewhere; act is one-hot at j.  expert_out[c] must equal the OCP e4m3
+    value of c times the block scale exactly, for every code and several j."""
+    H, I = 256, 128
+    ids = torch.zeros(1, 1, dtype=torch.int64, device="cuda")
+    t = moe.moe_align(ids, 1, 1)
+    table = oracle.e4m3_table() * scale
+    for j in (0, 1, 5, 8, 9, 15, 16, 31, 63, 64, 100, 127):
+        w = torch.zeros(1, H, I, dtype=torch.uint8)
+        w[0, :, j] = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+        s = torch.full((1, H // 128, I // 128), scale, dtype=torch.float32)
+        act = torch.zeros(1, I, dtype=torch.float32, device="cuda")
+        act[0, j] = 1.0
+        out = torch.full((1, H), 7.0, dtype=torch.float32, device="cuda")
+        moe.moe_grouped_down(act, (w.cuda(), s.cuda()), t, out, 1, 1, 1)
+        torch.cuda.synchronize()
+        got = out[0].cpu().double().numpy()
+        nan = np.isnan(table)
+        assert np.array_equal(np.isnan(got), nan), j
+        assert np.array_equal(got[~nan], table[~nan]), (j, np.flatnonzero(got[~nan] != table[~nan])[:8])
+
+
+# ------------------------------------------------------- full-layer parity --
+
+def _check_layer(moe, name, tokens=None):
+    model = model_for(name)
+    cfg = model.cfg
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    log(f"layer parity: config {name} M={cfg.M} H={cfg.H} E={cfg.E} top_k={cfg.top_k} I={cfg.I} S={cfg.S}")
+    out, views = _run_layer(moe, model, xt, it, wt)
+    ref = oracle_layer(model, x, ids, w, tokens=tokens)
+    compare_tables(views, ref["tables"])
+    got = bf16_to_np(out)
+    rows = ref["tokens"]
+    ok, err, bound = tolerance_ok(got[rows], ref["out"])
+    log(f"  out: max err {err:.3e} bound {bound:.3e}")
+    assert ok, (err, bound)
+    # intermediates (debug aid): act and expert_out rows at every slot position computed
+    pos = sorted(ref["act_pos"])
+    act = views["act"][pos].cpu().double().numpy()
+    ok, err, bound = tolerance_ok(act, np.stack([ref["act_pos"][p] for p in pos]))
+    assert ok, ("act", err, bound)
+    y = views["expert_out"][pos].cpu().double().numpy()
+    ok, err, bound = tolerance_ok(y, np.stack([ref["y_pos"][p] for p in pos]))
+    assert ok, ("expert_out", err, bound)
+    if cfg.S:
+        ok, err, bound = tolerance_ok(views["sh_act"][rows].cpu().double().numpy(), ref["sh_act"])
+        assert ok, ("sh_act", err, bound)
+        ok, err, bound = tolerance_ok(views["sh_out"][rows].cpu().double().numpy(), ref["sh_out"])
+        assert ok, ("sh_out", err, bound)
+    return out
+
+
+def test_layer_tiny(moe):
+    _check_layer(moe, "tiny")
+
+
+def test_layer_decode(moe):
+    _check_layer(moe, "decode")
+
+
+def test_layer_verify(moe):
+    _check_layer(moe, "verify")
+
+
+def test_layer_large_sampled(moe):
+    # full size; the oracle computes a sample of tokens one by one (first, last, two inside)
+    _check_layer(moe, "large", tokens=[0, 17, 42, 63])
+
+
+def test_layer_int32_ids_same_bits(moe):
+    model = model_for("decode")
+    _, (xt, it, wt) = device_inputs(model.cfg)
+    a, _ = _run_layer(moe, model, xt, it, wt)
+    b, _ = _run_layer(moe, model, xt, it.to(torch.int32), wt)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------------ odd shapes, many passes --
+
+ODD = [
+    # BF16, N not a multiple of the 64-column tile, K with a partial 128 chunk, shared expert
+    workloads.MoeConfig("bf16_odd", 5, 96, 6, 3, 160, 96, 4, "bf16", "softmax", seed=7),
+    # FP8, shared expert narrower than the routed one
+    workloads.MoeConfig("fp8_small", 9, 256, 16, 4, 384, 128, 8, "fp8", "softmax_bias", bias_std=2.0, seed=8),
+    # 70 tokens -> 4 row tiles per pass; the skew puts > 64 rows on some experts (several passes)
+    workloads.MoeConfig("bf16_many_rows", 70, 128, 4, 2, 64, 0, 16, "bf16", "softmax_bias", bias_std=4.0, seed=9),
+]
+
+
+@pytest.mark.parametrize("cfg", ODD, ids=lambda c: c.name)
+def test_layer_odd_shapes(moe, cfg):
+    model = DeviceModel(cfg, threads=4)
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    log(f"odd-shape parity: {cfg}")
+    out, views = _run_layer(moe, model, xt, it, wt)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    assert ok, (err, bound)
+
+
+def test_layer_repeated_ids_multi_pass(moe):
+    """Every slot of every token on one expert (ids repeat within a token): 96
+    rows on expert 2, more than one pass of row tiles for M=48."""
+    cfg = workloads.MoeConfig("repeat", 48, 128, 4, 2, 32, 0, 8, "bf16", "softmax", seed=11)
+    model = DeviceModel(cfg, threads=4)
+    (x, _, w), (xt, _, wt) = device_inputs(cfg)
+    ids = np.full((cfg.M, cfg.top_k), 2, dtype=np.int64)
+    it = torch.from_numpy(ids).cuda()
+    out, views = _run_layer(moe, model, xt, it, wt)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    assert ok, (err, bound)
+
+
+def test_layer_out_of_range_ids(moe):
+    model = model_for("tiny")
+    cfg = model.cfg
+    (x, ids, w), (xt, _, wt) = device_inputs(cfg)
+    ids = ids.copy()
+    ids[0, 1] = -1
+    ids[2, 0] = cfg.E + 3
+    it = torch.from_numpy(ids).cuda()
+    out, views = _run_layer(moe, model, xt, it, wt)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    assert ok, (err, bound)
+
+
+# ------------------------------------------------------ bit-exact properties --
+
+@pytest.mark.parametrize("name,ms", [("decode", [1, 2, 3, 5, 7]), ("verify", [1, 9, 16, 33, 64, 100, 127])])
+def test_row_invariance(moe, name, ms):
+    """Rows 0..m-1 of a run on the first m tokens equal the full run's rows bit for bit."""
+    model = model_for(name)
+    _, (xt, it, wt) = device_inputs(model.cfg)
+    full, _ = _run_layer(moe, model, xt, it, wt)
+    for m in ms:
+        part, _ = _run_layer(moe, model, xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous())
+        assert torch.equal(part.view(torch.int16), full[:m].view(torch.int16)), m
+
+
+def test_run_to_run_bit_exact(moe):
+    model = model_for("verify")
+    _, (xt, it, wt) = device_inputs(model.cfg)
+    first, _ = _run_layer(moe, model, xt, it, wt)
+    for _ in range(5):
+        again, _ = _run_layer(moe, model, xt, it, wt)
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
+
+
+# ------------------------------------------------------------------ blend --
+
+def test_blend_parity_and_invariants(moe):
+    rng = np.random.default_rng(5)
+    M, top_k, E, BS, H = 37, 4, 16, 8, 512
+    ids = np.stack([rng.choice(E, size=top_k, replace=False) for _ in range(M)]).astype(np.int64)
+    ids[3, 2] = -1
+    ref_t = oracle.align(ids, E, BS)
+    mt = ref_t["max_total"]
+    eo = rng.normal(size=(mt, H)).astype(np.float32)
+    w = rng.uniform(0.05, 1, size=(M, top_k)).astype(np.float32)
+    sh = rng.normal(size=(M, H)).astype(np.float32)
+    t = moe.moe_align(torch.from_numpy(ids).cuda(), E, BS)
+    eo_d, w_d, sh_d = (torch.from_numpy(a).cuda() for a in (eo, w, sh))
+    out = torch.empty(M, H, dtype=torch.bfloat16, device="cuda")
+    moe.moe_blend(out, eo_d, w_d, t.token_to_perm, sh_d)
+    ref = oracle.blend(eo, w, ref_t["token_to_perm"], sh.astype(np.float64))
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref)
+    assert ok, (err, bound)
+    # no shared expert: doubling every weight doubles the output exactly
+    a = torch.empty_like(out)
+    b = torch.empty_like(out)
+    moe.moe_blend(a, eo_d, w_d, t.token_to_perm)
+    moe.moe_blend(b, eo_d, 2 * w_d, t.token_to_perm)
+    torch.cuda.synchronize()
+    assert torch.equal(b.float(), 2 * a.float())
+    # top-1, weight 1, no shared: the output is the row rounded to bf16
+    ids1 = ids[:, :1].copy()
+    ids1[3, 0] = 1
+    t1 = moe.moe_align(torch.from_numpy(ids1).cuda(), E, BS)
+    o1 = torch.empty_like(out)
+    moe.moe_blend(o1, eo_d, torch.ones(M, 1, device="cuda"), t1.token_to_perm)
+    r1 = oracle.align(ids1, E, BS)["token_to_perm"]
+    assert torch.equal(o1, torch.from_numpy(eo[r1]).cuda().to(torch.bfloat16))
+
+
+# ------------------------------------------------------------ graph replay --
+
+def test_graph_replay_follows_new_routing(moe):
+    """Capture the layer once; overwrite ids/weights in place between replays;
+    every replay must match the oracle for the routing it saw."""
+    model = model_for("decode")
+    cfg = model.cfg
+    layer = model.layer()
+    (x, ids0, w0), (xt, it, wt) = device_inputs(cfg)
+    ws = layer.alloc_workspace(cfg.M)
+    out = torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        layer.forward(xt, it, wt, out=out, workspace=ws)  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        layer.forward(xt, it, wt, out=out, workspace=ws)
+    for r in range(3):
+        cfg_r = cfg.replace(seed=cfg.seed + 100 + r)
+        ids, w = workloads.routing(cfg_r)
+        it.copy_(torch.from_numpy(ids))
+        wt.copy_(torch.from_numpy(w))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eager = layer.forward(xt, it, wt)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), r
+        ref = oracle_layer(model, x, ids, w)
+        ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+        assert ok, (r, err, bound)
