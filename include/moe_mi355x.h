@@ -65,7 +65,17 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_IDX_I32 = 0, MOE_IDX_I64 = 1 } moe_index_dtype;
-typedef enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3 = 1 } moe_weight_dtype;
+
+/* Expert weight element type and layout.  The row-major forms are [E, N, K];
+ * the tiled forms are the same values reordered by moe_tile_weights() so that
+ * every wave streams one contiguous run (see there).  Both layouts give
+ * bit-identical results. */
+typedef enum {
+  MOE_W_BF16 = 0,            /* bf16, row-major [E, N, K]                      */
+  MOE_W_FP8_E4M3 = 1,        /* OCP e4m3fn codes, row-major [E, N, K]          */
+  MOE_W_BF16_TILED = 2,      /* bf16, tiled by moe_tile_weights                */
+  MOE_W_FP8_E4M3_TILED = 3   /* e4m3fn codes, tiled by moe_tile_weights        */
+} moe_weight_dtype;
 
 /* Experts one align launch handles (fp8_moe_grouped.rs: the one-launch sort's
  * 1024-expert limit, FP8_GROUPED_SORT_MAX_EXPERTS). */
@@ -119,10 +129,32 @@ typedef struct {
 int moe_align(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k,
               int32_t E, int32_t BS, const moe_align_tables* out, hipStream_t stream);
 
+/* ---------------------------------------------------------- weight tiling --
+ * A one-time, load-time reordering of an expert weight tensor (the source pages
+ * describe such a load-time repack for their lean tensor-core kernels:
+ * metrale forward_nvfp4_grouped_decode.rs, Nvfp4GroupedKernels doc).  The tiled
+ * copy holds, for each expert, 16-row tiles; in a tile, 128-deep chunks (K
+ * zero-padded up to a multiple of 128); in a chunk, 1 KB fragments in which the
+ * 16 bytes lane l of a wave feeds the matrix core sit at byte 16*l.  A wave
+ * then reads its weights as one contiguous stream (on MI355X, ~1.3x the HBM
+ * bandwidth of reading 16 row-major rows side by side).  Scales are unchanged. */
+
+/* Bytes of the tiled copy of row-major weights of dtype `wdt` (MOE_W_BF16 or
+ * MOE_W_FP8_E4M3) and shape [E, N, K]: E * N * roundup(K, 128) * element size.
+ * Returns 0 for an invalid shape (the projection rules of the grouped calls). */
+size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K);
+
+/* Write the tiled copy of `src` (row-major, dtype `wdt`) into `dst` (device,
+ * moe_tiled_weight_bytes bytes, must not overlap src) on `stream`.  The result
+ * is used with MOE_W_BF16_TILED / MOE_W_FP8_E4M3_TILED. */
+int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K,
+                     hipStream_t stream);
+
 /* ---------------------------------------------------- grouped expert FFN -- */
 
-/* One projection's weights: w is [E, N, K] (bf16 or e4m3fn codes); scale is
- * [E, N/128, K/128] float32 for FP8 and ignored (may be NULL) for BF16. */
+/* One projection's weights: w is [E, N, K] (bf16 or e4m3fn codes), row-major
+ * or tiled as the call's weight dtype says; scale is [E, N/128, K/128] float32
+ * for FP8 and ignored (may be NULL) for BF16. */
 typedef struct {
   const void* w;
   const float* scale;

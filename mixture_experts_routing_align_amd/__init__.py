@@ -9,11 +9,13 @@ binding's entry points raises.
 Entry points (same names as the C ABI): ``moe_align``,
 ``moe_grouped_gate_up_silu``, ``moe_grouped_down``, ``moe_blend``,
 ``moe_layer_forward`` (via :class:`MoeLayer`), ``moe_layer_workspace_bytes``,
-``moe_align_max_total``, ``moe_active_cap``.
+``moe_align_max_total``, ``moe_active_cap``, ``moe_tile_weights``,
+``moe_tiled_weight_bytes``.
 
-Weights are passed as ``(w, scale)`` pairs: ``w`` is ``[E, N, K]`` (one expert:
-``[N, K]``) ``torch.uint8`` e4m3fn codes with ``scale`` float32
-``[E, N/128, K/128]``, or ``torch.bfloat16`` with ``scale`` None.
+Weights are passed as ``(w, scale)`` pairs: ``w`` is ``[E, N, K]``
+``torch.uint8`` e4m3fn codes with ``scale`` float32 ``[E, N/128, K/128]``, or
+``torch.bfloat16`` with ``scale`` None - or as the :class:`TiledWeight` that
+``moe_tile_weights`` makes from such a pair.
 """
 
 from __future__ import annotations
@@ -36,7 +38,9 @@ from ._ffi import (  # noqa: F401
     MOE_MAX_EXPERTS,
     MOE_OK,
     MOE_W_BF16,
+    MOE_W_BF16_TILED,
     MOE_W_FP8_E4M3,
+    MOE_W_FP8_E4M3_TILED,
     TABLE_FIELDS,
     MoeAlignTables,
     MoeLayerDesc,
@@ -133,7 +137,21 @@ def moe_align(topk_ids: torch.Tensor, E: int, BS: int, tables: Optional[AlignTab
 
 # ------------------------------------------------------------ grouped FFN --
 
-def weight_dtype(w: torch.Tensor) -> int:
+@dataclass
+class TiledWeight:
+    """Expert weights in the tiled layout of ``moe_tile_weights`` (flat bytes),
+    with the row-major shape they came from and their (unchanged) scales."""
+    w: torch.Tensor
+    scale: Optional[torch.Tensor]
+    wdt: int
+    shape: Tuple[int, int, int]
+
+
+def weight_dtype(w) -> int:
+    if isinstance(w, TiledWeight):
+        return w.wdt
+    if isinstance(w, tuple):
+        w = w[0]
     if w.dtype in (torch.uint8, torch.float8_e4m3fn):
         return MOE_W_FP8_E4M3
     if w.dtype == torch.bfloat16:
@@ -141,14 +159,44 @@ def weight_dtype(w: torch.Tensor) -> int:
     raise ValueError(f"unsupported weight dtype {w.dtype}")
 
 
-def _weight(wt: Optional[Weight]) -> Optional[MoeWeight]:
+def weight_shape(wt) -> Tuple[int, int, int]:
+    """(E, N, K) of a weight pair or a tiled weight; a single [N, K] matrix (a
+    shared expert) counts as E = 1."""
+    if isinstance(wt, TiledWeight):
+        return tuple(wt.shape)
+    shape = tuple(wt[0].shape)
+    return (1,) + shape if len(shape) == 2 else shape
+
+
+def _weight(wt) -> Optional[MoeWeight]:
     if wt is None:
         return None
+    if isinstance(wt, TiledWeight):
+        return MoeWeight(wt.w.data_ptr(), _ptr(wt.scale))
     w, s = wt
     _need(w.is_contiguous() and (s is None or s.is_contiguous()), "weights must be contiguous")
     if weight_dtype(w) == MOE_W_FP8_E4M3:
         _need(s is not None and s.dtype == torch.float32, "FP8 weights need float32 block scales")
     return MoeWeight(w.data_ptr(), _ptr(s))
+
+
+def moe_tiled_weight_bytes(wdt: int, E: int, N: int, K: int) -> int:
+    n = int(lib().moe_tiled_weight_bytes(wdt, E, N, K))
+    if n == 0:
+        raise MoeError(MOE_ERR_SHAPE, lib().moe_last_error().decode())
+    return n
+
+
+def moe_tile_weights(wt: Weight, stream=None) -> TiledWeight:
+    """The tiled copy of a row-major ``(w, scale)`` pair (a new device buffer)."""
+    w, s = wt
+    _need(w.is_contiguous(), "weights must be contiguous")
+    wdt = weight_dtype(w)
+    E, N, K = weight_shape(wt)
+    dst = torch.empty(moe_tiled_weight_bytes(wdt, E, N, K), dtype=torch.uint8, device=w.device)
+    _check(lib().moe_tile_weights(w.data_ptr(), dst.data_ptr(), wdt, E, N, K, _stream(stream)))
+    tiled = MOE_W_FP8_E4M3_TILED if wdt == MOE_W_FP8_E4M3 else MOE_W_BF16_TILED
+    return TiledWeight(dst, s, tiled, (E, N, K))
 
 
 def _ref(x):
@@ -160,12 +208,12 @@ def moe_grouped_gate_up_silu(x: torch.Tensor, gate: Weight, up: Weight, tables: 
                              sh_act: Optional[torch.Tensor] = None, stream=None) -> None:
     """act[p] = silu(Wg x) * (Wu x) per sorted slot position (+ the shared expert into sh_act)."""
     M, H = x.shape
-    E, I, H2 = gate[0].shape
+    E, I, H2 = weight_shape(gate)
     _need(H2 == H and x.dtype == torch.bfloat16, "x must be bf16 [M, H] matching the weights")
     _need(act.dtype == torch.float32 and act.shape[1] == I, "act must be float32 [max_total, I]")
-    S = 0 if sh_gate is None else sh_gate[0].shape[0]
+    S = 0 if sh_gate is None else weight_shape(sh_gate)[1]
     c = tables.as_c()
-    wdt = weight_dtype(gate[0])
+    wdt = weight_dtype(gate)
     _check(lib().moe_grouped_gate_up_silu(
         x.data_ptr(), wdt, ctypes.byref(_weight(gate)), ctypes.byref(_weight(up)), ctypes.byref(c),
         act.data_ptr(), _ref(_weight(sh_gate)), _ref(_weight(sh_up)), _ptr(sh_act),
@@ -176,13 +224,13 @@ def moe_grouped_down(act: torch.Tensor, down: Weight, tables: AlignTables, exper
                      top_k: int, BS: int, sh_down: Optional[Weight] = None, sh_act: Optional[torch.Tensor] = None,
                      sh_out: Optional[torch.Tensor] = None, stream=None) -> None:
     """expert_out[p] = Wd act[p] per sorted slot position (+ the shared expert into sh_out)."""
-    E, H, I = down[0].shape
+    E, H, I = weight_shape(down)
     _need(act.dtype == torch.float32 and act.shape[1] == I, "act must be float32 [max_total, I]")
     _need(expert_out.dtype == torch.float32 and expert_out.shape[1] == H, "expert_out must be float32 [max_total, H]")
-    S = 0 if sh_down is None else sh_down[0].shape[1]
+    S = 0 if sh_down is None else weight_shape(sh_down)[2]
     c = tables.as_c()
     _check(lib().moe_grouped_down(
-        act.data_ptr(), weight_dtype(down[0]), ctypes.byref(_weight(down)), ctypes.byref(c),
+        act.data_ptr(), weight_dtype(down), ctypes.byref(_weight(down)), ctypes.byref(c),
         expert_out.data_ptr(), _ref(_weight(sh_down)), _ptr(sh_act), _ptr(sh_out),
         M, H, I, S, E, top_k, BS, _stream(stream)))
 
@@ -208,15 +256,24 @@ WORKSPACE_REGIONS = TABLE_FIELDS + ("act", "expert_out", "sh_act", "sh_out")
 class MoeLayer:
     """Expert weights of one MoE layer plus the fused ``moe_layer_forward`` call."""
 
-    def __init__(self, gate: Weight, up: Weight, down: Weight, top_k: int, BS: int,
-                 sh_gate: Optional[Weight] = None, sh_up: Optional[Weight] = None, sh_down: Optional[Weight] = None):
+    def __init__(self, gate, up, down, top_k: int, BS: int, sh_gate=None, sh_up=None, sh_down=None):
         self.gate, self.up, self.down = gate, up, down
         self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
         self.top_k, self.BS = top_k, BS
-        self.E, self.I, self.H = gate[0].shape
-        self.S = 0 if sh_gate is None else sh_gate[0].shape[0]
-        self.wdt = weight_dtype(gate[0])
+        self.E, self.I, self.H = weight_shape(gate)
+        self.S = 0 if sh_gate is None else weight_shape(sh_gate)[1]
+        self.wdt = weight_dtype(gate)
+        kinds = {weight_dtype(w) for w in (gate, up, down, sh_gate, sh_up, sh_down) if w is not None}
+        _need(len(kinds) == 1, "all weights of a layer must share one dtype and layout")
         self._keep = None
+
+    def tiled(self, stream=None) -> "MoeLayer":
+        """The same layer with every weight in the tiled layout."""
+        def t(w):
+            return None if w is None or isinstance(w, TiledWeight) else moe_tile_weights(w, stream)
+
+        return MoeLayer(t(self.gate), t(self.up), t(self.down), self.top_k, self.BS,
+                        t(self.sh_gate), t(self.sh_up), t(self.sh_down))
 
     def desc(self, M: int, idt: int = MOE_IDX_I64) -> MoeLayerDesc:
         none = MoeWeight(None, None)

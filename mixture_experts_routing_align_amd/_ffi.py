@@ -19,6 +19,8 @@ MOE_IDX_I32 = 0
 MOE_IDX_I64 = 1
 MOE_W_BF16 = 0
 MOE_W_FP8_E4M3 = 1
+MOE_W_BF16_TILED = 2
+MOE_W_FP8_E4M3_TILED = 3
 MOE_MAX_EXPERTS = 1024
 
 c_void_p = ctypes.c_void_p
@@ -69,6 +71,8 @@ SIGNATURES = {
     "moe_layer_forward": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                   c_void_p]),
     "moe_layer_workspace_layout": (c_int, [P(MoeLayerDesc), P(c_size_t)]),
+    "moe_tiled_weight_bytes": (c_size_t, [c_int, c_int64, c_int32, c_int32]),
+    "moe_tile_weights": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int32, c_void_p]),
 }
 
 _LIB = None

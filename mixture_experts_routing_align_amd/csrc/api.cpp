@@ -70,15 +70,17 @@ int check_tables(const char* fn, const moe_align_tables* t, bool all) {
   return MOE_OK;
 }
 
+bool is_fp8(moe_weight_dtype wdt) { return wdt == MOE_W_FP8_E4M3 || wdt == MOE_W_FP8_E4M3_TILED; }
+bool is_tiled(moe_weight_dtype wdt) { return wdt == MOE_W_BF16_TILED || wdt == MOE_W_FP8_E4M3_TILED; }
+
 int check_weight(const char* fn, const char* name, const moe_weight* w, moe_weight_dtype wdt) {
   if (w == nullptr || w->w == nullptr) return fail(MOE_ERR_NULL, "%s: %s weights are NULL", fn, name);
-  if (wdt == MOE_W_FP8_E4M3 && w->scale == nullptr)
-    return fail(MOE_ERR_NULL, "%s: %s FP8 block scales are NULL", fn, name);
+  if (is_fp8(wdt) && w->scale == nullptr) return fail(MOE_ERR_NULL, "%s: %s FP8 block scales are NULL", fn, name);
   return MOE_OK;
 }
 
 int check_wdt(const char* fn, moe_weight_dtype wdt) {
-  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3)
+  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3 && wdt != MOE_W_BF16_TILED && wdt != MOE_W_FP8_E4M3_TILED)
     return fail(MOE_ERR_SHAPE, "%s: unknown weight dtype %d", fn, (int)wdt);
   return MOE_OK;
 }
@@ -87,7 +89,7 @@ int check_wdt(const char* fn, moe_weight_dtype wdt) {
 // blocks; BF16 needs K in whole 32-deep MFMA steps and N in whole 16-row tiles.
 int check_projection(const char* fn, const char* name, moe_weight_dtype wdt, int32_t N, int32_t K) {
   if (N < 1 || K < 1) return fail(MOE_ERR_SHAPE, "%s: %s is %dx%d", fn, name, N, K);
-  if (wdt == MOE_W_FP8_E4M3) {
+  if (is_fp8(wdt)) {
     if (N % moe::kFp8Block || K % moe::kFp8Block)
       return fail(MOE_ERR_SHAPE, "%s: FP8 %s is %dx%d, not whole 128x128 scale blocks", fn, name, N, K);
   } else if (N % 16 || K % 32) {
@@ -107,6 +109,36 @@ void fill_tables(moe::GroupedArgs& a, const moe_align_tables* t) {
   a.expert_counts = t->expert_counts;
   a.active_experts = t->active_experts;
   a.active_count = t->active_count;
+}
+
+moe::GroupedArgs gate_up_args(const void* x_bf16, const moe_weight* gate, const moe_weight* up,
+                              const moe_align_tables* t, float* act, const moe_weight* sh_gate,
+                              const moe_weight* sh_up, float* sh_act, int64_t M, int32_t H, int32_t I, int32_t S,
+                              int32_t top_k, int32_t cap) {
+  moe::GroupedArgs a{};
+  a.x = x_bf16;
+  a.w0 = gate->w;
+  a.s0 = gate->scale;
+  a.w1 = up->w;
+  a.s1 = up->scale;
+  a.out = act;
+  a.N = I;
+  a.K = H;
+  if (S > 0) {
+    a.sx = x_bf16;
+    a.sw0 = sh_gate->w;
+    a.ss0 = sh_gate->scale;
+    a.sw1 = sh_up->w;
+    a.ss1 = sh_up->scale;
+    a.sout = sh_act;
+    a.sN = S;
+    a.sK = H;
+  }
+  fill_tables(a, t);
+  a.M = (int)M;
+  a.top_k = top_k;
+  a.cap = cap;
+  return a;
 }
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -157,7 +189,7 @@ int layout(const moe_layer_desc* d, size_t off[13]) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -210,31 +242,9 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
       return rc;
     if (sh_act == nullptr) return fail(MOE_ERR_NULL, "%s: sh_act is NULL with S > 0", fn);
   }
-  moe::GroupedArgs a{};
-  a.x = x_bf16;
-  a.w0 = gate->w;
-  a.s0 = gate->scale;
-  a.w1 = up->w;
-  a.s1 = up->scale;
-  a.out = act;
-  a.N = I;
-  a.K = H;
-  if (S > 0) {
-    a.sx = x_bf16;
-    a.sw0 = sh_gate->w;
-    a.ss0 = sh_gate->scale;
-    a.sw1 = sh_up->w;
-    a.ss1 = sh_up->scale;
-    a.sout = sh_act;
-    a.sN = S;
-    a.sK = H;
-  }
-  fill_tables(a, t);
-  a.M = (int)M;
-  a.top_k = top_k;
-  a.cap = s.cap;
-  return hip_status(moe::launch_grouped_gate_up(a, wdt == MOE_W_FP8_E4M3, moe::grouped_row_tiles(M, top_k), stream),
-                    fn);
+  const moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
+  return hip_status(
+      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
 }
 
 int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down, const moe_align_tables* t,
@@ -276,7 +286,8 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
   a.M = (int)M;
   a.top_k = top_k;
   a.cap = s.cap;
-  return hip_status(moe::launch_grouped_down(a, wdt == MOE_W_FP8_E4M3, moe::grouped_row_tiles(M, top_k), stream), fn);
+  return hip_status(
+      moe::launch_grouped_down(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
 }
 
 int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights, const int32_t* token_to_perm,
@@ -291,6 +302,28 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
   return hip_status(moe::launch_blend(static_cast<uint16_t*>(out_bf16), expert_out, topk_weights, token_to_perm,
                                       sh_out, (int)M, H, top_k, stream),
                     fn);
+}
+
+size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K) {
+  const char* fn = "moe_tiled_weight_bytes";
+  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3) {
+    fail(MOE_ERR_SHAPE, "%s: source dtype %d is not a row-major dtype", fn, (int)wdt);
+    return 0;
+  }
+  if (E < 1 || check_projection(fn, "weights", wdt, N, K) != MOE_OK) {
+    if (E < 1) fail(MOE_ERR_SHAPE, "%s: E=%lld", fn, (long long)E);
+    return 0;
+  }
+  return moe::tiled_weight_bytes(is_fp8(wdt), E, N, K);
+}
+
+int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K,
+                     hipStream_t stream) {
+  const char* fn = "moe_tile_weights";
+  if (moe_tiled_weight_bytes(wdt, E, N, K) == 0) return MOE_ERR_SHAPE;
+  if (src == nullptr || dst == nullptr) return fail(MOE_ERR_NULL, "%s: src or dst is NULL", fn);
+  if (src == dst) return fail(MOE_ERR_SHAPE, "%s: src and dst must not alias", fn);
+  return hip_status(moe::launch_tile_weights(src, dst, is_fp8(wdt), E, N, K, stream), fn);
 }
 
 int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[13]) {
@@ -342,11 +375,31 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   float* sh_act = shared ? reinterpret_cast<float*>(ws + off[10]) : nullptr;
   float* sh_out = shared ? reinterpret_cast<float*>(ws + off[11]) : nullptr;
 
-  if ((rc = moe_align(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, stream))) return rc;
-  if ((rc = moe_grouped_gate_up_silu(x_bf16, d->wdt, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,
-                                     shared ? &d->sh_up : nullptr, sh_act, d->M, d->H, d->I, d->S, d->E, d->top_k,
-                                     d->BS, stream)))
-    return rc;
+  const int64_t n = d->M * d->top_k;
+  if (n <= moe::kFusedAlignMaxSlots) {
+    // few slots: every gate+up workgroup aligns topk_ids itself (in LDS) and
+    // one writes the tables, which saves the align launch and its latency
+    moe::GroupedArgs a = gate_up_args(x_bf16, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,
+                                      shared ? &d->sh_up : nullptr, sh_act, d->M, d->H, d->I, d->S, d->top_k,
+                                      moe_active_cap(n, d->E));
+    a.ids = topk_ids;
+    a.ids64 = d->idt == MOE_IDX_I64;
+    a.n = (int)n;
+    a.E = d->E;
+    a.BS = d->BS;
+    a.max_total = (int)moe_align_max_total(n, d->E, d->BS);
+    a.tables = to_align_out(t);
+    rc = hip_status(moe::launch_grouped_gate_up(a, is_fp8(d->wdt), is_tiled(d->wdt),
+                                                moe::grouped_row_tiles(d->M, d->top_k), stream),
+                    fn);
+    if (rc) return rc;
+  } else {
+    if ((rc = moe_align(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, stream))) return rc;
+    if ((rc = moe_grouped_gate_up_silu(x_bf16, d->wdt, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,
+                                       shared ? &d->sh_up : nullptr, sh_act, d->M, d->H, d->I, d->S, d->E, d->top_k,
+                                       d->BS, stream)))
+      return rc;
+  }
   if ((rc = moe_grouped_down(act, d->wdt, &d->down, &t, expert_out, shared ? &d->sh_down : nullptr, sh_act, sh_out,
                              d->M, d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))
     return rc;

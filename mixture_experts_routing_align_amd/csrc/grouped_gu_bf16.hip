@@ -1,0 +1,10 @@
+// Grouped gate+up with BF16 weights (kernels in grouped_impl.h).
+#include "grouped_impl.h"
+
+namespace moe {
+
+hipError_t launch_gate_up_bf16(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s) {
+  return grouped_detail::launch<false, true>(a, rt, rowcap, tiled, s);
+}
+
+}  // namespace moe

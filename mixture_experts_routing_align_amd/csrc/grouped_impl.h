@@ -1,0 +1,614 @@
+// Grouped expert projections for gfx950: gate+up with SiLU, and down.
+//
+// What is computed (metrale fp8_moe_grouped.rs: module doc, and the gate+up and
+// down launchers' docs; nbxtensor moe_decode_vec.py: the SwiGLU epilogue):
+//   gate+up: act[p, c] = silu(g) * u, g = sum_k Wg[e][c][k] x[t][k],
+//            u = sum_k Wu[e][c][k] x[t][k], for each sorted position p holding a
+//            slot of active expert e (t = slot / top_k); the shared expert does
+//            the same for every token t into sh_act[t, c].
+//   down:    out[p, c] = sum_k Wd[e][c][k] act[p][k] (shared: rows are tokens).
+// A workgroup owns one active expert (or one group of shared-expert rows) and a
+// 64-column tile of the output, and applies each weight row it streams from HBM
+// to every row routed to that expert, so each expert's weights are read once
+// per pass.  Rows of the intermediates are sorted positions.
+//
+// gfx950 design (not the pages' CUDA geometry):
+//  * Matrix cores: v_mfma_f32_16x16x32_bf16.  The weights are the A operand
+//    (16 output columns per wave), the expert's rows the B operand (16-row
+//    tiles; rows past the expert's count are fed as zeros).  FP8 e4m3 codes
+//    convert exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, scale
+//    1); bf16 activations are exact, so the only rounding is the float32
+//    accumulation.  Each 128-deep FP8 scale block is accumulated alone and then
+//    multiplied by its scale.  The down projection's float32 input is split into
+//    bf16 hi + lo and both halves go through the matrix core, so it keeps ~16
+//    bits of the input's mantissa.
+//  * Memory: each lane streams 16-byte (dwordx4) loads of its weight row,
+//    several 128-deep chunks ahead in a register ring.  The expert's activation
+//    rows are staged in LDS once per workgroup and read as B operands by all
+//    four waves: for the whole depth at once when they fit ("resident": the
+//    weight stream then runs with no barrier at all), else 128 deep at a time
+//    in two LDS slots with one barrier per chunk.  LDS rows are padded by 16
+//    bytes against bank conflicts.
+//  * Row invariance: a row's value depends only on its own inputs: every output
+//    element is the same sequence of MFMA k-steps, scale FMAs and chunk sums
+//    whatever tile, slot, pass or staging mode the row goes through, and the
+//    rows per pass come from the shape class, never from the routing.
+//  * Graph replay: the grid is (ceil(N/64), cap + shared row groups), sized from
+//    shapes only; a workgroup past the device-side active count exits at once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "align_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace grouped_detail {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;  // 4 wave64 per workgroup
+constexpr int kWaveCols = 16;   // output columns per wave: one MFMA tile edge
+constexpr int kTileCols = 64;   // output columns per workgroup
+constexpr int kKC = 128;        // depth of one chunk (= one FP8 scale block)
+constexpr int kPad = 8;         // bf16 elements of padding per staged row (16 B)
+constexpr int kMaxRowCap = 128; // most rows one pass stages
+constexpr size_t kResidentLdsBudget = 80 * 1024;
+constexpr int kMaxScaleBlocks = 128;  // FP8 depth limit: 128 scale blocks = 16384
+
+__host__ __device__ constexpr int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// 8 FP8 e4m3 codes (two dwords, lowest byte first) -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Element offset, inside a 128-deep chunk, of the 8 consecutive k a lane of
+// quad q feeds to MFMA step s.  The A and B operands use the same map, so the
+// k order inside one MFMA is a permutation the product does not see.
+//  FP8: one 16-byte load holds 16 codes = steps s and s+1 (s even).
+//  BF16: one 16-byte load holds 8 elements = one step.
+template <bool FP8>
+__device__ __forceinline__ int k_of_step(int s, int q) {
+  return FP8 ? ((s >> 1) * 64 + q * 16 + (s & 1) * 8) : (s * 32 + q * 8);
+}
+
+// LDS bytes of the fused alignment region for E experts and n slots.
+__host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
+  return ((size_t)kWaves * E + E + (E + 1) + E + 2 * kWaves + 2 + n) * sizeof(int);
+}
+
+template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
+__global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int rowcap, int ctw, size_t xs_bytes) {
+  constexpr int NS = GATE_UP ? 2 : 1;   // weight streams (gate, up) or (down)
+  constexpr int NX = GATE_UP ? 1 : 2;   // B planes: bf16 x, or bf16 hi + lo of act
+  constexpr int WL = FP8 ? 2 : 4;       // 16-byte weight loads per lane per chunk
+  constexpr int ESZ = FP8 ? 1 : 2;      // weight element bytes
+  constexpr int NBUF = RESIDENT ? 3 : 2;  // weight chunks in the register ring
+  constexpr int EPP = GATE_UP ? 8 : 4;  // source elements per 16-byte staging piece
+  constexpr int SL = kMaxScaleBlocks / 64;  // scale registers per stream (one scale per lane)
+
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [slot][plane][row][stride], then the align region
+  __shared__ int s_src[kMaxRowCap];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int by = blockIdx.y;
+
+  // ---- which expert / rows this workgroup serves
+  const bool routed = by < p.cap;
+  int e = 0, rows = 0, row_base = 0, N, K;
+  const int* fsrc = nullptr;  // fused: sources of all of the expert's rows
+  if (routed) {
+    N = p.N;
+    K = p.K;
+    if constexpr (FUSED) {
+      int* a = reinterpret_cast<int*>(reinterpret_cast<char*>(xs) + xs_bytes);
+      const int E = p.E;
+      const align_dev::ExpertLds s{a, a + kWaves * E, a + kWaves * E + E, a + kWaves * E + 2 * E + 1,
+                                   a + kWaves * E + 3 * E + 1, a + kWaves * E + 3 * E + 1 + kWaves,
+                                   a + kWaves * E + 3 * E + 1 + 2 * kWaves};
+      int* src_all = s.scal + 2;
+      const IdT* ids = static_cast<const IdT*>(p.ids);
+      const int nbits = align_dev::id_bits(E);
+      align_dev::count_pass<kWaves>(ids, p.n, E, nbits, s.cnt);
+      align_dev::expert_scan<kWaves>(s, E, p.BS);
+      const int nact = s.scal[0];
+      if (by < nact) {
+        e = s.active[by];
+        rows = s.count[e];
+        row_base = s.off[e];
+        align_dev::expert_rows<kWaves>(ids, p.n, E, nbits, s.cnt, e, p.top_k, src_all);
+      }
+      if (blockIdx.x == 0 && by == 0) {  // the tables the later steps read
+        __syncthreads();  // expert_rows is done with the bases scatter_pass advances
+        align_dev::scatter_pass<kWaves>(ids, p.n, E, nbits, s.cnt, s.off, p.tables.sorted_token_ids,
+                                        p.tables.token_to_perm);
+        align_dev::write_rest<kWaves>(s, p.n, E, p.BS, p.max_total, p.cap, p.tables);
+      }
+      if (by >= nact) return;
+      fsrc = src_all;
+    } else {
+      const int nact = *p.active_count;  // both loads in flight together
+      const int e0 = p.active_experts[by];
+      if (by >= nact) return;
+      e = e0;
+    }
+  } else {
+    N = p.sN;
+    K = p.sK;
+  }
+
+  const char *W0, *W1 = nullptr;
+  const float *S0 = nullptr, *S1 = nullptr;
+  const char* X;
+  float* OUT;
+  if (routed) {
+    const size_t wstride = (size_t)N * (TILED ? round_up(K, kKC) : K) * ESZ;
+    W0 = static_cast<const char*>(p.w0) + (size_t)e * wstride;
+    if (GATE_UP) W1 = static_cast<const char*>(p.w1) + (size_t)e * wstride;
+    if (FP8) {
+      const size_t sstride = (size_t)(N / kFp8Block) * (K / kFp8Block);
+      S0 = p.s0 + (size_t)e * sstride;
+      if (GATE_UP) S1 = p.s1 + (size_t)e * sstride;
+    }
+    X = static_cast<const char*>(p.x);
+    OUT = p.out;
+  } else {
+    W0 = static_cast<const char*>(p.sw0);
+    W1 = static_cast<const char*>(p.sw1);
+    S0 = p.ss0;
+    S1 = p.ss1;
+    X = static_cast<const char*>(p.sx);
+    OUT = p.sout;
+  }
+  // this workgroup's 64-column tiles: [t_begin, t_end)
+  const int t_begin = blockIdx.x * ctw;
+  const int t_end = min(t_begin + ctw, (N + kTileCols - 1) / kTileCols);
+  if (t_begin >= t_end) return;
+  const int nch = (K + kKC - 1) / kKC;
+  const int nv = (t_end - t_begin) * nch;  // (tile, chunk) steps of one pass
+  const int kpad = TILED ? round_up(K, kKC) : K;
+  const int kblocks = K / kFp8Block;
+
+  // a wave whose 16 columns lie past N reads the tile's first columns (valid
+  // memory), multiplies nothing and stores nothing
+  auto wave_col = [&](int t, bool& on) {
+    const int c0 = t * kTileCols + wave * kWaveCols;
+    on = c0 < N;
+    return on ? c0 : t * kTileCols;
+  };
+  // row-major: this lane's weight row (A operand row r16 of the wave's tile);
+  // tiled: the wave's 16-row tile, one contiguous run of 128-deep fragments
+  auto lane_offset = [&](int wcol) -> size_t {
+    return TILED ? (size_t)(wcol / kWaveCols) * kpad * kWaveCols * ESZ + lane * 16 : (size_t)(wcol + r16) * K * ESZ;
+  };
+
+  // load cursor: tile `lt`, chunk `lc` of the next weight load, and this lane's
+  // pointers into that tile (recomputed only when the tile changes)
+  int lt = t_begin, lc = 0;
+  const char* lp0 = nullptr;
+  const char* lp1 = nullptr;
+  auto set_load_tile = [&](int t) {
+    bool on;
+    const size_t lo = lane_offset(wave_col(t, on));
+    lp0 = W0 + lo;
+    if (GATE_UP) lp1 = W1 + lo;
+  };
+  // unconditional loads of the cursor's chunk, then advance the cursor (past the
+  // last step it stays on the last chunk, which is then loaded again): the
+  // steady state has no branch around loads and no integer division
+  auto load_next = [&](uint4 (&wr)[NS][WL]) {
+#pragma unroll
+    for (int j = 0; j < WL; ++j) {
+      if (TILED) {
+        const size_t off = (size_t)lc * kKC * kWaveCols * ESZ + j * 1024;
+        wr[0][j] = *reinterpret_cast<const uint4*>(lp0 + off);
+        if (GATE_UP) wr[NS - 1][j] = *reinterpret_cast<const uint4*>(lp1 + off);
+      } else {
+        // bf16 depth past K (a partial last chunk) loads a valid address and is zeroed
+        const int kk = lc * kKC + k_of_step<FP8>(FP8 ? 2 * j : j, q);
+        const int kc = FP8 ? kk : min(kk, K - 8);
+        uint4 v0 = *reinterpret_cast<const uint4*>(lp0 + (size_t)kc * ESZ);
+        uint4 v1 = GATE_UP ? *reinterpret_cast<const uint4*>(lp1 + (size_t)kc * ESZ) : v0;
+        if (!FP8 && kk >= K) v0 = v1 = uint4{0u, 0u, 0u, 0u};
+        wr[0][j] = v0;
+        if (GATE_UP) wr[NS - 1][j] = v1;
+      }
+    }
+    if (lc + 1 < nch) {
+      ++lc;
+    } else if (lt + 1 < t_end) {
+      ++lt;
+      lc = 0;
+      set_load_tile(lt);
+    }
+  };
+
+  // the first weight chunks of the first pass go out before anything else
+  uint4 wb[NBUF][NS][WL];
+  set_load_tile(lt);
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j]);
+
+  if (routed && !FUSED) {
+    rows = p.expert_counts[e];
+    row_base = p.expert_offsets[e];
+  } else if (!routed) {
+    row_base = (by - p.cap) * rowcap;
+    rows = min(rowcap, p.M - row_base);
+  }
+
+  // the FP8 scales of a tile's 16 columns of this wave, one 128-deep block per lane
+  float sreg[NS][SL];
+  auto load_scales = [&](int t) {
+    if (!FP8) return;
+    bool on;
+    const int wcol = wave_col(t, on);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const float* sw = (st == 0 ? S0 : S1) + (size_t)(wcol / kFp8Block) * kblocks;
+#pragma unroll
+      for (int i = 0; i < SL; ++i) sreg[st][i] = lane + 64 * i < kblocks ? sw[lane + 64 * i] : 0.f;
+    }
+  };
+  auto scale_of = [&](int st, int c) -> float {
+    if (SL == 1 || c < 64) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sreg[st][0]), c & 63));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sreg[st][SL - 1]), c & 63));
+  };
+
+  const int stride = (RESIDENT ? K : kKC) + kPad;     // staged row length (bf16 elements)
+  const int plane = rowcap * stride;                  // elements per B plane
+  const int pieces = (RESIDENT ? K : kKC) / EPP;      // 16-byte pieces per staged row
+
+  // one 16-byte piece of a source row, as loaded (bf16 x) or as fp32 act
+  auto load_piece = [&](int src, int kk) -> uint4 {
+    if (kk >= K) return uint4{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const uint4*>(X + ((size_t)src * K + kk) * (GATE_UP ? 2 : 4));
+  };
+  // write a piece at element offset `col` of staged row `r` in LDS slot `slot`
+  auto store_piece = [&](uint4 v, int slot, int r, int col) {
+    uint16_t* base = xs + (size_t)slot * NX * plane + r * stride + col;
+    if (GATE_UP) {
+      *reinterpret_cast<uint4*>(base) = v;
+    } else {
+      const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = bf16_rne_bits(f[i]);
+        lo[i] = bf16_rne_bits(f[i] - bf16_bits_to_f32(hi[i]));
+      }
+      uint2 h2, l2;
+      h2.x = hi[0] | ((uint32_t)hi[1] << 16);
+      h2.y = hi[2] | ((uint32_t)hi[3] << 16);
+      l2.x = lo[0] | ((uint32_t)lo[1] << 16);
+      l2.y = lo[2] | ((uint32_t)lo[3] << 16);
+      *reinterpret_cast<uint2*>(base) = h2;
+      *reinterpret_cast<uint2*>(base + plane) = l2;
+    }
+  };
+
+  for (int r0 = 0; r0 < rows; r0 += rowcap) {
+    const int nr = min(rowcap, rows - r0);
+    const int nrt = (nr + 15) >> 4;
+
+    if (r0 > 0) {  // a later pass streams the weights again from the start
+      lt = t_begin;
+      lc = 0;
+      set_load_tile(lt);
+#pragma unroll
+      for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j]);
+    }
+    load_scales(t_begin);
+
+    // the source rows of this pass: fused from the LDS row list, else from the
+    // tables (token of a slot for gate+up, the sorted position for down)
+    const int* srcv = s_src;
+    if (FUSED && routed) {
+      srcv = fsrc + r0;
+      __syncthreads();
+    } else {
+      int my_src = 0;
+      if (tid < nr) {
+        if (!routed)
+          my_src = row_base + r0 + tid;                                   // token
+        else if (GATE_UP)
+          my_src = p.sorted_token_ids[row_base + r0 + tid] / p.top_k;     // token of the slot
+        else
+          my_src = row_base + r0 + tid;                                   // sorted position
+      }
+      __syncthreads();  // the previous pass is done with LDS
+      if (tid < nr) s_src[tid] = my_src;
+      __syncthreads();
+    }
+
+    f32x4 acc[NS][RT];
+    auto zero_acc = [&]() {
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[st][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    zero_acc();
+
+    // multiply chunk c: A from registers, B from LDS slot `slot` at element `kb`
+    auto compute = [&](const uint4 (&wc)[NS][WL], int slot, int kb, int c) {
+      const int k0 = c * kKC;
+      bf16x8 a[NS][4];
+#pragma unroll
+      for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (FP8) {
+            const uint4 v = wc[st][s >> 1];
+            a[st][s] = (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
+          } else {
+            a[st][s] = as_bf16x8(wc[st][s]);
+          }
+        }
+      float sc[NS];
+      if (FP8) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) sc[st] = scale_of(st, c);
+      }
+      const uint16_t* xb = xs + (size_t)slot * NX * plane + kb;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (rt < nrt) {
+          // B column n = row r16 of the tile.  Rows past the expert's count
+          // (stale LDS, or the last staged row again when the tile is wider
+          // than the staged rows) only reach output columns that are never
+          // stored: each MFMA output column depends on its own B column alone.
+          const int rowc = min(rt * 16 + r16, rowcap - 1);
+          bf16x8 b[NX][4];
+#pragma unroll
+          for (int x = 0; x < NX; ++x)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              b[x][s] = as_bf16x8(
+                  *reinterpret_cast<const uint4*>(xb + x * plane + rowc * stride + k_of_step<FP8>(s, q)));
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            if (FP8) {
+              f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int x = 0; x < NX; ++x) t = mfma(a[st][s], b[x][s], t);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[st][rt][i] = fmaf(sc[st], t[i], acc[st][rt][i]);
+            } else {
+              // bf16 depth comes in whole 32-deep steps; steps past K are skipped
+#pragma unroll
+              for (int s = 0; s < 4; ++s)
+                if (k0 + s * 32 < K)
+#pragma unroll
+                  for (int x = 0; x < NX; ++x) acc[st][rt] = mfma(a[st][s], b[x][s], acc[st][rt]);
+            }
+          }
+        }
+      }
+    };
+
+    // lane holds columns wcol + 4q .. +3 of tile row r16
+    auto epilogue = [&](int wcol) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = rt * 16 + r16;
+        if (rt < nrt && r < nr) {
+          float4 v;
+          if (GATE_UP) {
+            const f32x4 g = acc[0][rt], u = acc[NS - 1][rt];
+            v.x = g[0] / (1.0f + expf(-g[0])) * u[0];
+            v.y = g[1] / (1.0f + expf(-g[1])) * u[1];
+            v.z = g[2] / (1.0f + expf(-g[2])) * u[2];
+            v.w = g[3] / (1.0f + expf(-g[3])) * u[3];
+          } else {
+            v.x = acc[0][rt][0];
+            v.y = acc[0][rt][1];
+            v.z = acc[0][rt][2];
+            v.w = acc[0][rt][3];
+          }
+          *reinterpret_cast<float4*>(OUT + (size_t)(row_base + r0 + r) * N + wcol + 4 * q) = v;
+        }
+      }
+    };
+
+    // compute cursor: tile `ct`, chunk `cc`; one step multiplies the chunk and,
+    // at a tile's last chunk, stores the tile and moves to the next
+    int ct = t_begin, cc = 0;
+    bool con;
+    int cwcol = wave_col(ct, con);
+    auto step = [&](const uint4 (&wc)[NS][WL], int slot, int kb) {
+      if (con) compute(wc, slot, kb, cc);
+      if (cc + 1 < nch) {
+        ++cc;
+      } else {
+        if (con) epilogue(cwcol);
+        zero_acc();
+        cc = 0;
+        if (++ct < t_end) {
+          cwcol = wave_col(ct, con);
+          load_scales(ct);
+        }
+      }
+    };
+
+    if (RESIDENT) {
+      // every row of this pass, the whole depth
+      const int total = nr * pieces;
+      for (int base = 0; base < total; base += 8 * kThreads) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + u * kThreads + tid;
+          v[u] = idx < total ? load_piece(srcv[idx / pieces], (idx % pieces) * EPP) : uint4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + u * kThreads + tid;
+          if (idx < total) store_piece(v[u], 0, idx / pieces, (idx % pieces) * EPP);
+        }
+      }
+      __syncthreads();
+      // steady state: the load of step v + NBUF - 1 goes out before step v is
+      // multiplied; no barrier and no branch around loads
+      for (int v0 = 0; v0 < nv; v0 += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          load_next(wb[(j + NBUF - 1) % NBUF]);
+          if (v0 + j < nv) step(wb[j], 0, cc * kKC);
+        }
+      }
+    } else {
+      // 128 deep at a time through two LDS slots, one barrier per step
+      constexpr int XP = (RT * 16 * (kKC / EPP) + kThreads - 1) / kThreads;
+      const int total = nr * pieces;
+      uint4 xr[XP];
+      auto load_x = [&](int c) {
+#pragma unroll
+        for (int u = 0; u < XP; ++u) {
+          const int idx = u * kThreads + tid;
+          xr[u] = idx < total ? load_piece(srcv[idx / pieces], c * kKC + (idx % pieces) * EPP)
+                              : uint4{0u, 0u, 0u, 0u};
+        }
+      };
+      auto store_x = [&](int slot) {
+#pragma unroll
+        for (int u = 0; u < XP; ++u) {
+          const int idx = u * kThreads + tid;
+          if (idx < total) store_piece(xr[u], slot, idx / pieces, (idx % pieces) * EPP);
+        }
+      };
+      load_x(0);
+      store_x(0);
+      __syncthreads();
+      for (int v0 = 0; v0 < nv; v0 += NBUF) {
+#pragma unroll
+        for (int j = 0; j < NBUF; ++j) {
+          const int v = v0 + j;
+          if (v < nv) {
+            load_x(cc + 1 < nch ? cc + 1 : 0);  // issued before the weights: waiting on it leaves them in flight
+            load_next(wb[(j + NBUF - 1) % NBUF]);
+            step(wb[j], v & 1, 0);
+            if (v + 1 < nv) store_x((v + 1) & 1);
+            __syncthreads();
+          }
+        }
+      }
+    }
+    __syncthreads();  // the next pass may restage LDS
+  }
+}
+
+// compute units of the current device (cached per device)
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
+hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, int rows_y, hipStream_t s) {
+  auto kern = grouped_kernel<FP8, GATE_UP, RT, RESIDENT, TILED, FUSED, IdT>;
+  const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
+  static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
+  if (lds > 64 * 1024 && lds > configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured = lds;
+  }
+  // column tiles per workgroup: the fewest that let every workgroup of the
+  // worst case (all `rows_y` experts active) be resident at once
+  static size_t occ_lds = (size_t)-1;  // occupancy of this kernel at the last LDS size asked
+  static int occ_per_cu = 0;
+  if (occ_lds != lds) {
+    int per_cu = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                                      kThreads, lds);
+    if (e != hipSuccess) return e;
+    occ_per_cu = per_cu;
+    occ_lds = lds;
+  }
+  const int slots = std::max(1, occ_per_cu) * device_cus();
+  int ctw = 1;
+  while (ctw < tiles && (long long)rows_y * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
+  const dim3 grid((tiles + ctw - 1) / ctw, rows_y);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, rowcap, ctw, xs_bytes);
+  return hipGetLastError();
+}
+
+template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED>
+hipError_t launch_fused_or_not(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, int rows_y,
+                               hipStream_t s) {
+  if (GATE_UP && a.ids != nullptr) {
+    if (a.ids64)
+      return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, rows_y, s);
+    return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, rows_y, s);
+  }
+  return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, rows_y, s);
+}
+
+template <bool FP8, bool GATE_UP, int RT, bool TILED>
+hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
+  constexpr int NX = GATE_UP ? 1 : 2;
+  const int kmax = (a.sw0 != nullptr && a.sK > a.K) ? a.sK : a.K;
+  const size_t resident = (size_t)NX * rowcap * (kmax + kPad) * 2;
+  const size_t chunked = (size_t)2 * NX * rowcap * (kKC + kPad) * 2;
+  const int nmax = (a.sw0 != nullptr && a.sN > a.N) ? a.sN : a.N;
+  const int shared_groups = a.sw0 != nullptr ? (a.M + rowcap - 1) / rowcap : 0;
+  const int tiles = (nmax + kTileCols - 1) / kTileCols;
+  const int rows_y = a.cap + shared_groups;
+  if (resident <= kResidentLdsBudget)
+    return launch_fused_or_not<FP8, GATE_UP, RT, true, TILED>(a, rowcap, resident, tiles, rows_y, s);
+  return launch_fused_or_not<FP8, GATE_UP, RT, false, TILED>(a, rowcap, chunked, tiles, rows_y, s);
+}
+
+template <bool FP8, bool GATE_UP, bool TILED>
+hipError_t launch_layout(const GroupedArgs& a, int rt, int rowcap, hipStream_t s) {
+  switch (rt) {
+    case 1: return launch_rt<FP8, GATE_UP, 1, TILED>(a, rowcap, s);
+    case 2: return launch_rt<FP8, GATE_UP, 2, TILED>(a, rowcap, s);
+    case 4: return launch_rt<FP8, GATE_UP, 4, TILED>(a, rowcap, s);
+    default: return launch_rt<FP8, GATE_UP, 8, TILED>(a, rowcap, s);
+  }
+}
+
+template <bool FP8, bool GATE_UP>
+hipError_t launch(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s) {
+  return tiled ? launch_layout<FP8, GATE_UP, true>(a, rt, rowcap, s) : launch_layout<FP8, GATE_UP, false>(a, rt, rowcap, s);
+}
+
+}  // namespace grouped_detail
+}  // namespace moe

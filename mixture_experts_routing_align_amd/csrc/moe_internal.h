@@ -50,15 +50,28 @@ struct GroupedArgs {
   const int32_t* active_experts;
   const int32_t* active_count;
   int M, top_k, cap;
+  // fused alignment (gate+up only; ids != nullptr): every routed workgroup
+  // aligns topk_ids in LDS itself, and workgroup (0, 0) writes `tables`
+  const void* ids;
+  int ids64, n, E, BS, max_total;
+  AlignOut tables;
 };
+
+// Largest slot count the fused align + gate+up kernel takes (its per-workgroup
+// alignment cost grows with n; above this the layer runs the align kernel).
+constexpr int kFusedAlignMaxSlots = 2048;
 
 // Row tiles (16 rows each) one workgroup keeps in registers per pass over the
 // weights; chosen from the shape class (the most rows an expert can hold), never
 // from the routing.
 int grouped_row_tiles(int64_t M, int top_k);
 
-hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, int row_tiles, hipStream_t s);
-hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, int row_tiles, hipStream_t s);
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
+
+// The tiled (MFMA-fragment-ordered) copy of row-major [E, N, K] weights.
+size_t tiled_weight_bytes(bool fp8, int64_t E, int N, int K);
+hipError_t launch_tile_weights(const void* src, void* dst, bool fp8, int64_t E, int N, int K, hipStream_t s);
 
 hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,
                         const float* sh_out, int M, int H, int top_k, hipStream_t s);

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 @pytest.mark.parametrize("seed", range(5))

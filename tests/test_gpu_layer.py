@@ -267,3 +267,134 @@ def test_graph_replay_follows_new_routing(moe):
         ref = oracle_layer(model, x, ids, w)
         ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
         assert ok, (r, err, bound)
+
+
+# ------------------------------------------------------------- tiled layout --
+
+def _tiled_reference(bits: np.ndarray, fp8: bool) -> np.ndarray:
+    """The documented tiled layout, rebuilt on the host: per expert, 16-row
+    tiles; per tile, 128-deep chunks (zero-padded); per chunk, 1 KB fragments
+    where lane l's 16 bytes hold row 16t + l%16 at the k its quad l/16 feeds."""
+    E, N, K = bits.shape
+    esz = 1 if fp8 else 2
+    raw = bits.view(np.uint8).reshape(E, N, K * esz)
+    kp = -(-K // 128) * 128
+    out = np.zeros((E, N // 16, kp // 128, (128 * esz) // 64, 64, 16), dtype=np.uint8)
+    for t in range(N // 16):
+        for c in range(kp // 128):
+            for j in range((128 * esz) // 64):
+                for lane in range(64):
+                    row, qd = 16 * t + lane % 16, lane // 16
+                    kk = c * 128 + (j * 64 + qd * 16 if fp8 else j * 32 + qd * 8)
+                    if kk < K:
+                        out[:, t, c, j, lane] = raw[:, row, kk * esz:kk * esz + 16]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("fp8,E,N,K", [(True, 2, 256, 384), (False, 3, 48, 96), (False, 1, 32, 256)])
+def test_tiled_layout_matches_documented_order(moe, fp8, E, N, K):
+    rng = np.random.default_rng(30)
+    if fp8:
+        bits = rng.integers(0, 256, size=(E, N, K)).astype(np.uint8)
+        w = torch.from_numpy(bits).cuda()
+        s = torch.ones(E, N // 128, K // 128, device="cuda")
+    else:
+        bits = rng.integers(0, 2 ** 16, size=(E, N, K)).astype(np.uint16)
+        w = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        s = None
+    tw = moe.moe_tile_weights((w, s))
+    torch.cuda.synchronize()
+    assert np.array_equal(tw.w.cpu().numpy(), _tiled_reference(bits, fp8))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "verify"])
+def test_tiled_layer_bit_identical(moe, name):
+    """The tiled layout changes where weights sit, not what is computed."""
+    model = model_for(name)
+    (x, ids, w), (xt, it, wt) = device_inputs(model.cfg)
+    layer = model.layer()
+    tiled = layer.tiled()
+    a = layer.forward(xt, it, wt)
+    b = tiled.forward(xt, it, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", ODD, ids=lambda c: c.name)
+def test_tiled_odd_shapes_bit_identical(moe, cfg):
+    model = DeviceModel(cfg, threads=4)
+    _, (xt, it, wt) = device_inputs(cfg)
+    layer = model.layer()
+    a = layer.forward(xt, it, wt)
+    b = layer.tiled().forward(xt, it, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ------------------------------------------ fused layer vs the four steps --
+
+def _separate_steps(moe, layer, xt, it, wt):
+    """align, gate+up, down and blend called one by one through their entry points."""
+    M = xt.shape[0]
+    t = moe.moe_align(it, layer.E, layer.BS)
+    mt = t.sorted_token_ids.numel()
+    act = torch.empty(mt, layer.I, device="cuda")
+    eo = torch.empty(mt, layer.H, device="cuda")
+    sh_act = sh_out = None
+    if layer.S:
+        sh_act = torch.empty(M, layer.S, device="cuda")
+        sh_out = torch.empty(M, layer.H, device="cuda")
+    moe.moe_grouped_gate_up_silu(xt, layer.gate, layer.up, t, act, layer.top_k, layer.BS, layer.sh_gate, layer.sh_up,
+                                 sh_act)
+    moe.moe_grouped_down(act, layer.down, t, eo, M, layer.top_k, layer.BS, layer.sh_down, sh_act, sh_out)
+    out = torch.empty(M, layer.H, dtype=torch.bfloat16, device="cuda")
+    moe.moe_blend(out, eo, wt, t.token_to_perm, sh_out)
+    torch.cuda.synchronize()
+    return out, t
+
+
+@pytest.mark.parametrize("name,ids_dtype", [("tiny", torch.int64), ("decode", torch.int64), ("decode", torch.int32),
+                                            ("verify", torch.int64)])
+def test_fused_layer_equals_separate_steps(moe, name, ids_dtype):
+    """moe_layer_forward aligns inside the gate+up kernel for small slot counts;
+    its output and tables equal the four separate calls' bit for bit."""
+    model = model_for(name)
+    _, (xt, it, wt) = device_inputs(model.cfg)
+    it = it.to(ids_dtype)
+    for layer in (model.layer(), model.layer().tiled()):
+        ws = layer.alloc_workspace(xt.shape[0], moe.MOE_IDX_I64 if ids_dtype == torch.int64 else moe.MOE_IDX_I32)
+        fused = layer.forward(xt, it, wt, workspace=ws)
+        torch.cuda.synchronize()
+        views = layer.workspace_views(ws, xt.shape[0], moe.MOE_IDX_I64 if ids_dtype == torch.int64 else moe.MOE_IDX_I32)
+        sep, t = _separate_steps(moe, layer, xt, it, wt)
+        assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
+        for k in moe.TABLE_FIELDS:
+            assert torch.equal(views[k], getattr(t, k)), k
+
+
+@pytest.mark.parametrize("cfg", ODD, ids=lambda c: c.name)
+def test_fused_odd_shapes_equal_separate_steps(moe, cfg):
+    model = DeviceModel(cfg, threads=4)
+    _, (xt, it, wt) = device_inputs(cfg)
+    layer = model.layer()
+    fused = layer.forward(xt, it, wt)
+    sep, _ = _separate_steps(moe, layer, xt, it, wt)
+    assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
+
+
+def test_fused_layer_with_dropped_and_repeated_ids(moe):
+    """Out-of-range ids and an expert repeated within a token, through the fused path."""
+    cfg = workloads.MoeConfig("messy", 12, 128, 6, 3, 64, 0, 4, "bf16", "softmax", seed=13)
+    model = DeviceModel(cfg, threads=4)
+    (x, _, w), (xt, _, wt) = device_inputs(cfg)
+    rng = np.random.default_rng(14)
+    ids = rng.integers(-2, cfg.E + 2, size=(cfg.M, cfg.top_k)).astype(np.int64)
+    ids[3] = [1, 1, 1]
+    it = torch.from_numpy(ids).cuda()
+    out, views = _run_layer(moe, model, xt, it, wt)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    assert ok, (err, bound)
+    sep, _ = _separate_steps(moe, model.layer(), xt, it, wt)
+    assert torch.equal(out.view(torch.int16), sep.view(torch.int16))
