@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--copies", type=int, default=4, help="weight copies / routings cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown-reps", type=int, default=50)
+    ap.add_argument("--breakdown-reps", type=int, default=25)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (counter calibration) and exit")
     return ap.parse_args()
@@ -89,9 +89,13 @@ def time_graphs(multi, singles, steps, warmup):
     return time.perf_counter() - t0
 
 
+KERNEL_SOURCES = ("grouped_impl.h", "grouped_gu_fp8.hip", "align_device.h", "moe_internal.h")
+
+
 def source_digest():
+    """Digest of the sources the dominant kernel (fused align + FP8 gate+up) is built from."""
     h = hashlib.sha256()
-    for f in ("grouped.hip",):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mixture_experts_routing_align_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -204,41 +208,41 @@ def main():
     weight_bytes = sum(bytes_per[i % G]["total"] for i in range(args.steps))
     weight_gbps = weight_bytes / elapsed / 1e9
 
-    # per-kernel durations: the four steps launched one by one, HIP events between them
+    # per-kernel durations: each step of the layer (the same kernels
+    # moe_layer_forward launches) captured R*G times back to back in one graph;
+    # HIP events on the replay stream bracket each replay
     log("per-kernel breakdown")
-    names = ("align", "gate_up", "down", "blend")
-    acc = {k: 0.0 for k in names}
-    gu_bytes = 0.0
-    down_bytes = 0.0
-    count = 0
-    with torch.cuda.stream(stream):
-        for rep in range(args.breakdown_reps):
-            for i in range(G):
-                L = layers[i]
-                v = L.workspace_views(wss[i], cfg.M)
-                tables = moe.AlignTables(**{k: v[k] for k in moe.TABLE_FIELDS})
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-                ev[0].record(stream)
-                moe.moe_align(ids_d[i], cfg.E, cfg.BS, tables, stream=stream)
-                ev[1].record(stream)
-                moe.moe_grouped_gate_up_silu(xt, L.gate, L.up, tables, v["act"], cfg.top_k, cfg.BS, stream=stream)
-                ev[2].record(stream)
-                moe.moe_grouped_down(v["act"], L.down, tables, v["expert_out"], cfg.M, cfg.top_k, cfg.BS,
-                                     stream=stream)
-                ev[3].record(stream)
-                moe.moe_blend(outs[i], v["expert_out"], w_d[i], tables.token_to_perm, stream=stream)
-                ev[4].record(stream)
-                ev[4].synchronize()
-                if rep == 0:
-                    continue  # first pass warms up
-                for j, k in enumerate(names):
-                    acc[k] += ev[j].elapsed_time(ev[j + 1]) * 1e3
-                gu_bytes += bytes_per[i]["gate_up"]
-                down_bytes += bytes_per[i]["down"]
-                count += 1
-    kernels_us = {k: acc[k] / count for k in names}
-    gu_gbps = gu_bytes / count / (kernels_us["gate_up"] * 1e-6) / 1e9
-    down_gbps = down_bytes / count / (kernels_us["down"] * 1e-6) / 1e9
+    views = [layers[i].workspace_views(wss[i], cfg.M) for i in range(G)]
+    tables = [moe.AlignTables(**{k: views[i][k] for k in moe.TABLE_FIELDS}) for i in range(G)]
+    R = max(1, args.breakdown_reps)
+
+    def k_align_gate_up(i):
+        moe.moe_align_gate_up_silu(ids_d[i], xt, layers[i].gate, layers[i].up, cfg.E, cfg.BS, views[i]["act"],
+                                   tables[i], stream=stream)
+
+    def k_down(i):
+        moe.moe_grouped_down(views[i]["act"], layers[i].down, tables[i], views[i]["expert_out"], cfg.M, cfg.top_k,
+                             cfg.BS, stream=stream)
+
+    def k_blend(i):
+        moe.moe_blend(outs[i], views[i]["expert_out"], w_d[i], tables[i].token_to_perm, stream=stream)
+
+    kernels_us = {}
+    for name, fn in (("align_gate_up", k_align_gate_up), ("down", k_down), ("blend", k_blend)):
+        g = graph_of(lambda fn=fn: [fn(i) for _ in range(R) for i in range(G)], stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            ev0.record(stream)
+            for _ in range(3):
+                g.replay()
+            ev1.record(stream)
+        ev1.synchronize()
+        kernels_us[name] = ev0.elapsed_time(ev1) * 1e3 / (3 * R * G)
+    gu_bytes = float(np.mean([b["gate_up"] for b in bytes_per]))
+    down_bytes = float(np.mean([b["down"] for b in bytes_per]))
+    gu_gbps = gu_bytes / (kernels_us["align_gate_up"] * 1e-6) / 1e9
+    down_gbps = down_bytes / (kernels_us["down"] * 1e-6) / 1e9
 
     # align latency on the prefill-scale align workload, graph-replayed
     log("align latency (n=32768, E=256, BS=64)")
@@ -273,7 +277,7 @@ def main():
     del big
 
     digest = source_digest()
-    gu_bytes_per_launch = gu_bytes / count
+    gu_bytes_per_launch = gu_bytes
     traffic = traffic_from_profile(digest)
     result = {
         "metric": METRIC,
@@ -300,9 +304,9 @@ def main():
         "active_experts_mean": float(np.mean([b["active"] for b in bytes_per])),
         "weight_bytes_per_step_mean": float(np.mean([b["total"] for b in bytes_per])),
         "kernels_us": kernels_us,
-        "kernel_gbps": {"gate_up": gu_gbps, "down": down_gbps},
+        "kernel_gbps": {"align_gate_up": gu_gbps, "down": down_gbps},
         "roofline": {
-            "kernel": "grouped_kernel<fp8, gate_up> (moe_grouped_gate_up_silu)",
+            "kernel": "grouped_kernel<fp8 gate+up, fused align> (moe_align_gate_up_silu)",
             "bound": "hbm",
             "achieved": gu_gbps,
             "peak": HBM_PEAK_GBPS,

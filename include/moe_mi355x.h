@@ -175,6 +175,22 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
                              int64_t M, int32_t H, int32_t I, int32_t S, int32_t E,
                              int32_t top_k, int32_t BS, hipStream_t stream);
 
+/* Slot counts up to this use the one-launch alignment + gate+up below. */
+#define MOE_FUSED_ALIGN_MAX_SLOTS 2048
+
+/* moe_align followed by moe_grouped_gate_up_silu in ONE launch, for
+ * n = M*top_k <= MOE_FUSED_ALIGN_MAX_SLOTS: every gate+up workgroup aligns
+ * topk_ids itself in LDS (the same deterministic counts, scan and stable rank)
+ * to find its expert and rows, and one workgroup writes all of `t`.  The
+ * tables and act equal the two separate calls' bit for bit; the saving is the
+ * align launch and the dependent table reads in front of the weight stream.
+ * Errors: as for the two calls, plus MOE_ERR_LIMIT for n above the limit. */
+int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void* x_bf16, moe_weight_dtype wdt,
+                           const moe_weight* gate, const moe_weight* up, const moe_align_tables* t, float* act,
+                           const moe_weight* sh_gate, const moe_weight* sh_up, float* sh_act, int64_t M,
+                           int32_t H, int32_t I, int32_t S, int32_t E, int32_t top_k, int32_t BS,
+                           hipStream_t stream);
+
 /* expert_out[p, :] = W_down[e] act[p, :] for every slot position p of active
  * expert e (float32 [max_total, H]; padding rows not written); with a shared
  * expert (sh_down non-NULL, S > 0) also sh_out[t, :] = W_sh_down sh_act[t, :]

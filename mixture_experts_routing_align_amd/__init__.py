@@ -10,7 +10,7 @@ Entry points (same names as the C ABI): ``moe_align``,
 ``moe_grouped_gate_up_silu``, ``moe_grouped_down``, ``moe_blend``,
 ``moe_layer_forward`` (via :class:`MoeLayer`), ``moe_layer_workspace_bytes``,
 ``moe_align_max_total``, ``moe_active_cap``, ``moe_tile_weights``,
-``moe_tiled_weight_bytes``.
+``moe_tiled_weight_bytes``, ``moe_align_gate_up_silu``.
 
 Weights are passed as ``(w, scale)`` pairs: ``w`` is ``[E, N, K]``
 ``torch.uint8`` e4m3fn codes with ``scale`` float32 ``[E, N/128, K/128]``, or
@@ -35,6 +35,7 @@ from ._ffi import (  # noqa: F401
     MOE_ERR_WORKSPACE,
     MOE_IDX_I32,
     MOE_IDX_I64,
+    MOE_FUSED_ALIGN_MAX_SLOTS,
     MOE_MAX_EXPERTS,
     MOE_OK,
     MOE_W_BF16,
@@ -218,6 +219,29 @@ def moe_grouped_gate_up_silu(x: torch.Tensor, gate: Weight, up: Weight, tables: 
         x.data_ptr(), wdt, ctypes.byref(_weight(gate)), ctypes.byref(_weight(up)), ctypes.byref(c),
         act.data_ptr(), _ref(_weight(sh_gate)), _ref(_weight(sh_up)), _ptr(sh_act),
         M, H, I, S, E, top_k, BS, _stream(stream)))
+
+
+def moe_align_gate_up_silu(topk_ids: torch.Tensor, x: torch.Tensor, gate, up, E: int, BS: int, act: torch.Tensor,
+                           tables: Optional[AlignTables] = None, sh_gate=None, sh_up=None,
+                           sh_act: Optional[torch.Tensor] = None, stream=None) -> AlignTables:
+    """moe_align + moe_grouped_gate_up_silu in one launch (n <= MOE_FUSED_ALIGN_MAX_SLOTS)."""
+    _need(topk_ids.dim() == 2 and topk_ids.is_contiguous(), "topk_ids must be a contiguous [M, top_k] tensor")
+    _need(topk_ids.dtype in (torch.int32, torch.int64), "topk_ids must be int32 or int64")
+    M, top_k = topk_ids.shape
+    H = x.shape[1]
+    E2, I, H2 = weight_shape(gate)
+    _need(E2 == E and H2 == H and x.dtype == torch.bfloat16, "x must be bf16 [M, H] matching the weights")
+    _need(act.dtype == torch.float32 and act.shape[1] == I, "act must be float32 [max_total, I]")
+    if tables is None:
+        tables = AlignTables.allocate(M, top_k, E, BS, topk_ids.device)
+    S = 0 if sh_gate is None else weight_shape(sh_gate)[1]
+    idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
+    c = tables.as_c()
+    _check(lib().moe_align_gate_up_silu(
+        topk_ids.data_ptr(), idt, x.data_ptr(), weight_dtype(gate), ctypes.byref(_weight(gate)),
+        ctypes.byref(_weight(up)), ctypes.byref(c), act.data_ptr(), _ref(_weight(sh_gate)), _ref(_weight(sh_up)),
+        _ptr(sh_act), M, H, I, S, E, top_k, BS, _stream(stream)))
+    return tables
 
 
 def moe_grouped_down(act: torch.Tensor, down: Weight, tables: AlignTables, expert_out: torch.Tensor, M: int,

@@ -22,6 +22,7 @@ MOE_W_FP8_E4M3 = 1
 MOE_W_BF16_TILED = 2
 MOE_W_FP8_E4M3_TILED = 3
 MOE_MAX_EXPERTS = 1024
+MOE_FUSED_ALIGN_MAX_SLOTS = 2048
 
 c_void_p = ctypes.c_void_p
 c_int = ctypes.c_int
@@ -62,6 +63,9 @@ SIGNATURES = {
     "moe_grouped_gate_up_silu": (c_int, [c_void_p, c_int, P(MoeWeight), P(MoeWeight), P(MoeAlignTables),
                                          c_void_p, P(MoeWeight), P(MoeWeight), c_void_p, c_int64, c_int32,
                                          c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p]),
+    "moe_align_gate_up_silu": (c_int, [c_void_p, c_int, c_void_p, c_int, P(MoeWeight), P(MoeWeight),
+                                       P(MoeAlignTables), c_void_p, P(MoeWeight), P(MoeWeight), c_void_p, c_int64,
+                                       c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p]),
     "moe_grouped_down": (c_int, [c_void_p, c_int, P(MoeWeight), P(MoeAlignTables), c_void_p, P(MoeWeight),
                                  c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_void_p]),

@@ -189,7 +189,7 @@ int layout(const moe_layer_desc* d, size_t off[13]) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -243,6 +243,46 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
     if (sh_act == nullptr) return fail(MOE_ERR_NULL, "%s: sh_act is NULL with S > 0", fn);
   }
   const moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
+  return hip_status(
+      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
+}
+
+int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void* x_bf16, moe_weight_dtype wdt,
+                           const moe_weight* gate, const moe_weight* up, const moe_align_tables* t, float* act,
+                           const moe_weight* sh_gate, const moe_weight* sh_up, float* sh_act, int64_t M,
+                           int32_t H, int32_t I, int32_t S, int32_t E, int32_t top_k, int32_t BS,
+                           hipStream_t stream) {
+  const char* fn = "moe_align_gate_up_silu";
+  AlignShape s;
+  int rc = check_routing_shape(fn, M, top_k, E, BS, &s);
+  if (rc) return rc;
+  if (idt != MOE_IDX_I32 && idt != MOE_IDX_I64)
+    return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)idt);
+  if (s.n > moe::kFusedAlignMaxSlots)
+    return fail(MOE_ERR_LIMIT, "%s: %lld slots exceed the fused limit %d", fn, (long long)s.n,
+                moe::kFusedAlignMaxSlots);
+  if ((rc = check_wdt(fn, wdt))) return rc;
+  if (S < 0) return fail(MOE_ERR_SHAPE, "%s: S=%d is negative", fn, S);
+  if ((rc = check_projection(fn, "gate/up", wdt, I, H))) return rc;
+  if (S > 0 && (rc = check_projection(fn, "shared gate/up", wdt, S, H))) return rc;
+  if (M == 0) return MOE_OK;
+  if (topk_ids == nullptr || x_bf16 == nullptr || act == nullptr)
+    return fail(MOE_ERR_NULL, "%s: topk_ids, x or act is NULL", fn);
+  if ((rc = check_weight(fn, "gate", gate, wdt)) || (rc = check_weight(fn, "up", up, wdt))) return rc;
+  if ((rc = check_tables(fn, t, true))) return rc;
+  if (S > 0) {
+    if ((rc = check_weight(fn, "shared gate", sh_gate, wdt)) || (rc = check_weight(fn, "shared up", sh_up, wdt)))
+      return rc;
+    if (sh_act == nullptr) return fail(MOE_ERR_NULL, "%s: sh_act is NULL with S > 0", fn);
+  }
+  moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
+  a.ids = topk_ids;
+  a.ids64 = idt == MOE_IDX_I64;
+  a.n = (int)s.n;
+  a.E = E;
+  a.BS = BS;
+  a.max_total = (int)s.max_total;
+  a.tables = to_align_out(*t);
   return hip_status(
       moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
 }
@@ -379,20 +419,10 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   if (n <= moe::kFusedAlignMaxSlots) {
     // few slots: every gate+up workgroup aligns topk_ids itself (in LDS) and
     // one writes the tables, which saves the align launch and its latency
-    moe::GroupedArgs a = gate_up_args(x_bf16, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,
-                                      shared ? &d->sh_up : nullptr, sh_act, d->M, d->H, d->I, d->S, d->top_k,
-                                      moe_active_cap(n, d->E));
-    a.ids = topk_ids;
-    a.ids64 = d->idt == MOE_IDX_I64;
-    a.n = (int)n;
-    a.E = d->E;
-    a.BS = d->BS;
-    a.max_total = (int)moe_align_max_total(n, d->E, d->BS);
-    a.tables = to_align_out(t);
-    rc = hip_status(moe::launch_grouped_gate_up(a, is_fp8(d->wdt), is_tiled(d->wdt),
-                                                moe::grouped_row_tiles(d->M, d->top_k), stream),
-                    fn);
-    if (rc) return rc;
+    if ((rc = moe_align_gate_up_silu(topk_ids, d->idt, x_bf16, d->wdt, &d->gate, &d->up, &t, act,
+                                     shared ? &d->sh_gate : nullptr, shared ? &d->sh_up : nullptr, sh_act, d->M,
+                                     d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))
+      return rc;
   } else {
     if ((rc = moe_align(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, stream))) return rc;
     if ((rc = moe_grouped_gate_up_silu(x_bf16, d->wdt, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include "moe_mi355x.h"
+
 namespace moe {
 
 constexpr int kFp8Block = 128;   // FP8 scale block edge (both N and K)
@@ -59,7 +61,7 @@ struct GroupedArgs {
 
 // Largest slot count the fused align + gate+up kernel takes (its per-workgroup
 // alignment cost grows with n; above this the layer runs the align kernel).
-constexpr int kFusedAlignMaxSlots = 2048;
+constexpr int kFusedAlignMaxSlots = MOE_FUSED_ALIGN_MAX_SLOTS;
 
 // Row tiles (16 rows each) one workgroup keeps in registers per pass over the
 // weights; chosen from the shape class (the most rows an expert can hold), never

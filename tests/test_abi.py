@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -166,3 +166,24 @@ def test_layer_refusals(lib):
     assert rc == _ffi.MOE_ERR_NULL
     d0 = _desc(M=0)
     assert lib.moe_layer_forward(ctypes.byref(d0), None, None, None, None, None, 0, None) == _ffi.MOE_OK
+
+
+def test_fused_align_gate_up_refusals(lib):
+    t = _tables()
+    g, u = _w(), _w()
+
+    def call(M, top_k=8, idt=1, **kw):
+        a = dict(H=256, I=128, S=0, E=8, BS=16)
+        a.update(kw)
+        return lib.moe_align_gate_up_silu(FAKE, idt, FAKE, 1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(t), FAKE,
+                                          None, None, None, M, a["H"], a["I"], a["S"], a["E"], top_k, a["BS"], None)
+
+    assert call(257) == _ffi.MOE_ERR_LIMIT               # 2056 slots > 2048
+    assert call(4, idt=9) == _ffi.MOE_ERR_SHAPE
+    assert call(4, H=100) == _ffi.MOE_ERR_SHAPE
+    assert call(4, E=4096) == _ffi.MOE_ERR_LIMIT
+    assert call(0) == _ffi.MOE_OK
+    bad = _tables()
+    bad.total = None
+    assert lib.moe_align_gate_up_silu(FAKE, 1, FAKE, 1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad), FAKE,
+                                      None, None, None, 4, 256, 128, 0, 8, 8, 16, None) == _ffi.MOE_ERR_NULL
