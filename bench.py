@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer rows/s + weight-stream HBM GB/s (% of peak) at M=8; align latency us"
 HBM_PEAK_GBPS = 8000.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "grouped_gate_up_decode_pmc.txt")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "layer_partials_decode_pmc.txt")
 
 
 def log(msg):
@@ -89,11 +89,11 @@ def time_graphs(multi, singles, steps, warmup):
     return time.perf_counter() - t0
 
 
-KERNEL_SOURCES = ("grouped_impl.h", "grouped_gu_fp8.hip", "align_device.h", "moe_internal.h")
+KERNEL_SOURCES = ("layer_fused.hip", "mma_common.h", "align_device.h", "moe_internal.h")
 
 
 def source_digest():
-    """Digest of the sources the dominant kernel (fused align + FP8 gate+up) is built from."""
+    """Digest of the sources the dominant kernel (the single-pass layer kernel) is built from."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "mixture_experts_routing_align_amd", "csrc", f), "rb") as fh:
@@ -208,27 +208,22 @@ def main():
     weight_bytes = sum(bytes_per[i % G]["total"] for i in range(args.steps))
     weight_gbps = weight_bytes / elapsed / 1e9
 
-    # per-kernel durations: each step of the layer (the same kernels
-    # moe_layer_forward launches) captured R*G times back to back in one graph;
-    # HIP events on the replay stream bracket each replay
+    # per-kernel durations: each launch of the layer (moe_layer_forward on this
+    # shape is moe_layer_partials then moe_layer_blend_partials) captured R*G
+    # times back to back in one graph; HIP events on the replay stream bracket
+    # each replay
     log("per-kernel breakdown")
-    views = [layers[i].workspace_views(wss[i], cfg.M) for i in range(G)]
-    tables = [moe.AlignTables(**{k: views[i][k] for k in moe.TABLE_FIELDS}) for i in range(G)]
+    assert all(l.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS for l in layers)
     R = max(1, args.breakdown_reps)
 
-    def k_align_gate_up(i):
-        moe.moe_align_gate_up_silu(ids_d[i], xt, layers[i].gate, layers[i].up, cfg.E, cfg.BS, views[i]["act"],
-                                   tables[i], stream=stream)
-
-    def k_down(i):
-        moe.moe_grouped_down(views[i]["act"], layers[i].down, tables[i], views[i]["expert_out"], cfg.M, cfg.top_k,
-                             cfg.BS, stream=stream)
+    def k_partials(i):
+        moe.moe_layer_partials(layers[i], xt, ids_d[i], wss[i], stream=stream)
 
     def k_blend(i):
-        moe.moe_blend(outs[i], views[i]["expert_out"], w_d[i], tables[i].token_to_perm, stream=stream)
+        moe.moe_layer_blend_partials(layers[i], ids_d[i], w_d[i], outs[i], wss[i], stream=stream)
 
     kernels_us = {}
-    for name, fn in (("align_gate_up", k_align_gate_up), ("down", k_down), ("blend", k_blend)):
+    for name, fn in (("layer_partials", k_partials), ("blend_partials", k_blend)):
         g = graph_of(lambda fn=fn: [fn(i) for _ in range(R) for i in range(G)], stream)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
@@ -239,10 +234,8 @@ def main():
             ev1.record(stream)
         ev1.synchronize()
         kernels_us[name] = ev0.elapsed_time(ev1) * 1e3 / (3 * R * G)
-    gu_bytes = float(np.mean([b["gate_up"] for b in bytes_per]))
-    down_bytes = float(np.mean([b["down"] for b in bytes_per]))
-    gu_gbps = gu_bytes / (kernels_us["align_gate_up"] * 1e-6) / 1e9
-    down_gbps = down_bytes / (kernels_us["down"] * 1e-6) / 1e9
+    layer_bytes = float(np.mean([b["total"] for b in bytes_per]))
+    part_gbps = layer_bytes / (kernels_us["layer_partials"] * 1e-6) / 1e9
 
     # align latency on the prefill-scale align workload, graph-replayed
     log("align latency (n=32768, E=256, BS=64)")
@@ -277,7 +270,6 @@ def main():
     del big
 
     digest = source_digest()
-    gu_bytes_per_launch = gu_bytes
     traffic = traffic_from_profile(digest)
     result = {
         "metric": METRIC,
@@ -304,16 +296,16 @@ def main():
         "active_experts_mean": float(np.mean([b["active"] for b in bytes_per])),
         "weight_bytes_per_step_mean": float(np.mean([b["total"] for b in bytes_per])),
         "kernels_us": kernels_us,
-        "kernel_gbps": {"align_gate_up": gu_gbps, "down": down_gbps},
+        "kernel_gbps": {"layer_partials": part_gbps},
         "roofline": {
-            "kernel": "grouped_kernel<fp8 gate+up, fused align> (moe_align_gate_up_silu)",
+            "kernel": "layer_kernel<fp8> (moe_layer_partials: align + gate+up+SiLU + down slices)",
             "bound": "hbm",
-            "achieved": gu_gbps,
+            "achieved": part_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": gu_gbps / HBM_PEAK_GBPS,
+            "frac": part_gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": gu_bytes_per_launch,
+            "algorithmic_bytes_per_launch": layer_bytes,
             "source_digest": digest,
         },
         "align_us": align_s / areps * 1e6,

@@ -194,8 +194,10 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
 /* expert_out[p, :] = W_down[e] act[p, :] for every slot position p of active
  * expert e (float32 [max_total, H]; padding rows not written); with a shared
  * expert (sh_down non-NULL, S > 0) also sh_out[t, :] = W_sh_down sh_act[t, :]
- * (float32 [M, H]).  Shapes: FP8 needs H, I, S multiples of 128; BF16 needs
- * I, S multiples of 32 and H a multiple of 16. */
+ * (float32 [M, H]).  The depth is summed in 64-deep halves of 128-deep chunks,
+ * ascending, from 0: each half's float32 product (times its block scale, FP8)
+ * is rounded and then added, with no fused multiply-add across halves.  Shapes: FP8 needs H,
+ * I, S multiples of 128; BF16 needs I, S multiples of 32 and H a multiple of 16. */
 int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down,
                      const moe_align_tables* t, float* expert_out, const moe_weight* sh_down,
                      const float* sh_act, float* sh_out, int64_t M, int32_t H, int32_t I,
@@ -227,28 +229,70 @@ typedef struct {
   moe_weight sh_gate, sh_up, sh_down;   /* shared expert (.w NULL if none) */
 } moe_layer_desc;
 
-/* Bytes of workspace moe_layer_forward needs for `d` (tables, act,
- * expert_out, and the shared expert's sh_act and sh_out), each region
- * 256-byte aligned.  Depends on the shapes only, never on the routing.
- * Returns 0 for an invalid descriptor (moe_last_error says why). */
+/* The two ways moe_layer_forward runs, chosen from the descriptor's shapes
+ * (never from the routing, so a captured graph stays valid for any routing):
+ *  - MOE_LAYER_PATH_STEPS: align (or align fused into gate+up for at most
+ *    MOE_FUSED_ALIGN_MAX_SLOTS slots), gate+up+SiLU, down and blend, the same
+ *    kernels the four entry points above launch;
+ *  - MOE_LAYER_PATH_SINGLE_PASS: tiled weights and at most
+ *    MOE_FUSED_LAYER_MAX_SLOTS slots (decode width).  One launch aligns and, per
+ *    active expert and 64-wide slice j of the intermediate, runs gate+up+SiLU
+ *    into LDS and then the 64-deep slice j of down, writing float32 partial
+ *    outputs part[j][slot][:]; a second launch forms each slot's expert output
+ *    as the sum of its slices (j ascending, from 0) and blends.  The separate
+ *    down projection sums the 64-deep halves of its chunks in the same order,
+ *    so both paths give the same bits.  (The decomposition of the layer into gate+up then down
+ *    per expert is metrale forward_nvfp4_grouped_decode.rs's; the per-slice
+ *    split is this library's.) */
+typedef enum { MOE_LAYER_PATH_STEPS = 0, MOE_LAYER_PATH_SINGLE_PASS = 1 } moe_layer_path_kind;
+#define MOE_FUSED_LAYER_MAX_SLOTS 256
+
+/* Workspace regions of moe_layer_forward, in this order: sorted_token_ids,
+ * block_expert_ids, expert_offsets, expert_counts, token_to_perm,
+ * active_experts, active_count, total (the tables, int32), then float32:
+ * act [max_total, I], expert_out [max_total, H], sh_act [M, S], sh_out [M, H]
+ * (the steps path), part [ceil(I/64), M*top_k, H] and sh_part [ceil(S/64), M, H]
+ * (the single-pass path).  A region the chosen path (or a layer without a shared
+ * expert) does not use has size 0. */
+#define MOE_LAYER_WORKSPACE_REGIONS 14
+
+/* Bytes of workspace moe_layer_forward needs for `d`, each region 256-byte
+ * aligned.  Depends on the shapes only, never on the routing.  Returns 0 for
+ * an invalid descriptor (moe_last_error says why). */
 size_t moe_layer_workspace_bytes(const moe_layer_desc* d);
+
+/* The moe_layer_path_kind moe_layer_forward takes for `d`, or a negative
+ * moe_status for an invalid descriptor. */
+int moe_layer_path(const moe_layer_desc* d);
 
 /* The whole layer on `stream`: align, gate+up+SiLU, down, blend, with no host
  * synchronisation.  x is bf16 [M, H], topk_ids [M, top_k] (d->idt),
  * topk_weights float32 [M, top_k], out bf16 [M, H].  The workspace (device,
- * >= moe_layer_workspace_bytes(d), 256-byte aligned) holds the tables and
- * intermediates afterwards, laid out as moe_layer_workspace_layout says.
- * Errors: as for the four steps, plus MOE_ERR_WORKSPACE. */
+ * >= moe_layer_workspace_bytes(d), 256-byte aligned) holds the tables and the
+ * chosen path's intermediates afterwards, laid out as
+ * moe_layer_workspace_layout says.  Errors: as for the four steps, plus
+ * MOE_ERR_WORKSPACE. */
 int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids,
                       const float* topk_weights, void* out_bf16, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
-/* Byte offsets of the workspace regions moe_layer_forward uses, in this order:
- * sorted_token_ids, block_expert_ids, expert_offsets, expert_counts,
- * token_to_perm, active_experts, active_count, total, act, expert_out,
- * sh_act, sh_out (the last two are 0 without a shared expert); offsets[12] is
- * the total size.  Returns MOE_OK or an error for an invalid descriptor. */
-int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[13]);
+/* The two launches of the single-pass path, callable one at a time (for
+ * example to time each); moe_layer_forward on that path is exactly
+ * moe_layer_partials followed by moe_layer_blend_partials on the same
+ * workspace.  moe_layer_partials aligns topk_ids (writing the tables into the
+ * workspace) and writes the float32 partial outputs part / sh_part;
+ * moe_layer_blend_partials reads them with topk_ids and topk_weights and
+ * writes out (bf16 [M, H]).  Both return MOE_ERR_SHAPE when `d` does not take
+ * MOE_LAYER_PATH_SINGLE_PASS; other errors as for moe_layer_forward. */
+int moe_layer_partials(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+int moe_layer_blend_partials(const moe_layer_desc* d, const void* topk_ids, const float* topk_weights,
+                             void* out_bf16, const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Byte offsets of the MOE_LAYER_WORKSPACE_REGIONS regions, in the order above;
+ * offsets[MOE_LAYER_WORKSPACE_REGIONS] is the total size.  Returns MOE_OK or an
+ * error for an invalid descriptor. */
+int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[MOE_LAYER_WORKSPACE_REGIONS + 1]);
 
 #ifdef __cplusplus
 }

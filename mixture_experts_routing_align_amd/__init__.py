@@ -36,6 +36,10 @@ from ._ffi import (  # noqa: F401
     MOE_IDX_I32,
     MOE_IDX_I64,
     MOE_FUSED_ALIGN_MAX_SLOTS,
+    MOE_FUSED_LAYER_MAX_SLOTS,
+    MOE_LAYER_PATH_SINGLE_PASS,
+    MOE_LAYER_PATH_STEPS,
+    MOE_LAYER_WORKSPACE_REGIONS,
     MOE_MAX_EXPERTS,
     MOE_OK,
     MOE_W_BF16,
@@ -274,7 +278,7 @@ def moe_blend(out: torch.Tensor, expert_out: torch.Tensor, topk_weights: torch.T
 
 # ------------------------------------------------------------- whole layer --
 
-WORKSPACE_REGIONS = TABLE_FIELDS + ("act", "expert_out", "sh_act", "sh_out")
+WORKSPACE_REGIONS = TABLE_FIELDS + ("act", "expert_out", "sh_act", "sh_out", "part", "sh_part")
 
 
 class MoeLayer:
@@ -315,27 +319,39 @@ class MoeLayer:
 
     def workspace_layout(self, M: int, idt: int = MOE_IDX_I64):
         d = self.desc(M, idt)
-        off = (ctypes.c_size_t * 13)()
+        off = (ctypes.c_size_t * (MOE_LAYER_WORKSPACE_REGIONS + 1))()
         _check(lib().moe_layer_workspace_layout(ctypes.byref(d), off))
         return list(off)
+
+    def path(self, M: int, idt: int = MOE_IDX_I64) -> int:
+        """MOE_LAYER_PATH_STEPS or MOE_LAYER_PATH_SINGLE_PASS for M tokens."""
+        d = self.desc(M, idt)
+        rc = lib().moe_layer_path(ctypes.byref(d))
+        if rc < 0:
+            raise MoeError(rc, lib().moe_last_error().decode())
+        return rc
 
     def alloc_workspace(self, M: int, idt: int = MOE_IDX_I64, device="cuda") -> torch.Tensor:
         return torch.empty(self.workspace_bytes(M, idt), dtype=torch.uint8, device=device)
 
     def workspace_views(self, ws: torch.Tensor, M: int, idt: int = MOE_IDX_I64) -> dict:
-        """Typed views of the tables and intermediates inside a used workspace."""
+        """Typed views of the tables and of the chosen path's intermediates
+        inside a used workspace (regions the path does not use are left out)."""
         off = self.workspace_layout(M, idt)
         n = M * self.top_k
         mt = moe_align_max_total(n, self.E, self.BS)
+        single = self.path(M, idt) == MOE_LAYER_PATH_SINGLE_PASS
         sizes = {
             "sorted_token_ids": (mt,), "block_expert_ids": (mt // self.BS,), "expert_offsets": (self.E + 1,),
             "expert_counts": (self.E,), "token_to_perm": (n,), "active_experts": (moe_active_cap(n, self.E),),
-            "active_count": (1,), "total": (1,), "act": (mt, self.I), "expert_out": (mt, self.H),
-            "sh_act": (M, self.S), "sh_out": (M, self.H),
+            "active_count": (1,), "total": (1,),
+            "act": (mt, self.I), "expert_out": (mt, self.H), "sh_act": (M, self.S), "sh_out": (M, self.H),
+            "part": (-(-self.I // 64), n, self.H), "sh_part": (-(-self.S // 64), M, self.H),
         }
+        used = set(TABLE_FIELDS) | ({"part", "sh_part"} if single else {"act", "expert_out", "sh_act", "sh_out"})
         views = {}
         for i, name in enumerate(WORKSPACE_REGIONS):
-            if name.startswith("sh_") and self.S == 0:
+            if name not in used or (name.startswith("sh_") and self.S == 0):
                 continue
             shape = sizes[name]
             dt = torch.int32 if i < 8 else torch.float32
@@ -363,6 +379,25 @@ class MoeLayer:
         _check(lib().moe_layer_forward(ctypes.byref(d), x.data_ptr(), topk_ids.data_ptr(), topk_weights.data_ptr(),
                                        out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
         return out
+
+
+def moe_layer_partials(layer: MoeLayer, x, topk_ids, workspace, stream=None) -> None:
+    """First launch of the single-pass layer: tables and per-slice partial outputs into `workspace`."""
+    M = x.shape[0]
+    idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
+    d = layer.desc(M, idt)
+    _check(lib().moe_layer_partials(ctypes.byref(d), x.data_ptr(), topk_ids.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), _stream(stream)))
+
+
+def moe_layer_blend_partials(layer: MoeLayer, topk_ids, topk_weights, out, workspace, stream=None):
+    """Second launch of the single-pass layer: sum the partials, blend into `out`."""
+    M = topk_ids.shape[0]
+    idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
+    d = layer.desc(M, idt)
+    _check(lib().moe_layer_blend_partials(ctypes.byref(d), topk_ids.data_ptr(), topk_weights.data_ptr(),
+                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out
 
 
 def moe_layer_workspace_bytes(layer: MoeLayer, M: int, idt: int = MOE_IDX_I64) -> int:

@@ -23,6 +23,10 @@ MOE_W_BF16_TILED = 2
 MOE_W_FP8_E4M3_TILED = 3
 MOE_MAX_EXPERTS = 1024
 MOE_FUSED_ALIGN_MAX_SLOTS = 2048
+MOE_FUSED_LAYER_MAX_SLOTS = 256
+MOE_LAYER_PATH_STEPS = 0
+MOE_LAYER_PATH_SINGLE_PASS = 1
+MOE_LAYER_WORKSPACE_REGIONS = 14
 
 c_void_p = ctypes.c_void_p
 c_int = ctypes.c_int
@@ -75,6 +79,10 @@ SIGNATURES = {
     "moe_layer_forward": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                   c_void_p]),
     "moe_layer_workspace_layout": (c_int, [P(MoeLayerDesc), P(c_size_t)]),
+    "moe_layer_path": (c_int, [P(MoeLayerDesc)]),
+    "moe_layer_partials": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_layer_blend_partials": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                         c_void_p]),
     "moe_tiled_weight_bytes": (c_size_t, [c_int, c_int64, c_int32, c_int32]),
     "moe_tile_weights": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int32, c_void_p]),
 }

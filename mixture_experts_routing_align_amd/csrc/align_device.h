@@ -186,10 +186,11 @@ __device__ void scatter_pass(const IdT* __restrict__ ids, int n, int E, int nbit
   }
 }
 
-// The sources of expert e's rows, in sorted order: src[r] = slot / top_k of its
-// r-th slot.  Reads (does not advance) the per-wave bases.  No barrier.
+// The sources of expert e's rows, in sorted order: src[r] = slot / div of its
+// r-th slot (div = top_k gives the token, div = 1 the slot itself).  Reads
+// (does not advance) the per-wave bases.  No barrier.
 template <int NW, typename IdT>
-__device__ void expert_rows(const IdT* __restrict__ ids, int n, int E, int nbits, const int* cnt, int e, int top_k,
+__device__ void expert_rows(const IdT* __restrict__ ids, int n, int E, int nbits, const int* cnt, int e, int div,
                             int* src) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int beg, end;
@@ -201,7 +202,7 @@ __device__ void expert_rows(const IdT* __restrict__ ids, int n, int E, int nbits
     const int id = load_id(ids, i, end, E, valid);
     const bool mine = valid && id == e;
     const uint64_t m = __ballot(mine);
-    if (mine) src[base + __popcll(m & lanes_below(lane))] = i / top_k;
+    if (mine) src[base + __popcll(m & lanes_below(lane))] = i / div;
     base += __popcll(m);
   }
 }

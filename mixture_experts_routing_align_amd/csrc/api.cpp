@@ -143,7 +143,15 @@ moe::GroupedArgs gate_up_args(const void* x_bf16, const moe_weight* gate, const 
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-int layout(const moe_layer_desc* d, size_t off[13]) {
+// The path moe_layer_forward takes for a checked descriptor (shape only, never
+// the routing): the single-pass layer for tiled weights at decode width.
+int layer_path(const moe_layer_desc* d) {
+  const bool fits = is_tiled(d->wdt) &&
+                    moe::fused_layer_fits(is_fp8(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
+  return fits ? MOE_LAYER_PATH_SINGLE_PASS : MOE_LAYER_PATH_STEPS;
+}
+
+int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1], int* path = nullptr) {
   const char* fn = "moe_layer_workspace";
   if (d == nullptr) return fail(MOE_ERR_NULL, "%s: descriptor is NULL", fn);
   AlignShape s;
@@ -159,29 +167,31 @@ int layout(const moe_layer_desc* d, size_t off[13]) {
     if ((rc = check_projection(fn, "shared gate/up", d->wdt, d->S, d->H))) return rc;
     if ((rc = check_projection(fn, "shared down", d->wdt, d->H, d->S))) return rc;
   }
-  const size_t mt = (size_t)s.max_total, n = (size_t)s.n, M = (size_t)d->M;
+  const int lp = layer_path(d);
+  if (path) *path = lp;
+  const bool single = lp == MOE_LAYER_PATH_SINGLE_PASS;
+  const size_t mt = (size_t)s.max_total, n = (size_t)s.n, M = (size_t)d->M, H = (size_t)d->H;
+  const size_t S = (size_t)d->S, I = (size_t)d->I;
   size_t cur = 0;
   auto take = [&](int i, size_t bytes) {
     off[i] = cur;
     cur = align256(cur + bytes);
   };
-  take(0, mt * 4);                            // sorted_token_ids
-  take(1, (mt / d->BS) * 4);                  // block_expert_ids
-  take(2, ((size_t)d->E + 1) * 4);            // expert_offsets
-  take(3, (size_t)d->E * 4);                  // expert_counts
-  take(4, n * 4);                             // token_to_perm
-  take(5, (size_t)s.cap * 4);                 // active_experts
-  take(6, 4);                                 // active_count
-  take(7, 4);                                 // total
-  take(8, mt * (size_t)d->I * 4);             // act
-  take(9, mt * (size_t)d->H * 4);             // expert_out
-  if (d->S > 0) {
-    take(10, M * (size_t)d->S * 4);           // sh_act
-    take(11, M * (size_t)d->H * 4);           // sh_out
-  } else {
-    off[10] = off[11] = 0;
-  }
-  off[12] = cur;
+  take(0, mt * 4);                                        // sorted_token_ids
+  take(1, (mt / d->BS) * 4);                              // block_expert_ids
+  take(2, ((size_t)d->E + 1) * 4);                        // expert_offsets
+  take(3, (size_t)d->E * 4);                              // expert_counts
+  take(4, n * 4);                                         // token_to_perm
+  take(5, (size_t)s.cap * 4);                             // active_experts
+  take(6, 4);                                             // active_count
+  take(7, 4);                                             // total
+  take(8, single ? 0 : mt * I * 4);                       // act
+  take(9, single ? 0 : mt * H * 4);                       // expert_out
+  take(10, single ? 0 : M * S * 4);                       // sh_act
+  take(11, single ? 0 : M * H * 4);                       // sh_out
+  take(12, single ? ((I + 63) / 64) * n * H * 4 : 0);     // part: per 64-wide slice of I, per slot
+  take(13, single ? ((S + 63) / 64) * M * H * 4 : 0);     // sh_part: per 64-wide slice of S, per token
+  off[14] = cur;
   return MOE_OK;
 }
 
@@ -189,7 +199,7 @@ int layout(const moe_layer_desc* d, size_t off[13]) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -366,41 +376,52 @@ int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E
   return hip_status(moe::launch_tile_weights(src, dst, is_fp8(wdt), E, N, K, stream), fn);
 }
 
-int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[13]) {
+int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[MOE_LAYER_WORKSPACE_REGIONS + 1]) {
   if (offsets == nullptr) return fail(MOE_ERR_NULL, "moe_layer_workspace_layout: offsets is NULL");
   return layout(d, offsets);
 }
 
 size_t moe_layer_workspace_bytes(const moe_layer_desc* d) {
-  size_t off[13];
+  size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1];
   if (layout(d, off) != MOE_OK) return 0;
-  return off[12];
+  return off[MOE_LAYER_WORKSPACE_REGIONS];
 }
 
-int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids, const float* topk_weights,
-                      void* out_bf16, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "moe_layer_forward";
-  size_t off[13];
-  int rc = layout(d, off);
+int moe_layer_path(const moe_layer_desc* d) {
+  size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1];
+  int path = 0;
+  const int rc = layout(d, off, &path);
+  return rc ? rc : path;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the layer calls: the descriptor, the workspace and the
+// weights.  Fills the workspace offsets and the path.
+int layer_setup(const char* fn, const moe_layer_desc* d, const void* workspace, size_t workspace_bytes,
+                size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1], int* path) {
+  int rc = layout(d, off, path);
   if (rc) return rc;
   if (d->M == 0) return MOE_OK;
-  if (!x_bf16 || !topk_ids || !topk_weights || !out_bf16)
-    return fail(MOE_ERR_NULL, "%s: x, topk_ids, topk_weights or out is NULL", fn);
   if (workspace == nullptr) return fail(MOE_ERR_NULL, "%s: workspace is NULL", fn);
-  if (workspace_bytes < off[12])
-    return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, off[12]);
+  if (workspace_bytes < off[MOE_LAYER_WORKSPACE_REGIONS])
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes,
+                off[MOE_LAYER_WORKSPACE_REGIONS]);
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace is not 256-byte aligned", fn);
-  const bool shared = d->S > 0;
   if ((rc = check_weight(fn, "gate", &d->gate, d->wdt)) || (rc = check_weight(fn, "up", &d->up, d->wdt)) ||
       (rc = check_weight(fn, "down", &d->down, d->wdt)))
     return rc;
-  if (shared && ((rc = check_weight(fn, "shared gate", &d->sh_gate, d->wdt)) ||
-                 (rc = check_weight(fn, "shared up", &d->sh_up, d->wdt)) ||
-                 (rc = check_weight(fn, "shared down", &d->sh_down, d->wdt))))
+  if (d->S > 0 && ((rc = check_weight(fn, "shared gate", &d->sh_gate, d->wdt)) ||
+                   (rc = check_weight(fn, "shared up", &d->sh_up, d->wdt)) ||
+                   (rc = check_weight(fn, "shared down", &d->sh_down, d->wdt))))
     return rc;
+  return MOE_OK;
+}
 
-  char* ws = static_cast<char*>(workspace);
+moe_align_tables workspace_tables(char* ws, const size_t* off) {
   moe_align_tables t;
   t.sorted_token_ids = reinterpret_cast<int32_t*>(ws + off[0]);
   t.block_expert_ids = reinterpret_cast<int32_t*>(ws + off[1]);
@@ -410,12 +431,101 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   t.active_experts = reinterpret_cast<int32_t*>(ws + off[5]);
   t.active_count = reinterpret_cast<int32_t*>(ws + off[6]);
   t.total = reinterpret_cast<int32_t*>(ws + off[7]);
+  return t;
+}
+
+moe::FusedLayerArgs single_pass_args(const moe_layer_desc* d, char* ws, const size_t* off, const void* x_bf16,
+                                     const void* topk_ids, const float* topk_weights, void* out_bf16) {
+  const bool shared = d->S > 0;
+  const int64_t n = d->M * d->top_k;
+  moe::FusedLayerArgs a{};
+  a.ids = topk_ids;
+  a.ids64 = d->idt == MOE_IDX_I64;
+  a.x = x_bf16;
+  const moe_weight* w[3] = {&d->gate, &d->up, &d->down};
+  const moe_weight* sw[3] = {&d->sh_gate, &d->sh_up, &d->sh_down};
+  for (int i = 0; i < 3; ++i) {
+    a.w[i] = w[i]->w;
+    a.s[i] = w[i]->scale;
+    a.sw[i] = shared ? sw[i]->w : nullptr;
+    a.ss[i] = shared ? sw[i]->scale : nullptr;
+  }
+  a.topk_weights = topk_weights;
+  a.out = static_cast<uint16_t*>(out_bf16);
+  a.part = reinterpret_cast<float*>(ws + off[12]);
+  a.sh_part = shared ? reinterpret_cast<float*>(ws + off[13]) : nullptr;
+  a.M = (int)d->M;
+  a.H = d->H;
+  a.I = d->I;
+  a.S = d->S;
+  a.E = d->E;
+  a.top_k = d->top_k;
+  a.BS = d->BS;
+  a.n = (int)n;
+  a.cap = moe_active_cap(n, d->E);
+  a.max_total = (int)moe_align_max_total(n, d->E, d->BS);
+  a.tables = to_align_out(workspace_tables(ws, off));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_partials(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_layer_partials";
+  size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1];
+  int path = 0;
+  int rc = layer_setup(fn, d, workspace, workspace_bytes, off, &path);
+  if (rc || d->M == 0) return rc;
+  if (path != MOE_LAYER_PATH_SINGLE_PASS)
+    return fail(MOE_ERR_SHAPE, "%s: this layer shape does not take the single-pass path", fn);
+  if (!x_bf16 || !topk_ids) return fail(MOE_ERR_NULL, "%s: x or topk_ids is NULL", fn);
+  const moe::FusedLayerArgs a =
+      single_pass_args(d, static_cast<char*>(workspace), off, x_bf16, topk_ids, nullptr, nullptr);
+  return hip_status(moe::launch_layer_partials(a, is_fp8(d->wdt), stream), fn);
+}
+
+int moe_layer_blend_partials(const moe_layer_desc* d, const void* topk_ids, const float* topk_weights,
+                             void* out_bf16, const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_layer_blend_partials";
+  size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1];
+  int path = 0;
+  int rc = layer_setup(fn, d, workspace, workspace_bytes, off, &path);
+  if (rc || d->M == 0) return rc;
+  if (path != MOE_LAYER_PATH_SINGLE_PASS)
+    return fail(MOE_ERR_SHAPE, "%s: this layer shape does not take the single-pass path", fn);
+  if (!topk_ids || !topk_weights || !out_bf16)
+    return fail(MOE_ERR_NULL, "%s: topk_ids, topk_weights or out is NULL", fn);
+  const moe::FusedLayerArgs a = single_pass_args(d, static_cast<char*>(const_cast<void*>(workspace)), off, nullptr,
+                                                 topk_ids, topk_weights, out_bf16);
+  return hip_status(moe::launch_blend_partials(a, stream), fn);
+}
+
+int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids, const float* topk_weights,
+                      void* out_bf16, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_layer_forward";
+  size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1];
+  int path = 0;
+  int rc = layer_setup(fn, d, workspace, workspace_bytes, off, &path);
+  if (rc || d->M == 0) return rc;
+  if (!x_bf16 || !topk_ids || !topk_weights || !out_bf16)
+    return fail(MOE_ERR_NULL, "%s: x, topk_ids, topk_weights or out is NULL", fn);
+  char* ws = static_cast<char*>(workspace);
+  if (path == MOE_LAYER_PATH_SINGLE_PASS) {
+    const moe::FusedLayerArgs a = single_pass_args(d, ws, off, x_bf16, topk_ids, topk_weights, out_bf16);
+    if ((rc = hip_status(moe::launch_layer_partials(a, is_fp8(d->wdt), stream), fn))) return rc;
+    return hip_status(moe::launch_blend_partials(a, stream), fn);
+  }
+  const bool shared = d->S > 0;
+  const int64_t n = d->M * d->top_k;
+  moe_align_tables t = workspace_tables(ws, off);
   float* act = reinterpret_cast<float*>(ws + off[8]);
   float* expert_out = reinterpret_cast<float*>(ws + off[9]);
   float* sh_act = shared ? reinterpret_cast<float*>(ws + off[10]) : nullptr;
   float* sh_out = shared ? reinterpret_cast<float*>(ws + off[11]) : nullptr;
 
-  const int64_t n = d->M * d->top_k;
   if (n <= moe::kFusedAlignMaxSlots) {
     // few slots: every gate+up workgroup aligns topk_ids itself (in LDS) and
     // one writes the tables, which saves the align launch and its latency

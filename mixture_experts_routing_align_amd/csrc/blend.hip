@@ -16,16 +16,13 @@
 // token reads are each contiguous, so every load is coalesced.
 #include <hip/hip_runtime.h>
 
+#include "mma_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays a quiet NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+using mma::bf16_rne_out;
 
 __global__ __launch_bounds__(256) void blend_kernel(uint16_t* __restrict__ out,
                                                     const float* __restrict__ expert_out,
@@ -55,8 +52,8 @@ __global__ __launch_bounds__(256) void blend_kernel(uint16_t* __restrict__ out,
     a3 += s.w;
   }
   uint2 packed;
-  packed.x = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
-  packed.y = f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16);
+  packed.x = bf16_rne_out(a0) | (bf16_rne_out(a1) << 16);
+  packed.y = bf16_rne_out(a2) | (bf16_rne_out(a3) << 16);
   *reinterpret_cast<uint2*>(out + (size_t)t * H + h) = packed;
   }
 }

@@ -46,29 +46,27 @@ __global__ __launch_bounds__(256) void tile_weights_kernel(const uint8_t* __rest
   reinterpret_cast<uint4*>(dst)[u] = v;
 }
 
-// rows one pass stages: the most an expert holds when ids are distinct within a
-// token (M), as a power of two of at least 4, capped at kMaxRowCap
-int rows_per_pass(int64_t M) {
+}  // namespace
+
+int grouped_rows_per_pass(int64_t M) {
   int r = 4;
   while (r < M && r < kMaxRowCap) r <<= 1;
   return r;
 }
 
-}  // namespace
-
 int grouped_row_tiles(int64_t M, int top_k) {
   (void)top_k;
-  const int r = rows_per_pass(M);
+  const int r = grouped_rows_per_pass(M);
   return r <= 16 ? 1 : r / 16;
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s) {
-  const int rowcap = rows_per_pass(a.M);
+  const int rowcap = grouped_rows_per_pass(a.M);
   return fp8 ? launch_gate_up_fp8(a, row_tiles, rowcap, tiled, s) : launch_gate_up_bf16(a, row_tiles, rowcap, tiled, s);
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s) {
-  const int rowcap = rows_per_pass(a.M);
+  const int rowcap = grouped_rows_per_pass(a.M);
   return fp8 ? launch_down_fp8(a, row_tiles, rowcap, tiled, s) : launch_down_bf16(a, row_tiles, rowcap, tiled, s);
 }
 

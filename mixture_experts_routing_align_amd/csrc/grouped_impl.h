@@ -42,58 +42,20 @@
 #include <algorithm>
 
 #include "align_device.h"
+#include "mma_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace grouped_detail {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace mma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;  // 4 wave64 per workgroup
-constexpr int kWaveCols = 16;   // output columns per wave: one MFMA tile edge
 constexpr int kTileCols = 64;   // output columns per workgroup
-constexpr int kKC = 128;        // depth of one chunk (= one FP8 scale block)
-constexpr int kPad = 8;         // bf16 elements of padding per staged row (16 B)
 constexpr int kMaxRowCap = 128; // most rows one pass stages
 constexpr size_t kResidentLdsBudget = 80 * 1024;
 constexpr int kMaxScaleBlocks = 128;  // FP8 depth limit: 128 scale blocks = 16384
-
-__host__ __device__ constexpr int round_up(int v, int m) { return (v + m - 1) / m * m; }
-
-__device__ __forceinline__ uint16_t bf16_rne_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-// 8 FP8 e4m3 codes (two dwords, lowest byte first) -> 8 bf16, exact.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Element offset, inside a 128-deep chunk, of the 8 consecutive k a lane of
-// quad q feeds to MFMA step s.  The A and B operands use the same map, so the
-// k order inside one MFMA is a permutation the product does not see.
-//  FP8: one 16-byte load holds 16 codes = steps s and s+1 (s even).
-//  BF16: one 16-byte load holds 8 elements = one step.
-template <bool FP8>
-__device__ __forceinline__ int k_of_step(int s, int q) {
-  return FP8 ? ((s >> 1) * 64 + q * 16 + (s & 1) * 8) : (s * 32 + q * 8);
-}
 
 // LDS bytes of the fused alignment region for E experts and n slots.
 __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
@@ -393,21 +355,37 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
                   *reinterpret_cast<const uint4*>(xb + x * plane + rowc * stride + k_of_step<FP8>(s, q)));
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
-            if (FP8) {
+            if (GATE_UP && FP8) {
               f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int x = 0; x < NX; ++x) t = mfma(a[st][s], b[x][s], t);
+              for (int s = 0; s < 4; ++s) t = mfma(a[st][s], b[0][s], t);
 #pragma unroll
               for (int i = 0; i < 4; ++i) acc[st][rt][i] = fmaf(sc[st], t[i], acc[st][rt][i]);
-            } else {
+            } else if (GATE_UP) {
               // bf16 depth comes in whole 32-deep steps; steps past K are skipped
 #pragma unroll
               for (int s = 0; s < 4; ++s)
-                if (k0 + s * 32 < K)
+                if (k0 + s * 32 < K) acc[st][rt] = mfma(a[st][s], b[0][s], acc[st][rt]);
+            } else {
+              // down: each 64-deep half of the chunk is multiplied from zero,
+              // scaled (FP8), rounded and then added to the sum (no fused
+              // multiply-add), so partial sums over 64-deep slices formed
+              // elsewhere and added in the same order give the same bits;
+              // bf16 steps past K are skipped, a half wholly past K adds nothing
 #pragma unroll
-                  for (int x = 0; x < NX; ++x) acc[st][rt] = mfma(a[st][s], b[x][s], acc[st][rt]);
+              for (int h = 0; h < 2; ++h) {
+                if (FP8 || k0 + 64 * h < K) {
+                  f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int s = 2 * h; s < 2 * h + 2; ++s)
+                    if (FP8 || k0 + s * 32 < K)
+#pragma unroll
+                      for (int x = 0; x < NX; ++x) t = mfma(a[st][s], b[x][s], t);
+#pragma unroll
+                  for (int i = 0; i < 4; ++i)
+                    acc[st][rt][i] = add_rn(acc[st][rt][i], FP8 ? mul_rn(sc[st], t[i]) : t[i]);
+                }
+              }
             }
           }
         }
@@ -423,10 +401,10 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
           float4 v;
           if (GATE_UP) {
             const f32x4 g = acc[0][rt], u = acc[NS - 1][rt];
-            v.x = g[0] / (1.0f + expf(-g[0])) * u[0];
-            v.y = g[1] / (1.0f + expf(-g[1])) * u[1];
-            v.z = g[2] / (1.0f + expf(-g[2])) * u[2];
-            v.w = g[3] / (1.0f + expf(-g[3])) * u[3];
+            v.x = silu_mul(g[0], u[0]);
+            v.y = silu_mul(g[1], u[1]);
+            v.z = silu_mul(g[2], u[2]);
+            v.w = silu_mul(g[3], u[3]);
           } else {
             v.x = acc[0][rt][0];
             v.y = acc[0][rt][1];

@@ -63,9 +63,12 @@ struct GroupedArgs {
 // alignment cost grows with n; above this the layer runs the align kernel).
 constexpr int kFusedAlignMaxSlots = MOE_FUSED_ALIGN_MAX_SLOTS;
 
-// Row tiles (16 rows each) one workgroup keeps in registers per pass over the
-// weights; chosen from the shape class (the most rows an expert can hold), never
-// from the routing.
+// Rows one pass over the weights stages: the most an expert holds when ids are
+// distinct within a token (M), as a power of two of at least 4, at most 128.
+// Chosen from the shape class, never from the routing.
+int grouped_rows_per_pass(int64_t M);
+
+// Row tiles (16 rows each) one workgroup keeps in registers per pass.
 int grouped_row_tiles(int64_t M, int top_k);
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
@@ -74,6 +77,36 @@ hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int r
 // The tiled (MFMA-fragment-ordered) copy of row-major [E, N, K] weights.
 size_t tiled_weight_bytes(bool fp8, int64_t E, int N, int K);
 hipError_t launch_tile_weights(const void* src, void* dst, bool fp8, int64_t E, int N, int K, hipStream_t s);
+
+// Single-pass decode layer: one launch aligns (in LDS), runs gate+up+SiLU for a
+// 128-wide slice of the intermediate and the matching 128-deep slice of down
+// per workgroup, and writes float32 partial outputs per slice; a second launch
+// sums the slices and blends.  Tiled weights only.
+struct FusedLayerArgs {
+  const void* ids;
+  int ids64;
+  const void* x;          // bf16 [M, H]
+  const void* w[3];       // routed gate, up [E, I, H] and down [E, H, I], tiled
+  const float* s[3];      // their FP8 scales (unused for bf16)
+  const void* sw[3];      // shared expert (sw[0] == nullptr: none), tiled
+  const float* ss[3];
+  const float* topk_weights;
+  uint16_t* out;          // bf16 [M, H]
+  float* part;            // [ceil(I/128)][n][H] routed partials by slot
+  float* sh_part;         // [ceil(S/128)][M][H] shared partials by token
+  int M, H, I, S, E, top_k, BS, n, cap, max_total;
+  AlignOut tables;
+};
+
+// Most slots the single-pass layer takes (its partial outputs grow with n).
+constexpr int kFusedLayerMaxSlots = 256;
+
+// Whether the single-pass layer runs this shape (tiled weights assumed): slot
+// count, depth limits and the LDS it needs.
+bool fused_layer_fits(bool fp8, int64_t M, int H, int I, int S, int E, int top_k);
+// the first launch (align, gate+up+SiLU, down partials) and the second (sum + blend)
+hipError_t launch_layer_partials(const FusedLayerArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_blend_partials(const FusedLayerArgs& a, hipStream_t s);
 
 hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,
                         const float* sh_out, int M, int H, int top_k, hipStream_t s);

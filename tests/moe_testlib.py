@@ -52,6 +52,12 @@ class DeviceModel(DeviceWeights):
         return MoeLayer(self.weight("gate"), self.weight("up"), self.weight("down"), self.cfg.top_k, self.cfg.BS,
                         sh.get("gate"), sh.get("up"), sh.get("down"))
 
+    def tiled_layer(self):
+        """The layer with tiled weights (built once per model)."""
+        if getattr(self, "_tiled", None) is None:
+            self._tiled = self.layer().tiled()
+        return self._tiled
+
     def routed_weight(self, which, e):
         if self.host is not None:
             return self.host[(which, e)]

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -125,26 +125,40 @@ def _desc(M=8, H=2048, I=768, S=0, E=128, top_k=8, BS=16, wdt=1, idt=1):
     return _ffi.MoeLayerDesc(M, H, I, S, E, top_k, BS, wdt, idt, w, w, w, sh, sh, sh)
 
 
-def test_workspace_layout(lib):
+def _tiled(d):
+    d.wdt = _ffi.MOE_W_FP8_E4M3_TILED if d.wdt == _ffi.MOE_W_FP8_E4M3 else _ffi.MOE_W_BF16_TILED
+    return d
+
+
+@pytest.mark.parametrize("tiled", [False, True])
+def test_workspace_layout(lib, tiled):
+    R = _ffi.MOE_LAYER_WORKSPACE_REGIONS
     for kw in (dict(), dict(M=128, S=2048), dict(M=64, H=7168, E=256, I=2048, S=2048, BS=64),
-               dict(M=4, H=256, E=8, top_k=2, I=128, wdt=0)):
+               dict(M=4, H=256, E=8, top_k=2, I=128, wdt=0), dict(M=5, H=256, S=256, I=384)):
         d = _desc(**kw)
-        off = (ctypes.c_size_t * 13)()
+        if tiled:
+            d = _tiled(d)
+        off = (ctypes.c_size_t * (R + 1))()
         assert lib.moe_layer_workspace_layout(ctypes.byref(d), off) == _ffi.MOE_OK
         a = {k: v for k, v in dict(M=8, H=2048, I=768, S=0, E=128, top_k=8, BS=16).items()}
         a.update({k: v for k, v in kw.items() if k in a})
         n = a["M"] * a["top_k"]
         mt = oracle.max_total(n, a["E"], a["BS"])
+        path = lib.moe_layer_path(ctypes.byref(d))
+        # the single pass runs tiled weights at decode width (at most 256 slots)
+        assert path == (_ffi.MOE_LAYER_PATH_SINGLE_PASS if tiled and n <= 256 else _ffi.MOE_LAYER_PATH_STEPS)
+        single = path == _ffi.MOE_LAYER_PATH_SINGLE_PASS
+        M, H, I, S = a["M"], a["H"], a["I"], a["S"]
         sizes = [mt * 4, mt // a["BS"] * 4, (a["E"] + 1) * 4, a["E"] * 4, n * 4, min(n, a["E"]) * 4, 4, 4,
-                 mt * a["I"] * 4, mt * a["H"] * 4]
+                 0 if single else mt * I * 4, 0 if single else mt * H * 4,
+                 0 if single else M * S * 4, 0 if single else M * H * 4,
+                 -(-I // 64) * n * H * 4 if single else 0, -(-S // 64) * M * H * 4 if single else 0]
+        assert len(sizes) == R
         for i, s in enumerate(sizes):
             assert off[i] % 256 == 0
-            assert off[i + 1] >= off[i] + s if i + 1 < 10 else True
+            assert off[i + 1] >= off[i] + s, (kw, i)
         total = lib.moe_layer_workspace_bytes(ctypes.byref(d))
-        assert total == off[12] and total >= off[9] + sizes[9]
-        if a["S"]:
-            assert off[10] >= off[9] + sizes[9] and off[11] >= off[10] + a["M"] * a["S"] * 4
-            assert total >= off[11] + a["M"] * a["H"] * 4
+        assert total == off[R]
 
 
 def test_layer_refusals(lib):
@@ -187,3 +201,24 @@ def test_fused_align_gate_up_refusals(lib):
     bad.total = None
     assert lib.moe_align_gate_up_silu(FAKE, 1, FAKE, 1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad), FAKE,
                                       None, None, None, 4, 256, 128, 0, 8, 8, 16, None) == _ffi.MOE_ERR_NULL
+
+
+def test_single_pass_stage_refusals(lib):
+    """The stage calls refuse a descriptor that takes the steps path (row-major
+    weights, or more than 256 slots) and check the workspace like the layer."""
+    d = _desc()                                   # row-major FP8: steps path
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(d))
+    assert lib.moe_layer_partials(ctypes.byref(d), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
+    assert "single-pass" in _err(lib)
+    assert lib.moe_layer_blend_partials(ctypes.byref(d), FAKE, FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
+    big = _tiled(_desc(M=128))                    # 1024 slots
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(big))
+    assert lib.moe_layer_partials(ctypes.byref(big), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
+    t = _tiled(_desc())                           # decode shape, tiled: single pass
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(t))
+    assert lib.moe_layer_partials(ctypes.byref(t), FAKE, FAKE, 0x100000, need - 1, None) == _ffi.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_partials(ctypes.byref(t), None, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_layer_blend_partials(ctypes.byref(t), FAKE, None, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_NULL
+    t0 = _tiled(_desc(M=0))
+    assert lib.moe_layer_partials(ctypes.byref(t0), None, None, None, 0, None) == _ffi.MOE_OK
+

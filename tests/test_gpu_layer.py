@@ -32,8 +32,8 @@ def model_for(name, **kw):
     return _MODELS[name]
 
 
-def _run_layer(moe, model, xt, it, wt):
-    layer = model.layer()
+def _run_layer(moe, model, xt, it, wt, tiled=False):
+    layer = model.tiled_layer() if tiled else model.layer()
     ws = layer.alloc_workspace(xt.shape[0], moe.MOE_IDX_I64 if it.dtype == torch.int64 else moe.MOE_IDX_I32)
     out = layer.forward(xt, it, wt, workspace=ws)
     torch.cuda.synchronize()
@@ -123,6 +123,50 @@ def test_layer_int32_ids_same_bits(moe):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# ------------------------------------------------ single-pass decode layer --
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_single_pass_layer_parity(moe, name):
+    """Tiled weights at decode width take the single-pass path: tables bit-exact,
+    output and each slot's expert output (the sum of its slices) within tolerance."""
+    model = model_for(name)
+    cfg = model.cfg
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    log(f"single-pass parity: config {name}")
+    out, views = _run_layer(moe, model, xt, it, wt, tiled=True)
+    assert "act" not in views and "part" in views
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    log(f"  out: max err {err:.3e} bound {bound:.3e}")
+    assert ok, (err, bound)
+    perm = ref["tables"]["token_to_perm"]
+    slots = [i for i in range(perm.size) if perm[i] >= 0]
+    y = views["part"].double().sum(dim=0)[slots].cpu().numpy()
+    ok, err, bound = tolerance_ok(y, np.stack([ref["y_pos"][perm[i]] for i in slots]))
+    assert ok, ("expert output", err, bound)
+
+
+def test_single_pass_stages_equal_forward(moe):
+    """moe_layer_partials then moe_layer_blend_partials give moe_layer_forward's bits."""
+    model = model_for("decode")
+    _, (xt, it, wt) = device_inputs(model.cfg)
+    layer = model.tiled_layer()
+    a = layer.forward(xt, it, wt)
+    ws = layer.alloc_workspace(xt.shape[0])
+    moe.moe_layer_partials(layer, xt, it, ws)
+    b = moe.moe_layer_blend_partials(layer, it, wt, torch.empty_like(a), ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_single_pass_large_m_takes_steps(moe):
+    """More than 256 slots (verify: 1024) keeps the separate kernels even with tiled weights."""
+    model = model_for("verify")
+    assert model.tiled_layer().path(model.cfg.M) == moe.MOE_LAYER_PATH_STEPS
+
+
 # ------------------------------------------------ odd shapes, many passes --
 
 ODD = [
@@ -147,15 +191,19 @@ def test_layer_odd_shapes(moe, cfg):
     assert ok, (err, bound)
 
 
-def test_layer_repeated_ids_multi_pass(moe):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_layer_repeated_ids_multi_pass(moe, tiled):
     """Every slot of every token on one expert (ids repeat within a token): 96
-    rows on expert 2, more than one pass of row tiles for M=48."""
+    rows on expert 2, more than one pass of row tiles for M=48 (tiled: the
+    single-pass layer, 64 rows per pass)."""
     cfg = workloads.MoeConfig("repeat", 48, 128, 4, 2, 32, 0, 8, "bf16", "softmax", seed=11)
     model = DeviceModel(cfg, threads=4)
     (x, _, w), (xt, _, wt) = device_inputs(cfg)
     ids = np.full((cfg.M, cfg.top_k), 2, dtype=np.int64)
     it = torch.from_numpy(ids).cuda()
-    out, views = _run_layer(moe, model, xt, it, wt)
+    if tiled:
+        assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    out, views = _run_layer(moe, model, xt, it, wt, tiled=tiled)
     ref = oracle_layer(model, x, ids, w)
     compare_tables(views, ref["tables"])
     ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
@@ -179,14 +227,17 @@ def test_layer_out_of_range_ids(moe):
 
 # ------------------------------------------------------ bit-exact properties --
 
-@pytest.mark.parametrize("name,ms", [("decode", [1, 2, 3, 5, 7]), ("verify", [1, 9, 16, 33, 64, 100, 127])])
-def test_row_invariance(moe, name, ms):
+@pytest.mark.parametrize("name,ms,tiled", [("decode", [1, 2, 3, 5, 7], False),
+                                           ("verify", [1, 9, 16, 33, 64, 100, 127], False),
+                                           ("decode", [1, 2, 3, 5, 7], True)])
+def test_row_invariance(moe, name, ms, tiled):
     """Rows 0..m-1 of a run on the first m tokens equal the full run's rows bit for bit."""
     model = model_for(name)
     _, (xt, it, wt) = device_inputs(model.cfg)
-    full, _ = _run_layer(moe, model, xt, it, wt)
+    full, _ = _run_layer(moe, model, xt, it, wt, tiled=tiled)
     for m in ms:
-        part, _ = _run_layer(moe, model, xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous())
+        part, _ = _run_layer(moe, model, xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous(),
+                             tiled=tiled)
         assert torch.equal(part.view(torch.int16), full[:m].view(torch.int16)), m
 
 
@@ -237,12 +288,13 @@ def test_blend_parity_and_invariants(moe):
 
 # ------------------------------------------------------------ graph replay --
 
-def test_graph_replay_follows_new_routing(moe):
+@pytest.mark.parametrize("tiled", [False, True])
+def test_graph_replay_follows_new_routing(moe, tiled):
     """Capture the layer once; overwrite ids/weights in place between replays;
     every replay must match the oracle for the routing it saw."""
     model = model_for("decode")
     cfg = model.cfg
-    layer = model.layer()
+    layer = model.tiled_layer() if tiled else model.layer()
     (x, ids0, w0), (xt, it, wt) = device_inputs(cfg)
     ws = layer.alloc_workspace(cfg.M)
     out = torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device="cuda")
