@@ -1,4 +1,5 @@
-// Deterministic MoE token alignment for gfx950: one workgroup of 16 wave64s.
+// Deterministic MoE token alignment for gfx950: one workgroup of 16 wave64s, or
+// for many slots three launches over blocks of 1024 slots (see below).
 //
 // What it computes (nbxtensor 0.0.1 wheel page, moe_align.py: module docstring
 // and the stage-1/2/3 kernel docstrings; metrale fp8_moe_grouped.rs:
@@ -20,6 +21,7 @@ namespace {
 constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = kAlignWaves * 64;
 constexpr int kMaxExperts = 1024;
+constexpr int kAlignBlocksMinSlots = 4096;  // from here on the alignment runs over several blocks
 
 template <typename IdT>
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(const IdT* __restrict__ ids, int n, int E, int BS,
@@ -37,11 +39,207 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(const IdT* __restr
   align_dev::write_rest<kAlignWaves>(s, n, E, BS, max_total, cap, o);
 }
 
+// ---- large slot counts: three launches over blocks of kChunk slots ----------
+//
+// No atomics and no workspace: each block's per-expert counts, and later its
+// per-expert bases, live in the first E entries of its own token_to_perm range
+// (kChunk >= MOE_MAX_EXPERTS), which only that block's scatter overwrites, after
+// it has read them.  Order is the stable host order: blocks ascending, waves
+// ascending within a block, lanes ascending within a wave.
+constexpr int kChunk = 1024;      // slots per block (the last block also takes the remainder)
+constexpr int kBlockWaves = 8;
+constexpr int kBlockThreads = kBlockWaves * 64;
+static_assert(kChunk >= kMaxExperts, "a block's token_to_perm range must hold E counts");
+
+__device__ __forceinline__ void block_range(int n, int G, int& lo, int& hi) {
+  lo = blockIdx.x * kChunk;
+  hi = (int)blockIdx.x == G - 1 ? n : lo + kChunk;
+}
+
+// per-wave per-expert counts of the block's slots into cnt[wave][expert]
+template <typename IdT>
+__device__ void block_counts(const IdT* __restrict__ ids, int lo, int hi, int E, int nbits, int* cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < kBlockWaves * E; i += kBlockThreads) cnt[i] = 0;
+  __syncthreads();
+  const int per = (((hi - lo + kBlockWaves - 1) / kBlockWaves) + 63) & ~63;
+  const int beg = min(hi, lo + w * per), end = min(hi, beg + per);
+  int* my = cnt + w * E;
+  for (int c = beg; c < end; c += 64) {
+    bool valid;
+    const int id = align_dev::load_id(ids, c + lane, end, E, valid);
+    const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+    if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
+  }
+  __syncthreads();
+}
+
+// launch 1: the block's count of every expert -> token_to_perm[lo + e]
+template <typename IdT>
+__global__ __launch_bounds__(kBlockThreads) void align_count_blocks(const IdT* __restrict__ ids, int n, int G, int E,
+                                                                   int nbits, int32_t* token_to_perm) {
+  __shared__ int cnt[kBlockWaves * kMaxExperts];
+  int lo, hi;
+  block_range(n, G, lo, hi);
+  block_counts(ids, lo, hi, E, nbits, cnt);
+  for (int e = threadIdx.x; e < E; e += kBlockThreads) {
+    int s = 0;
+    for (int w = 0; w < kBlockWaves; ++w) s += cnt[w * E + e];
+    token_to_perm[lo + e] = s;
+  }
+}
+
+// launch 2 (one workgroup): per-expert totals, padded offsets, the active list,
+// every table that is not a slot, and each block's base per expert (the
+// expert's offset plus the counts of the blocks before it) in place of its count
+__global__ __launch_bounds__(kAlignThreads) void align_scan_blocks(int n, int G, int E, int BS, int max_total, int cap,
+                                                                  AlignOut o) {
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_active[kMaxExperts];
+  __shared__ int s_wa[kAlignWaves], s_wb[kAlignWaves];
+  // J threads per expert, each over a contiguous run of `per` blocks; counts of
+  // up to kBatch blocks are loaded together and kept for the bases
+  constexpr int kBatch = 16;
+  __shared__ int s_part[kAlignThreads];
+  const int tid = threadIdx.x;
+  const int J = max(1, kAlignThreads / E);
+  const int per = (G + J - 1) / J;
+  const int ex = tid % E, jx = tid / E;  // a wave reads consecutive experts of one block row
+  const bool owner = jx < J;
+  const int b_lo = min(G, jx * per), b_hi = min(G, b_lo + per);
+  int32_t* col = o.token_to_perm + (owner ? ex : 0);
+  int c[kBatch];
+  int part = 0;
+  if (owner) {
+    for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < b_hi ? col[(size_t)(b0 + j) * kChunk] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) part += c[j];
+    }
+    s_part[tid] = part;
+  }
+  __syncthreads();
+  const int e = tid;  // E <= threads
+  int count = 0;
+  if (e < E) {
+    for (int j = 0; j < J; ++j) count += s_part[j * E + e];
+  }
+  const int pad = (count + BS - 1) / BS * BS;
+  int ex_pad, ex_act, total, nact;
+  align_dev::block_scan2<kAlignWaves>(pad, count > 0 ? 1 : 0, s_wa, s_wb, ex_pad, ex_act, total, nact);
+  if (e < E) {
+    s_off[e] = ex_pad;
+    if (count > 0) s_active[ex_act] = e;
+  }
+  __syncthreads();
+  if (owner) {
+    // block b's base: the expert's offset plus the counts of blocks 0..b-1
+    int run = s_off[ex];
+    for (int j = 0; j < jx; ++j) run += s_part[j * E + ex];
+    for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+      if (b0 > b_lo || b_hi - b_lo > kBatch) {  // reload unless this run fit one batch
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) c[j] = b0 + j < b_hi ? col[(size_t)(b0 + j) * kChunk] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (b0 + j < b_hi) col[(size_t)(b0 + j) * kChunk] = run;
+        run += c[j];
+      }
+    }
+  }
+  // every table that is not a slot and not an expert's padding or block map
+  // (those the scatter blocks write, one wave per expert)
+  if (e < E) {
+    o.expert_counts[e] = count;
+    o.expert_offsets[e] = ex_pad;
+  }
+  if (e == 0) {
+    o.expert_offsets[E] = total;
+    *o.total = total;
+    *o.active_count = nact;
+  }
+  for (int j = tid; j < cap; j += kAlignThreads) o.active_experts[j] = j < nact ? s_active[j] : -1;
+  for (int p = total + tid; p < max_total; p += kAlignThreads) o.sorted_token_ids[p] = n;
+  for (int b = total / BS + tid; b < max_total / BS; b += kAlignThreads) o.block_expert_ids[b] = -1;
+}
+
+// launch 3: the stable scatter of the block's slots from its bases; besides,
+// wave w of block b writes the padding sentinels and block owners of experts
+// b + G * (w + kBlockWaves * i), lanes over consecutive entries
+template <typename IdT>
+__global__ __launch_bounds__(kBlockThreads) void align_scatter_blocks(const IdT* __restrict__ ids, int n, int G, int E,
+                                                                     int BS, int nbits, AlignOut o) {
+  __shared__ int cnt[kBlockWaves * kMaxExperts];
+  __shared__ int base[kMaxExperts];
+  int lo, hi;
+  block_range(n, G, lo, hi);
+  for (int e = threadIdx.x; e < E; e += kBlockThreads) base[e] = o.token_to_perm[lo + e];
+  block_counts(ids, lo, hi, E, nbits, cnt);  // its first barrier: every base is read before any slot is written
+  for (int e = threadIdx.x; e < E; e += kBlockThreads) {
+    int run = base[e];
+    for (int w = 0; w < kBlockWaves; ++w) {
+      const int c = cnt[w * E + e];
+      cnt[w * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (((hi - lo + kBlockWaves - 1) / kBlockWaves) + 63) & ~63;
+  const int beg = min(hi, lo + w * per), end = min(hi, beg + per);
+  int* my = cnt + w * E;
+  for (int c = beg; c < end; c += 64) {
+    const int i = c + lane;
+    bool valid;
+    const int id = align_dev::load_id(ids, i, end, E, valid);
+    const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+    if (valid) {
+      const int pos = my[id] + __popcll(m & align_dev::lanes_below(lane));
+      o.sorted_token_ids[pos] = i;
+      o.token_to_perm[i] = pos;
+    } else if (i < end) {
+      o.token_to_perm[i] = -1;
+    }
+    // every lane has read its base above (a wave's LDS operations run in order)
+    if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
+  }
+  for (int e = blockIdx.x + G * w; e < E; e += G * kBlockWaves) {
+    const int e_lo = o.expert_offsets[e], e_hi = o.expert_offsets[e + 1];
+    for (int p = e_lo + o.expert_counts[e] + lane; p < e_hi; p += 64) o.sorted_token_ids[p] = n;
+    for (int b = e_lo / BS + lane; b < e_hi / BS; b += 64) o.block_expert_ids[b] = e;
+  }
+}
+
 }  // namespace
+
+int align_blocks(int n) { return n >= kAlignBlocksMinSlots ? n / kChunk : 0; }
 
 hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap,
                         const AlignOut& o, hipStream_t s) {
   const int nbits = align_dev::id_bits(E);
+  const int G = align_blocks(n);
+  if (G > 0) {  // many slots: count, scan, scatter over G blocks
+    if (ids64)
+      hipLaunchKernelGGL(align_count_blocks<int64_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                         static_cast<const int64_t*>(ids), n, G, E, nbits, o.token_to_perm);
+    else
+      hipLaunchKernelGGL(align_count_blocks<int32_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                         static_cast<const int32_t*>(ids), n, G, E, nbits, o.token_to_perm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(align_scan_blocks, dim3(1), dim3(kAlignThreads), 0, s, n, G, E, BS, max_total, cap, o);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ids64)
+      hipLaunchKernelGGL(align_scatter_blocks<int64_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                         static_cast<const int64_t*>(ids), n, G, E, BS, nbits, o);
+    else
+      hipLaunchKernelGGL(align_scatter_blocks<int32_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                         static_cast<const int32_t*>(ids), n, G, E, BS, nbits, o);
+    return hipGetLastError();
+  }
   if (ids64)
     hipLaunchKernelGGL(align_kernel<int64_t>, dim3(1), dim3(kAlignThreads), 0, s,
                        static_cast<const int64_t*>(ids), n, E, BS, max_total, cap, nbits, o);

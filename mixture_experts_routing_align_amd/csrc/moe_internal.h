@@ -23,7 +23,9 @@ struct AlignOut {
   int32_t* total;
 };
 
-// One launch, one workgroup: the whole alignment.
+// The whole alignment: one launch and one workgroup, or for n >= 4096 slots
+// three launches over align_blocks(n) blocks (count, scan, scatter).
+int align_blocks(int n);
 hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap,
                         const AlignOut& o, hipStream_t s);
 

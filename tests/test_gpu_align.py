@@ -41,6 +41,13 @@ ADVERSARIAL = [
     ("large_bs", lambda r: r.integers(0, 32, size=(64, 2)), 32, 256),
     ("all_invalid", lambda r: np.full((20, 2), -1), 8, 4),
     ("skewed_big", lambda r: np.minimum(r.geometric(0.05, size=(8192, 4)), 300), 300, 32),
+    # from 4096 slots on, the alignment runs over blocks of 1024 slots (count, scan, scatter)
+    ("blocks_one_expert", lambda r: np.full((5000, 2), 7), 16, 64),
+    ("blocks_max_experts", lambda r: r.integers(-1, 1025, size=(1500, 7)), 1024, 8),
+    ("blocks_exact_4096", lambda r: r.integers(0, 64, size=(512, 8)), 64, 16),
+    ("below_blocks_4095", lambda r: r.integers(0, 64, size=(4095, 1)), 64, 16),
+    ("blocks_ragged_tail", lambda r: r.integers(-2, 40, size=(2047, 3)), 37, 5),
+    ("blocks_bs1", lambda r: r.integers(0, 200, size=(3000, 4)), 200, 1),
 ]
 
 
@@ -73,7 +80,7 @@ def test_align_random_shapes(seed):
     rng = np.random.default_rng(1000 + seed)
     E = int(rng.integers(1, 1025))
     BS = int(rng.choice([1, 2, 4, 16, 64, 128]))
-    M = int(rng.integers(1, 3000))
+    M = int(rng.integers(1, 3000 if seed < 4 else 6000))
     top_k = int(rng.integers(1, 9))
     ids = rng.integers(-1, E + 1, size=(M, top_k))
     log(f"align random: seed={seed} M={M} top_k={top_k} E={E} BS={BS}")
