@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="weight copies / routings cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-reps", type=int, default=25)
+    ap.add_argument("--other-configs", default="",
+                    help="comma-separated workloads (tiny, verify, large) also timed whole-layer and reported "
+                         "under other_configs (context for the headline, not the headline)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (counter calibration) and exit")
     return ap.parse_args()
@@ -117,6 +120,58 @@ def traffic_from_profile(digest):
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def measure_config(name, dev, steps=50):
+    """Whole-layer time of one workload, with the headline's method: a graph of
+    one step per (weight copy, routing) pair, replayed; weights tiled."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_routing_align_amd as moe
+    import workloads
+    from workloads.device import DeviceWeights
+
+    cfg = workloads.CONFIGS[name]
+    G = 2 if cfg.E * cfg.I * cfg.H > (1 << 31) else 4  # the large workload: 2 copies of its 11 GB
+    log(f"other config {name}: generating weights, {G} copies")
+    w0 = DeviceWeights(cfg, device=dev, threads=16)
+    copies = [w0] + [w0.clone() for _ in range(G - 1)]
+    layers = []
+    for c in copies:
+        sh = c.sh or {}
+        layers.append(moe.MoeLayer(c.weight("gate"), c.weight("up"), c.weight("down"), cfg.top_k, cfg.BS,
+                                   sh.get("gate"), sh.get("up"), sh.get("down")).tiled())
+        c.w = c.s = None
+        torch.cuda.empty_cache()
+    routings = [workloads.routing(cfg.replace(seed=cfg.seed + r)) for r in range(G)]
+    xt = torch.from_numpy(workloads.x_bf16(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+    ids_d = [torch.from_numpy(ids).to(dev) for ids, _ in routings]
+    w_d = [torch.from_numpy(w).to(dev) for _, w in routings]
+    outs = [torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device=dev) for _ in range(G)]
+    wss = [layers[i].alloc_workspace(cfg.M) for i in range(G)]
+    sh_bytes = 0
+    if cfg.S:
+        esz = 1 if cfg.wdt == "fp8" else 2
+        sh_bytes = 3 * cfg.S * cfg.H * esz + (3 * (cfg.S // 128) * (cfg.H // 128) * 4 if cfg.wdt == "fp8" else 0)
+    per = [w0.algorithmic_bytes(ids)["total"] for ids, _ in routings]
+    stream = torch.cuda.Stream(device=dev)
+    multi = graph_of(lambda: [layers[i].forward(xt, ids_d[i], w_d[i], out=outs[i], workspace=wss[i])
+                              for i in range(G)], stream)
+    steps = max(G, steps // G * G)
+    elapsed = time_graphs(multi, [multi] * G, steps, G)
+    us = elapsed / steps * 1e6
+    nbytes = float(np.mean(per))
+    res = {
+        "layer_us": us, "rows_per_s": cfg.M / (us * 1e-6), "weight_bytes_per_call": nbytes,
+        "weight_gbps": nbytes / (us * 1e-6) / 1e9, "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "path": "single_pass" if layers[0].path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS else "steps",
+        "weight_copies": G, "shared_expert_bytes": sh_bytes,
+        "workload": f"M={cfg.M} H={cfg.H} E={cfg.E} top_k={cfg.top_k} I={cfg.I} S={cfg.S} BS={cfg.BS} {cfg.wdt}",
+    }
+    del layers, wss, outs, w0
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(cfg, routings):
@@ -329,6 +384,8 @@ def main():
         "launch_floor_us": floor_us,
         "read_ceiling_gbps": read_gbps,
     }
+    if args.other_configs:
+        result["other_configs"] = {name: measure_config(name, dev) for name in args.other_configs.split(",") if name}
     if not args.no_cpu_baseline:
         log("cpu baseline: float64 oracle")
         result["cpu_baseline"] = cpu_baseline(cfg, routings)

@@ -56,6 +56,7 @@ constexpr int kTileCols = 64;   // output columns per workgroup
 constexpr int kMaxRowCap = 128; // most rows one pass stages
 constexpr size_t kResidentLdsBudget = 80 * 1024;
 constexpr int kMaxScaleBlocks = 128;  // FP8 depth limit: 128 scale blocks = 16384
+constexpr int kMaxTilesPerGroup = 2;  // most 64-column tiles one workgroup runs in a row
 
 // LDS bytes of the fused alignment region for E experts and n slots.
 __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
@@ -528,7 +529,9 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
     configured = lds;
   }
   // column tiles per workgroup: the fewest that let every workgroup of the
-  // worst case (all `rows_y` experts active) be resident at once
+  // worst case (all `rows_y` experts active) be resident at once, but at most
+  // kMaxTilesPerGroup, so a wide grid (many experts, large M) keeps its
+  // parallelism instead of serialising the columns inside few workgroups
   static size_t occ_lds = (size_t)-1;  // occupancy of this kernel at the last LDS size asked
   static int occ_per_cu = 0;
   if (occ_lds != lds) {
@@ -541,7 +544,7 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
   }
   const int slots = std::max(1, occ_per_cu) * device_cus();
   int ctw = 1;
-  while (ctw < tiles && (long long)rows_y * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
+  while (ctw < tiles && ctw < kMaxTilesPerGroup && (long long)rows_y * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
   const dim3 grid((tiles + ctw - 1) / ctw, rows_y);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, rowcap, ctw, xs_bytes);
   return hipGetLastError();
