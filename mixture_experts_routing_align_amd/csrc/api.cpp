@@ -526,9 +526,10 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   float* sh_act = shared ? reinterpret_cast<float*>(ws + off[10]) : nullptr;
   float* sh_out = shared ? reinterpret_cast<float*>(ws + off[11]) : nullptr;
 
-  if (n <= moe::kFusedAlignMaxSlots) {
-    // few slots: every gate+up workgroup aligns topk_ids itself (in LDS) and
-    // one writes the tables, which saves the align launch and its latency
+  if (n <= moe::kFusedAlignMaxSlots && moe::grouped_passes(d->M) == 1) {
+    // few slots and one workgroup row per expert: every gate+up workgroup
+    // aligns topk_ids itself (in LDS) and one writes the tables, which saves
+    // the align launch and its latency
     if ((rc = moe_align_gate_up_silu(topk_ids, d->idt, x_bf16, d->wdt, &d->gate, &d->up, &t, act,
                                      shared ? &d->sh_gate : nullptr, shared ? &d->sh_up : nullptr, sh_act, d->M,
                                      d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))

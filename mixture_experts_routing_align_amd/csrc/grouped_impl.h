@@ -81,8 +81,12 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   const int q = lane >> 4, r16 = lane & 15;
   const int by = blockIdx.y;
 
-  // ---- which expert / rows this workgroup serves
-  const bool routed = by < p.cap;
+  // ---- which expert / rows this workgroup serves: workgroup row by < cap *
+  // passes is pass group pg = by / cap of active expert a = by % cap, which runs
+  // the expert's row passes pg, pg + passes, ...; the rows after those are
+  // shared-expert row groups
+  const bool routed = by < p.cap * p.passes;
+  const int a_idx = routed ? by % p.cap : 0, pg = routed ? by / p.cap : 0;
   int e = 0, rows = 0, row_base = 0, N, K;
   const int* fsrc = nullptr;  // fused: sources of all of the expert's rows
   if (routed) {
@@ -100,8 +104,8 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       align_dev::count_pass<kWaves>(ids, p.n, E, nbits, s.cnt);
       align_dev::expert_scan<kWaves>(s, E, p.BS);
       const int nact = s.scal[0];
-      if (by < nact) {
-        e = s.active[by];
+      if (a_idx < nact) {
+        e = s.active[a_idx];
         rows = s.count[e];
         row_base = s.off[e];
         align_dev::expert_rows<kWaves>(ids, p.n, E, nbits, s.cnt, e, p.top_k, src_all);
@@ -112,13 +116,14 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
                                         p.tables.token_to_perm);
         align_dev::write_rest<kWaves>(s, p.n, E, p.BS, p.max_total, p.cap, p.tables);
       }
-      if (by >= nact) return;
+      if (a_idx >= nact || pg * rowcap >= rows) return;
       fsrc = src_all;
     } else {
       const int nact = *p.active_count;  // both loads in flight together
-      const int e0 = p.active_experts[by];
-      if (by >= nact) return;
+      const int e0 = p.active_experts[a_idx];
+      if (a_idx >= nact) return;
       e = e0;
+      if (p.passes > 1 && pg * rowcap >= p.expert_counts[e]) return;  // no pass for this group
     }
   } else {
     N = p.sN;
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     rows = p.expert_counts[e];
     row_base = p.expert_offsets[e];
   } else if (!routed) {
-    row_base = (by - p.cap) * rowcap;
+    row_base = (by - p.cap * p.passes) * rowcap;
     rows = min(rowcap, p.M - row_base);
   }
 
@@ -275,11 +280,12 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     }
   };
 
-  for (int r0 = 0; r0 < rows; r0 += rowcap) {
+  const int first_r0 = routed ? pg * rowcap : 0;
+  for (int r0 = first_r0; r0 < rows; r0 += (routed ? p.passes : 1) * rowcap) {
     const int nr = min(rowcap, rows - r0);
     const int nrt = (nr + 15) >> 4;
 
-    if (r0 > 0) {  // a later pass streams the weights again from the start
+    if (r0 > first_r0) {  // a later pass streams the weights again from the start
       lt = t_begin;
       lc = 0;
       set_load_tile(lt);
@@ -570,7 +576,7 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   const int nmax = (a.sw0 != nullptr && a.sN > a.N) ? a.sN : a.N;
   const int shared_groups = a.sw0 != nullptr ? (a.M + rowcap - 1) / rowcap : 0;
   const int tiles = (nmax + kTileCols - 1) / kTileCols;
-  const int rows_y = a.cap + shared_groups;
+  const int rows_y = a.cap * a.passes + shared_groups;
   if (resident <= kResidentLdsBudget)
     return launch_fused_or_not<FP8, GATE_UP, RT, true, TILED>(a, rowcap, resident, tiles, rows_y, s);
   return launch_fused_or_not<FP8, GATE_UP, RT, false, TILED>(a, rowcap, chunked, tiles, rows_y, s);
@@ -578,12 +584,8 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
 
 template <bool FP8, bool GATE_UP, bool TILED>
 hipError_t launch_layout(const GroupedArgs& a, int rt, int rowcap, hipStream_t s) {
-  switch (rt) {
-    case 1: return launch_rt<FP8, GATE_UP, 1, TILED>(a, rowcap, s);
-    case 2: return launch_rt<FP8, GATE_UP, 2, TILED>(a, rowcap, s);
-    case 4: return launch_rt<FP8, GATE_UP, 4, TILED>(a, rowcap, s);
-    default: return launch_rt<FP8, GATE_UP, 8, TILED>(a, rowcap, s);
-  }
+  (void)rt;  // one 16-row tile per pass: the row passes of an expert are spread over workgroups
+  return launch_rt<FP8, GATE_UP, 1, TILED>(a, rowcap, s);
 }
 
 template <bool FP8, bool GATE_UP>

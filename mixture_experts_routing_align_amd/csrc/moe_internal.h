@@ -54,6 +54,7 @@ struct GroupedArgs {
   const int32_t* active_experts;
   const int32_t* active_count;
   int M, top_k, cap;
+  int passes;  // row-pass groups per expert (workgroup rows per active expert), >= 1
   // fused alignment (gate+up only; ids != nullptr): every routed workgroup
   // aligns topk_ids in LDS itself, and workgroup (0, 0) writes `tables`
   const void* ids;
@@ -72,6 +73,11 @@ int grouped_rows_per_pass(int64_t M);
 
 // Row tiles (16 rows each) one workgroup keeps in registers per pass.
 int grouped_row_tiles(int64_t M, int top_k);
+
+// The separate grouped kernels: rows per pass (at most 16) and the number of
+// workgroup rows per active expert that share an expert's row passes.
+int grouped_step_rows(int64_t M);
+int grouped_passes(int64_t M);
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
