@@ -105,7 +105,7 @@ def source_digest():
 
 
 def traffic_from_profile(digest):
-    """HBM bytes per gate+up launch from the committed rocprofv3 counter summary,
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
     if not os.path.exists(PROFILE_PMC):
         return None
