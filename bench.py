@@ -328,16 +328,51 @@ def main():
     ev1.synchronize()
     align_ev_us = ev0.elapsed_time(ev1) * 1e3 / areps
 
-    # plain streaming-read ceiling measured in the same run (context for % of peak)
-    big = torch.ones(1 << 30, dtype=torch.float32, device=dev)  # 4 GiB
-    big.sum()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(5):
-        big.sum()
-    torch.cuda.synchronize()
-    read_gbps = 5 * big.numel() * 4 / (time.perf_counter() - t0) / 1e9
+    # plain streaming-read ceiling in the same run: one launch of the library's
+    # read-only kernel over as many bytes as one layer streams (G disjoint
+    # buffers in rotation, like the weight copies), best of a few grid sizes;
+    # and the steady rate of one 4 GiB read
+    log("streaming-read ceiling")
+    nb = int(layer_bytes) // 16 * 16
+    bufs = [torch.ones(nb // 4, dtype=torch.int32, device=dev) for _ in range(G)]
+    ceiling = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(4 * blocks, dtype=torch.int32, device=dev)
+        g = graph_of(lambda: [moe.moe_stream_read_probe(bufs[i], sink, blocks, stream=stream) for _ in range(R)
+                              for i in range(G)], stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+            ev0.record(stream)
+            for _ in range(3):
+                g.replay()
+            ev1.record(stream)
+        ev1.synchronize()
+        ceiling[blocks] = ev0.elapsed_time(ev1) * 1e3 / (3 * R * G)
+    del bufs
+    best_blocks = min(ceiling, key=ceiling.get)
+    same_bytes_us = ceiling[best_blocks]
+    big = torch.ones(1 << 30, dtype=torch.int32, device=dev)  # 4 GiB
+    sink = torch.empty(4 * 8192, dtype=torch.int32, device=dev)
+    moe.moe_stream_read_probe(big, sink, 8192, stream=stream)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(5):
+            moe.moe_stream_read_probe(big, sink, 8192, stream=stream)
+        ev1.record(stream)
+    ev1.synchronize()
+    big_gbps = 5 * big.numel() * 4 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
     del big
+    stream_ceiling = {
+        "kernel": "stream_read_kernel (moe_stream_read_probe: 16-byte loads, nothing else)",
+        "same_bytes_us": same_bytes_us,
+        "same_bytes_gbps": nb / (same_bytes_us * 1e-6) / 1e9,
+        "same_bytes_blocks": best_blocks,
+        "us_by_blocks": {str(k): v for k, v in ceiling.items()},
+        "gib4_gbps": big_gbps,
+        "layer_partials_frac_of_same_bytes": same_bytes_us / kernels_us["layer_partials"],
+    }
 
     digest = source_digest()
     traffic = traffic_from_profile(digest)
@@ -382,7 +417,7 @@ def main():
         "align_us_events": align_ev_us,
         "align_workload": "n = 4096 x 8 int64 ids, Zipf(1.1), 256 experts, BS 64 (20 aligns per graph, HIP events)",
         "launch_floor_us": floor_us,
-        "read_ceiling_gbps": read_gbps,
+        "stream_ceiling": stream_ceiling,
     }
     if args.other_configs:
         result["other_configs"] = {name: measure_config(name, dev) for name in args.other_configs.split(",") if name}

@@ -400,6 +400,17 @@ def moe_layer_blend_partials(layer: MoeLayer, topk_ids, topk_weights, out, works
     return out
 
 
+def moe_stream_read_probe(src, sink, blocks: int = 2048, stream=None):
+    """One plain streaming read of the whole of `src` (a contiguous device
+    tensor, size a multiple of 16 bytes); `sink` is an int32 device tensor of at
+    least 4 * blocks elements.  A measurement aid: the read rate it reaches is
+    the ceiling the layer's weight stream is compared with."""
+    if sink.numel() < 4 * blocks:
+        raise ValueError("sink needs at least 4 * blocks int32 elements")
+    _check(lib().moe_stream_read_probe(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), blocks,
+                                       _stream(stream)))
+
+
 def moe_layer_workspace_bytes(layer: MoeLayer, M: int, idt: int = MOE_IDX_I64) -> int:
     return layer.workspace_bytes(M, idt)
 

@@ -84,6 +84,7 @@ SIGNATURES = {
     "moe_layer_blend_partials": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                          c_void_p]),
     "moe_tiled_weight_bytes": (c_size_t, [c_int, c_int64, c_int32, c_int32]),
+    "moe_stream_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]),
     "moe_tile_weights": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int32, c_void_p]),
 }
 

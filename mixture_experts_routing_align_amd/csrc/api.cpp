@@ -199,7 +199,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -545,6 +545,16 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
                              d->M, d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))
     return rc;
   return moe_blend(out_bf16, expert_out, topk_weights, t.token_to_perm, sh_out, d->M, d->H, d->top_k, stream);
+}
+
+int moe_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, hipStream_t stream) {
+  const char* fn = "moe_stream_read_probe";
+  if (bytes % 16) return fail(MOE_ERR_SHAPE, "%s: bytes=%zu is not a multiple of 16", fn, bytes);
+  if (blocks < 1 || blocks > 65536) return fail(MOE_ERR_SHAPE, "%s: blocks=%d outside [1, 65536]", fn, blocks);
+  if (bytes == 0) return MOE_OK;
+  if (!src || !sink) return fail(MOE_ERR_NULL, "%s: src or sink is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(src) % 16) return fail(MOE_ERR_SHAPE, "%s: src is not 16-byte aligned", fn);
+  return hip_status(moe::launch_stream_read(src, bytes, sink, blocks, stream), fn);
 }
 
 }  // extern "C"

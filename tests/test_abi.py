@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -222,3 +222,14 @@ def test_single_pass_stage_refusals(lib):
     t0 = _tiled(_desc(M=0))
     assert lib.moe_layer_partials(ctypes.byref(t0), None, None, None, 0, None) == _ffi.MOE_OK
 
+
+
+def test_stream_read_probe_refusals(lib):
+    assert lib.moe_stream_read_probe(FAKE, 24, FAKE, 8, None) == _ffi.MOE_ERR_SHAPE
+    assert "multiple of 16" in _err(lib)
+    assert lib.moe_stream_read_probe(FAKE, 32, FAKE, 0, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_stream_read_probe(FAKE, 32, FAKE, 65537, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_stream_read_probe(None, 32, FAKE, 8, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_stream_read_probe(FAKE, 32, None, 8, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_stream_read_probe(FAKE + 8, 32, FAKE, 8, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_stream_read_probe(None, 0, None, 8, None) == _ffi.MOE_OK

@@ -174,8 +174,13 @@ ODD = [
     workloads.MoeConfig("bf16_odd", 5, 96, 6, 3, 160, 96, 4, "bf16", "softmax", seed=7),
     # FP8, shared expert narrower than the routed one
     workloads.MoeConfig("fp8_small", 9, 256, 16, 4, 384, 128, 8, "fp8", "softmax_bias", bias_std=2.0, seed=8),
-    # 70 tokens -> 4 row tiles per pass; the skew puts > 64 rows on some experts (several passes)
+    # 70 tokens -> 16-row passes spread over 5 workgroup rows; the skew puts > 64 rows on some
+    # experts, so a workgroup row runs several passes
     workloads.MoeConfig("bf16_many_rows", 70, 128, 4, 2, 64, 0, 16, "bf16", "softmax_bias", bias_std=4.0, seed=9),
+    # >= 128 tokens: nine or more 16-row passes per expert, ~75 rows per expert, a partial
+    # 128-deep chunk and a shared expert
+    workloads.MoeConfig("bf16_wide", 150, 96, 4, 2, 160, 96, 4, "bf16", "softmax_bias", bias_std=4.0, seed=10),
+    workloads.MoeConfig("fp8_wide", 130, 256, 8, 2, 256, 128, 8, "fp8", "softmax_bias", bias_std=2.0, seed=11),
 ]
 
 
@@ -238,6 +243,18 @@ def test_row_invariance(moe, name, ms, tiled):
     for m in ms:
         part, _ = _run_layer(moe, model, xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous(),
                              tiled=tiled)
+        assert torch.equal(part.view(torch.int16), full[:m].view(torch.int16)), m
+
+
+@pytest.mark.parametrize("cfg", [c for c in ODD if c.M >= 128], ids=lambda c: c.name)
+def test_row_invariance_across_pass_shapes(moe, cfg):
+    """Rows of a run on the first m tokens equal the full run's rows bit for bit
+    for m that change the number of row passes and workgroup rows."""
+    model = DeviceModel(cfg, threads=4)
+    _, (xt, it, wt) = device_inputs(cfg)
+    full, _ = _run_layer(moe, model, xt, it, wt)
+    for m in (1, 17, 64, 127, 128, cfg.M - 1):
+        part, _ = _run_layer(moe, model, xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous())
         assert torch.equal(part.view(torch.int16), full[:m].view(torch.int16)), m
 
 
