@@ -298,9 +298,10 @@ int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[MOE_LAYER
  * device memory at `src` with 16-byte vector loads and does nothing else,
  * giving the plain HBM read rate for a buffer of that size against which the
  * layer's weight-stream bandwidth is judged.  `blocks` workgroups of 256
- * threads (1 <= blocks <= 65536) walk the buffer grid-stride; each wave
- * XOR-folds what it read into one 32-bit word of `sink` (device, at least
- * 4 * blocks words, caller-owned), so the loads are not dead.  `bytes` must be
+ * threads (1 <= blocks <= 65536) read it in 16 KB tiles, tile i by workgroup
+ * i mod blocks; each wave XOR-folds what it read into one 32-bit word of
+ * `sink` (device, at least 4 * blocks words, caller-owned), so the loads are
+ * not dead.  `bytes` must be
  * a multiple of 16 and `src` 16-byte aligned.  Errors: MOE_ERR_NULL (src or
  * sink NULL with bytes > 0), MOE_ERR_SHAPE (bytes not a multiple of 16, src
  * misaligned, blocks out of range), MOE_ERR_HIP.  bytes == 0 launches
