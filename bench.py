@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--other-configs", default="",
                     help="comma-separated workloads (tiny, verify, large) also timed whole-layer and reported "
                          "under other_configs (context for the headline, not the headline)")
+    ap.add_argument("--only-config", default="",
+                    help="time one other workload (tiny, verify or large) alone and print its line; for profiling")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (counter calibration) and exit")
     return ap.parse_args()
@@ -228,6 +230,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 8}))
+        return
+
+    if args.only_config:
+        res = measure_config(args.only_config, dev, steps=args.steps)
+        print(json.dumps({"only_config": args.only_config, **res}))
         return
 
     cfg = workloads.CONFIGS["decode"]
