@@ -62,25 +62,21 @@ int grouped_row_tiles(int64_t M, int top_k) {
 
 int grouped_step_rows(int64_t M) { return std::min(grouped_rows_per_pass(M), 16); }
 
-// an expert holds at most M rows when ids are distinct within a token; rows
-// past that (repeated ids) fall to the same groups' later passes
+// an expert holds at most M rows when ids are distinct within a token (with
+// repeated ids it can hold more, and gets more passes)
 int grouped_passes(int64_t M) {
   const int r = grouped_step_rows(M);
   return (int)std::max<int64_t>(1, (M + r - 1) / r);
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s) {
-  GroupedArgs b = a;
   const int rowcap = grouped_step_rows(a.M);
-  b.passes = grouped_passes(a.M);
-  return fp8 ? launch_gate_up_fp8(b, row_tiles, rowcap, tiled, s) : launch_gate_up_bf16(b, row_tiles, rowcap, tiled, s);
+  return fp8 ? launch_gate_up_fp8(a, row_tiles, rowcap, tiled, s) : launch_gate_up_bf16(a, row_tiles, rowcap, tiled, s);
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s) {
-  GroupedArgs b = a;
   const int rowcap = grouped_step_rows(a.M);
-  b.passes = grouped_passes(a.M);
-  return fp8 ? launch_down_fp8(b, row_tiles, rowcap, tiled, s) : launch_down_bf16(b, row_tiles, rowcap, tiled, s);
+  return fp8 ? launch_down_fp8(a, row_tiles, rowcap, tiled, s) : launch_down_bf16(a, row_tiles, rowcap, tiled, s);
 }
 
 size_t tiled_weight_bytes(bool fp8, int64_t E, int N, int K) {

@@ -7,10 +7,10 @@
 //            slot of active expert e (t = slot / top_k); the shared expert does
 //            the same for every token t into sh_act[t, c].
 //   down:    out[p, c] = sum_k Wd[e][c][k] act[p][k] (shared: rows are tokens).
-// A workgroup owns one active expert (or one group of shared-expert rows) and a
-// 64-column tile of the output, and applies each weight row it streams from HBM
-// to every row routed to that expert, so each expert's weights are read once
-// per pass.  Rows of the intermediates are sorted positions.
+// A workgroup owns one pass (up to 16 rows) of one active expert, or one group
+// of shared-expert rows, and one or two 64-column tiles of the output, and
+// applies each weight row it streams from HBM to every row of its pass.  Rows
+// of the intermediates are sorted positions.
 //
 // gfx950 design (not the pages' CUDA geometry):
 //  * Matrix cores: v_mfma_f32_16x16x32_bf16.  The weights are the A operand
@@ -33,8 +33,12 @@
 //    element is the same sequence of MFMA k-steps, scale FMAs and chunk sums
 //    whatever tile, slot, pass or staging mode the row goes through, and the
 //    rows per pass come from the shape class, never from the routing.
-//  * Graph replay: the grid is (ceil(N/64), cap + shared row groups), sized from
-//    shapes only; a workgroup past the device-side active count exits at once.
+//  * Work items: one workgroup runs one pass (rowcap rows) of one expert over a
+//    group of 64-column tiles.  The grid is (shared row groups + the most passes
+//    any routing of n slots can need, column groups), sized from shapes only; a
+//    routed workgroup finds its expert and pass from the active list and counts
+//    (a block scan of the experts' pass counts), and one past the routing's
+//    passes exits after that.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -79,19 +83,60 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r16 = lane & 15;
-  const int by = blockIdx.y;
+  // ---- grid: x = work item (the shared expert's row groups first, then the
+  // routed items), y = group of ctw 64-column tiles.  Routed item j is the j-th
+  // 16-row pass over the active experts taken in ascending order, each expert
+  // contributing ceil(count / rowcap) passes; the grid covers the most passes
+  // any routing of n slots can need, so it depends on shapes only.  Consecutive
+  // items are consecutive workgroups, which the dispatcher deals round-robin to
+  // the XCDs, and a column group past N leaves before any load.
+  const int item = blockIdx.x;
+  const bool routed = item >= p.sgroups;
+  const int N = routed ? p.N : p.sN, K = routed ? p.K : p.sK;
+  const int t_begin = blockIdx.y * ctw;
+  const int t_end = min(t_begin + ctw, (N + kTileCols - 1) / kTileCols);
+  if (t_begin >= t_end) return;
 
-  // ---- which expert / rows this workgroup serves: workgroup row by < cap *
-  // passes is pass group pg = by / cap of active expert a = by % cap, which runs
-  // the expert's row passes pg, pg + passes, ...; the rows after those are
-  // shared-expert row groups
-  const bool routed = by < p.cap * p.passes;
-  const int a_idx = routed ? by % p.cap : 0, pg = routed ? by / p.cap : 0;
-  int e = 0, rows = 0, row_base = 0, N, K;
+  int e = 0, rows = 0, row_base = 0, first_r0 = 0;
   const int* fsrc = nullptr;  // fused: sources of all of the expert's rows
   if (routed) {
-    N = p.N;
-    K = p.K;
+    // which expert and pass item j is: every thread takes a run of active
+    // indices, a block scan of their pass counts places the runs, and the
+    // thread whose run holds pass j publishes (expert, pass, count, offset)
+    __shared__ int s_item[4 + 2 * kWaves];
+    const int j = item - p.sgroups;
+    constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
+    const int per = (p.cap + kThreads - 1) / kThreads;
+    const int a0 = min(p.cap, tid * per);
+    auto find_item = [&](auto expert_of, auto count_of, auto offset_of) {
+      int ex[kPer], cn[kPer], np = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) ex[i] = (i < per && a0 + i < p.cap) ? expert_of(a0 + i) : -1;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        cn[i] = ex[i] >= 0 ? count_of(ex[i]) : 0;
+        np += (cn[i] + rowcap - 1) / rowcap;
+      }
+      if (tid == 0) s_item[0] = -1;
+      int base, unused_ex, unused_tot, total;
+      align_dev::block_scan2<kWaves>(np, 0, s_item + 4, s_item + 4 + kWaves, base, unused_ex, total, unused_tot);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int npi = (cn[i] + rowcap - 1) / rowcap;
+        if (j >= base && j < base + npi) {
+          s_item[0] = ex[i];
+          s_item[1] = j - base;
+          s_item[2] = cn[i];
+          s_item[3] = offset_of(ex[i]);
+        }
+        base += npi;
+      }
+      __syncthreads();
+      e = s_item[0];
+      first_r0 = s_item[1] * rowcap;
+      rows = s_item[2];
+      row_base = s_item[3];
+    };
     if constexpr (FUSED) {
       int* a = reinterpret_cast<int*>(reinterpret_cast<char*>(xs) + xs_bytes);
       const int E = p.E;
@@ -104,30 +149,25 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       align_dev::count_pass<kWaves>(ids, p.n, E, nbits, s.cnt);
       align_dev::expert_scan<kWaves>(s, E, p.BS);
       const int nact = s.scal[0];
-      if (a_idx < nact) {
-        e = s.active[a_idx];
-        rows = s.count[e];
-        row_base = s.off[e];
-        align_dev::expert_rows<kWaves>(ids, p.n, E, nbits, s.cnt, e, p.top_k, src_all);
-      }
-      if (blockIdx.x == 0 && by == 0) {  // the tables the later steps read
+      find_item([&](int ai) { return ai < nact ? s.active[ai] : -1; }, [&](int ex) { return s.count[ex]; },
+                [&](int ex) { return s.off[ex]; });
+      if (e >= 0) align_dev::expert_rows<kWaves>(ids, p.n, E, nbits, s.cnt, e, p.top_k, src_all);
+      if (item == p.sgroups && blockIdx.y == 0) {  // the tables the later steps read
         __syncthreads();  // expert_rows is done with the bases scatter_pass advances
         align_dev::scatter_pass<kWaves>(ids, p.n, E, nbits, s.cnt, s.off, p.tables.sorted_token_ids,
                                         p.tables.token_to_perm);
         align_dev::write_rest<kWaves>(s, p.n, E, p.BS, p.max_total, p.cap, p.tables);
       }
-      if (a_idx >= nact || pg * rowcap >= rows) return;
       fsrc = src_all;
     } else {
-      const int nact = *p.active_count;  // both loads in flight together
-      const int e0 = p.active_experts[a_idx];
-      if (a_idx >= nact) return;
-      e = e0;
-      if (p.passes > 1 && pg * rowcap >= p.expert_counts[e]) return;  // no pass for this group
+      // active_experts holds -1 past the active count
+      find_item([&](int ai) { return p.active_experts[ai]; }, [&](int ex) { return p.expert_counts[ex]; },
+                [&](int ex) { return p.expert_offsets[ex]; });
     }
+    if (e < 0) return;  // no such pass for this routing
   } else {
-    N = p.sN;
-    K = p.sK;
+    row_base = item * rowcap;
+    rows = min(rowcap, p.M - row_base);
   }
 
   const char *W0, *W1 = nullptr;
@@ -153,10 +193,6 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     X = static_cast<const char*>(p.sx);
     OUT = p.sout;
   }
-  // this workgroup's 64-column tiles: [t_begin, t_end)
-  const int t_begin = blockIdx.x * ctw;
-  const int t_end = min(t_begin + ctw, (N + kTileCols - 1) / kTileCols);
-  if (t_begin >= t_end) return;
   const int nch = (K + kKC - 1) / kKC;
   const int nv = (t_end - t_begin) * nch;  // (tile, chunk) steps of one pass
   const int kpad = TILED ? round_up(K, kKC) : K;
@@ -222,14 +258,6 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j]);
 
-  if (routed && !FUSED) {
-    rows = p.expert_counts[e];
-    row_base = p.expert_offsets[e];
-  } else if (!routed) {
-    row_base = (by - p.cap * p.passes) * rowcap;
-    rows = min(rowcap, p.M - row_base);
-  }
-
   // the FP8 scales of a tile's 16 columns of this wave, one 128-deep block per lane
   float sreg[NS][SL];
   auto load_scales = [&](int t) {
@@ -280,18 +308,10 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     }
   };
 
-  const int first_r0 = routed ? pg * rowcap : 0;
-  for (int r0 = first_r0; r0 < rows; r0 += (routed ? p.passes : 1) * rowcap) {
+  {  // this workgroup's one pass: rows [first_r0, first_r0 + rowcap) of the expert
+    const int r0 = first_r0;
     const int nr = min(rowcap, rows - r0);
     const int nrt = (nr + 15) >> 4;
-
-    if (r0 > first_r0) {  // a later pass streams the weights again from the start
-      lt = t_begin;
-      lc = 0;
-      set_load_tile(lt);
-#pragma unroll
-      for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j]);
-    }
     load_scales(t_begin);
 
     // the source rows of this pass: fused from the LDS row list, else from the
@@ -506,7 +526,6 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
         }
       }
     }
-    __syncthreads();  // the next pass may restage LDS
   }
 }
 
@@ -524,7 +543,7 @@ inline int device_cus() {
 }
 
 template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
-hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, int rows_y, hipStream_t s) {
+hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   auto kern = grouped_kernel<FP8, GATE_UP, RT, RESIDENT, TILED, FUSED, IdT>;
   const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
   static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
@@ -535,7 +554,7 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
     configured = lds;
   }
   // column tiles per workgroup: the fewest that let every workgroup of the
-  // worst case (all `rows_y` experts active) be resident at once, but at most
+  // worst case (every item busy) be resident at once, but at most
   // kMaxTilesPerGroup, so a wide grid (many experts, large M) keeps its
   // parallelism instead of serialising the columns inside few workgroups
   static size_t occ_lds = (size_t)-1;  // occupancy of this kernel at the last LDS size asked
@@ -549,22 +568,21 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
     occ_lds = lds;
   }
   const int slots = std::max(1, occ_per_cu) * device_cus();
+  const int items = a.sgroups + a.items;
   int ctw = 1;
-  while (ctw < tiles && ctw < kMaxTilesPerGroup && (long long)rows_y * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
-  const dim3 grid((tiles + ctw - 1) / ctw, rows_y);
+  while (ctw < tiles && ctw < kMaxTilesPerGroup && (long long)items * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
+  const dim3 grid(items, (tiles + ctw - 1) / ctw);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, rowcap, ctw, xs_bytes);
   return hipGetLastError();
 }
 
 template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED>
-hipError_t launch_fused_or_not(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, int rows_y,
-                               hipStream_t s) {
+hipError_t launch_fused_or_not(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   if (GATE_UP && a.ids != nullptr) {
-    if (a.ids64)
-      return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, rows_y, s);
-    return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, rows_y, s);
+    if (a.ids64) return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
+    return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
   }
-  return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, rows_y, s);
+  return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
 }
 
 template <bool FP8, bool GATE_UP, int RT, bool TILED>
@@ -574,17 +592,21 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   const size_t resident = (size_t)NX * rowcap * (kmax + kPad) * 2;
   const size_t chunked = (size_t)2 * NX * rowcap * (kKC + kPad) * 2;
   const int nmax = (a.sw0 != nullptr && a.sN > a.N) ? a.sN : a.N;
-  const int shared_groups = a.sw0 != nullptr ? (a.M + rowcap - 1) / rowcap : 0;
   const int tiles = (nmax + kTileCols - 1) / kTileCols;
-  const int rows_y = a.cap * a.passes + shared_groups;
+  GroupedArgs b = a;
+  b.sgroups = a.sw0 != nullptr ? (a.M + rowcap - 1) / rowcap : 0;
+  // the most rowcap-row passes n slots can need: sum over experts of
+  // ceil(count / rowcap) <= (n + active * (rowcap - 1)) / rowcap
+  const int64_t n = (int64_t)a.M * a.top_k;
+  b.items = (int)((n + (int64_t)a.cap * (rowcap - 1)) / rowcap);
   if (resident <= kResidentLdsBudget)
-    return launch_fused_or_not<FP8, GATE_UP, RT, true, TILED>(a, rowcap, resident, tiles, rows_y, s);
-  return launch_fused_or_not<FP8, GATE_UP, RT, false, TILED>(a, rowcap, chunked, tiles, rows_y, s);
+    return launch_fused_or_not<FP8, GATE_UP, RT, true, TILED>(b, rowcap, resident, tiles, s);
+  return launch_fused_or_not<FP8, GATE_UP, RT, false, TILED>(b, rowcap, chunked, tiles, s);
 }
 
 template <bool FP8, bool GATE_UP, bool TILED>
 hipError_t launch_layout(const GroupedArgs& a, int rt, int rowcap, hipStream_t s) {
-  (void)rt;  // one 16-row tile per pass: the row passes of an expert are spread over workgroups
+  (void)rt;  // one 16-row tile per pass: each pass of an expert is a workgroup of its own
   return launch_rt<FP8, GATE_UP, 1, TILED>(a, rowcap, s);
 }
 

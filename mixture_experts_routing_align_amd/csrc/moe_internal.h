@@ -54,7 +54,8 @@ struct GroupedArgs {
   const int32_t* active_experts;
   const int32_t* active_count;
   int M, top_k, cap;
-  int passes;  // row-pass groups per expert (workgroup rows per active expert), >= 1
+  int items;    // routed work items (rowcap-row passes of active experts) the grid covers; set at launch
+  int sgroups;  // shared-expert row groups, ahead of the routed items; set at launch
   // fused alignment (gate+up only; ids != nullptr): every routed workgroup
   // aligns topk_ids in LDS itself, and workgroup (0, 0) writes `tables`
   const void* ids;
@@ -74,8 +75,9 @@ int grouped_rows_per_pass(int64_t M);
 // Row tiles (16 rows each) one workgroup keeps in registers per pass.
 int grouped_row_tiles(int64_t M, int top_k);
 
-// The separate grouped kernels: rows per pass (at most 16) and the number of
-// workgroup rows per active expert that share an expert's row passes.
+// The separate grouped kernels: rows per pass (at most 16), and the passes an
+// expert holding M rows needs (1: every expert fits one pass when ids are
+// distinct within a token).
 int grouped_step_rows(int64_t M);
 int grouped_passes(int64_t M);
 
