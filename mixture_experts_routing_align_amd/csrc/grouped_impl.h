@@ -83,17 +83,29 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r16 = lane & 15;
-  // ---- grid: x = work item (the shared expert's row groups first, then the
-  // routed items), y = group of ctw 64-column tiles.  Routed item j is the j-th
-  // 16-row pass over the active experts taken in ascending order, each expert
-  // contributing ceil(count / rowcap) passes; the grid covers the most passes
-  // any routing of n slots can need, so it depends on shapes only.  Consecutive
-  // items are consecutive workgroups, which the dispatcher deals round-robin to
-  // the XCDs, and a column group past N leaves before any load.
-  const int item = blockIdx.x;
-  const bool routed = item >= p.sgroups;
+  // ---- work item and column group of this workgroup.  The one-dimensional
+  // grid holds first the shared expert's (row group, column group) pairs, so
+  // its longer rows start first, then the routed (item, column group) pairs
+  // with the item fastest: consecutive workgroups, which the dispatcher deals
+  // round-robin to the XCDs, carry different items of one column group.
+  // Routed item j is the j-th rowcap-row pass over the active experts taken in
+  // ascending order, each expert contributing ceil(count / rowcap) passes; the
+  // grid covers the most passes any routing of n slots can need, so it depends
+  // on shapes only.
+  const int ngs = (((p.sN + kTileCols - 1) / kTileCols) + ctw - 1) / ctw;  // shared column groups
+  const int nshared = p.sgroups * ngs;
+  const bool routed = (int)blockIdx.x >= nshared;
+  int item, tgrp;
+  if (routed) {
+    const int r = (int)blockIdx.x - nshared;
+    item = p.sgroups + r % p.items;
+    tgrp = r / p.items;
+  } else {
+    item = (int)blockIdx.x / ngs;
+    tgrp = (int)blockIdx.x % ngs;
+  }
   const int N = routed ? p.N : p.sN, K = routed ? p.K : p.sK;
-  const int t_begin = blockIdx.y * ctw;
+  const int t_begin = tgrp * ctw;
   const int t_end = min(t_begin + ctw, (N + kTileCols - 1) / kTileCols);
   if (t_begin >= t_end) return;
 
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       find_item([&](int ai) { return ai < nact ? s.active[ai] : -1; }, [&](int ex) { return s.count[ex]; },
                 [&](int ex) { return s.off[ex]; });
       if (e >= 0) align_dev::expert_rows<kWaves>(ids, p.n, E, nbits, s.cnt, e, p.top_k, src_all);
-      if (item == p.sgroups && blockIdx.y == 0) {  // the tables the later steps read
+      if (item == p.sgroups && tgrp == 0) {  // the tables the later steps read
         __syncthreads();  // expert_rows is done with the bases scatter_pass advances
         align_dev::scatter_pass<kWaves>(ids, p.n, E, nbits, s.cnt, s.off, p.tables.sorted_token_ids,
                                         p.tables.token_to_perm);
@@ -568,10 +580,15 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
     occ_lds = lds;
   }
   const int slots = std::max(1, occ_per_cu) * device_cus();
+  // (the shared and routed items may have different column counts: `tiles` is the larger)
   const int items = a.sgroups + a.items;
   int ctw = 1;
   while (ctw < tiles && ctw < kMaxTilesPerGroup && (long long)items * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
-  const dim3 grid(items, (tiles + ctw - 1) / ctw);
+  const long long groups_r = ((a.N + kTileCols - 1) / kTileCols + ctw - 1) / ctw;
+  const long long groups_s = a.sgroups ? ((a.sN + kTileCols - 1) / kTileCols + ctw - 1) / ctw : 0;
+  const long long blocks = a.sgroups * groups_s + a.items * groups_r;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;  // more workgroups than one launch takes
+  const dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, rowcap, ctw, xs_bytes);
   return hipGetLastError();
 }
