@@ -16,6 +16,8 @@ Sources (the web pages this path is defined by):
   ``silu(g) * u`` in fp32 and the fixed-order top-k reduction;
 * metrale ``forward_nvfp4_grouped_decode.rs`` source page - the layer's step
   order (route, sort, gate+up+SiLU, down, blend) and row independence;
+* metrale ``forward_nvfp4_grouped_decode.rs`` source page - the per-row router
+  (BF16 softmax gate, router GEMV and per-row top-k softmax) that feeds the path;
 * metrale ``fp8_moe_grouped.rs`` source page - the sort's outputs (sorted slot
   ids, expert offsets, ``token_to_perm``, ascending active experts and their
   count), the active-expert cap, the 1024-expert limit, the 128-wide FP8 scale
@@ -36,3 +38,4 @@ from .ffn import (  # noqa: F401
     silu,
 )
 from .numerics import bf16_to_f64, e4m3_table, e4m3_value  # noqa: F401
+from .router import router_logits, topk_softmax  # noqa: F401
