@@ -335,6 +335,22 @@ def main():
     ev1.synchronize()
     align_ev_us = ev0.elapsed_time(ev1) * 1e3 / areps
 
+    # the router (the step before the path) on the decode shape, graph-replayed
+    log("router latency (decode shape)")
+    rx = xt
+    rw = torch.from_numpy(workloads.router_weight_bf16(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+    r_ids = torch.empty(cfg.M, cfg.top_k, dtype=torch.int64, device=dev)
+    r_w = torch.empty(cfg.M, cfg.top_k, dtype=torch.float32, device=dev)
+    r_logits = torch.empty(cfg.M, cfg.E, dtype=torch.float32, device=dev)
+
+    def route():
+        moe._check(moe.lib().moe_router_topk(rx.data_ptr(), rw.data_ptr(), cfg.M, cfg.H, cfg.E, cfg.top_k,
+                                             r_logits.data_ptr(), r_ids.data_ptr(), moe.MOE_IDX_I64,
+                                             r_w.data_ptr(), stream.cuda_stream))
+
+    rg = graph_of(lambda: [route() for _ in range(AR)], stream)
+    router_us = per_call_us(rg)
+
     # plain streaming-read ceiling in the same run: one launch of the library's
     # read-only kernel over as many bytes as one layer streams (G disjoint
     # buffers in rotation, like the weight copies), best of a few grid sizes;
@@ -424,6 +440,9 @@ def main():
         "align_us_events": align_ev_us,
         "align_workload": "n = 4096 x 8 int64 ids, Zipf(1.1), 256 experts, BS 64 (20 aligns per graph, HIP events)",
         "launch_floor_us": floor_us,
+        "router_us": router_us,
+        "router_workload": "M=8 tokens, H=2048, E=128 bf16 gate, top-8 (logits GEMV + top-k softmax, 2 launches; "
+                           "20 per graph, HIP events)",
         "stream_ceiling": stream_ceiling,
     }
     if args.other_configs:

@@ -294,6 +294,31 @@ int moe_layer_blend_partials(const moe_layer_desc* d, const void* topk_ids, cons
  * error for an invalid descriptor. */
 int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[MOE_LAYER_WORKSPACE_REGIONS + 1]);
 
+/* ---------------------------------------------------------------- router --
+ * The step before the path: the per-row router that turns token activations
+ * into the topk_ids / topk_weights every call above takes (metrale
+ * forward_nvfp4_grouped_decode.rs, the decode layer's admission predicate: a
+ * BF16 softmax gate with no correction bias, computed by a router GEMV over the
+ * batch rows and a per-row top-k softmax).
+ *
+ *   logits[t][e] = sum_h W[e][h] * x[t][h]      x bf16 [M, H], W bf16 [E, H],
+ *                                               float32 accumulation
+ *   topk_ids[t]  = the top_k largest logits of row t, larger first; equal
+ *                  logits go to the lower expert
+ *   topk_weights[t][j] = softmax over the chosen logits (the full softmax over
+ *                  E, renormalised over its top k: the two are equal)
+ *
+ * Writes logits (float32 [M, E], caller-owned device memory; also the hand-off
+ * between the two launches), topk_ids ([M, top_k], int32 or int64 per idt) and
+ * topk_weights (float32 [M, top_k]).  Requires H a multiple of 8 (>= 8),
+ * 1 <= E <= MOE_MAX_EXPERTS, 1 <= top_k <= min(E, MOE_ROUTER_MAX_TOP_K),
+ * M < 2^20; finite logits (a NaN logit leaves the choice unspecified).  Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_LIMIT (E or M too large), MOE_ERR_HIP.
+ * M == 0 launches nothing. */
+#define MOE_ROUTER_MAX_TOP_K 64
+int moe_router_topk(const void* x_bf16, const void* router_w_bf16, int64_t M, int32_t H, int32_t E, int32_t top_k,
+                    float* logits, void* topk_ids, moe_index_dtype idt, float* topk_weights, hipStream_t stream);
+
 /* Measurement aid, not part of the layer: one launch that reads `bytes` of
  * device memory at `src` with 16-byte vector loads and does nothing else,
  * giving the plain HBM read rate for a buffer of that size against which the

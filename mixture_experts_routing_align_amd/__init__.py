@@ -42,6 +42,7 @@ from ._ffi import (  # noqa: F401
     MOE_LAYER_WORKSPACE_REGIONS,
     MOE_MAX_EXPERTS,
     MOE_OK,
+    MOE_ROUTER_MAX_TOP_K,
     MOE_W_BF16,
     MOE_W_BF16_TILED,
     MOE_W_FP8_E4M3,
@@ -398,6 +399,29 @@ def moe_layer_blend_partials(layer: MoeLayer, topk_ids, topk_weights, out, works
     _check(lib().moe_layer_blend_partials(ctypes.byref(d), topk_ids.data_ptr(), topk_weights.data_ptr(),
                                           out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out
+
+
+def moe_router_topk(x, router_w, top_k: int, ids_dtype=torch.int64, logits=None, stream=None):
+    """Per-row router: float32 logits of bf16 x [M, H] against the bf16 gate
+    weight [E, H], each row's top_k experts (larger logit first, ties to the
+    lower expert) and their softmax weights over the chosen logits.  Returns
+    (topk_ids [M, top_k] of ids_dtype, topk_weights float32 [M, top_k],
+    logits float32 [M, E])."""
+    M, H = x.shape
+    E = router_w.shape[0]
+    if router_w.shape[1] != H or x.dtype != torch.bfloat16 or router_w.dtype != torch.bfloat16:
+        raise ValueError("x [M, H] and router_w [E, H] must both be bfloat16 with the same H")
+    if not (x.is_contiguous() and router_w.is_contiguous()):
+        raise ValueError("x and router_w must be contiguous")
+    dev = x.device
+    if logits is None:
+        logits = torch.empty(M, E, dtype=torch.float32, device=dev)
+    ids = torch.empty(M, top_k, dtype=ids_dtype, device=dev)
+    wts = torch.empty(M, top_k, dtype=torch.float32, device=dev)
+    idt = MOE_IDX_I64 if ids_dtype == torch.int64 else MOE_IDX_I32
+    _check(lib().moe_router_topk(x.data_ptr(), router_w.data_ptr(), M, H, E, top_k, logits.data_ptr(), ids.data_ptr(),
+                                 idt, wts.data_ptr(), _stream(stream)))
+    return ids, wts, logits
 
 
 def moe_stream_read_probe(src, sink, blocks: int = 2048, stream=None):

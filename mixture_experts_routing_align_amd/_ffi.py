@@ -22,6 +22,7 @@ MOE_W_FP8_E4M3 = 1
 MOE_W_BF16_TILED = 2
 MOE_W_FP8_E4M3_TILED = 3
 MOE_MAX_EXPERTS = 1024
+MOE_ROUTER_MAX_TOP_K = 64
 MOE_FUSED_ALIGN_MAX_SLOTS = 2048
 MOE_FUSED_LAYER_MAX_SLOTS = 256
 MOE_LAYER_PATH_STEPS = 0
@@ -85,6 +86,8 @@ SIGNATURES = {
                                          c_void_p]),
     "moe_tiled_weight_bytes": (c_size_t, [c_int, c_int64, c_int32, c_int32]),
     "moe_stream_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]),
+    "moe_router_topk": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int,
+                                c_void_p, c_void_p]),
     "moe_tile_weights": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int32, c_void_p]),
 }
 

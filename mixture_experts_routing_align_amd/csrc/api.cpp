@@ -199,7 +199,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -555,6 +555,27 @@ int moe_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t
   if (!src || !sink) return fail(MOE_ERR_NULL, "%s: src or sink is NULL", fn);
   if (reinterpret_cast<uintptr_t>(src) % 16) return fail(MOE_ERR_SHAPE, "%s: src is not 16-byte aligned", fn);
   return hip_status(moe::launch_stream_read(src, bytes, sink, blocks, stream), fn);
+}
+
+int moe_router_topk(const void* x_bf16, const void* router_w_bf16, int64_t M, int32_t H, int32_t E, int32_t top_k,
+                    float* logits, void* topk_ids, moe_index_dtype idt, float* topk_weights, hipStream_t stream) {
+  const char* fn = "moe_router_topk";
+  if (M < 0) return fail(MOE_ERR_SHAPE, "%s: M=%lld is negative", fn, (long long)M);
+  if (M >= ((int64_t)1 << 20)) return fail(MOE_ERR_LIMIT, "%s: M=%lld reaches 2^20 rows", fn, (long long)M);
+  if (H < 8 || H % 8) return fail(MOE_ERR_SHAPE, "%s: H=%d must be a positive multiple of 8", fn, H);
+  if (E < 1) return fail(MOE_ERR_SHAPE, "%s: E=%d must be >= 1", fn, E);
+  if (E > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_LIMIT, "%s: E=%d exceeds the %d experts the router handles", fn, E, MOE_MAX_EXPERTS);
+  if (top_k < 1 || top_k > E || top_k > MOE_ROUTER_MAX_TOP_K)
+    return fail(MOE_ERR_SHAPE, "%s: top_k=%d must be in [1, min(E, %d)]", fn, top_k, MOE_ROUTER_MAX_TOP_K);
+  if (idt != MOE_IDX_I32 && idt != MOE_IDX_I64)
+    return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)idt);
+  if (M == 0) return MOE_OK;
+  if (!x_bf16 || !router_w_bf16 || !logits || !topk_ids || !topk_weights)
+    return fail(MOE_ERR_NULL, "%s: x, router weight, logits, topk_ids or topk_weights is NULL", fn);
+  return hip_status(moe::launch_router(x_bf16, router_w_bf16, (int)M, H, E, top_k, logits, topk_ids,
+                                       idt == MOE_IDX_I64, topk_weights, stream),
+                    fn);
 }
 
 }  // extern "C"

@@ -117,6 +117,8 @@ bool fused_layer_fits(bool fp8, int64_t M, int H, int I, int S, int E, int top_k
 // the first launch (align, gate+up+SiLU, down partials) and the second (sum + blend)
 hipError_t launch_layer_partials(const FusedLayerArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
+hipError_t launch_router(const void* x, const void* w, int M, int H, int E, int top_k, float* logits, void* ids,
+                         bool ids64, float* wts, hipStream_t s);
 hipError_t launch_blend_partials(const FusedLayerArgs& a, hipStream_t s);
 
 hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -233,3 +233,27 @@ def test_stream_read_probe_refusals(lib):
     assert lib.moe_stream_read_probe(FAKE, 32, None, 8, None) == _ffi.MOE_ERR_NULL
     assert lib.moe_stream_read_probe(FAKE + 8, 32, FAKE, 8, None) == _ffi.MOE_ERR_SHAPE
     assert lib.moe_stream_read_probe(None, 0, None, 8, None) == _ffi.MOE_OK
+
+
+def test_router_refusals(lib):
+    r = lib.moe_router_topk
+    ok = dict(x=FAKE, w=FAKE, M=4, H=64, E=16, k=2, lg=FAKE, ids=FAKE, idt=1, wts=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return r(a["x"], a["w"], a["M"], a["H"], a["E"], a["k"], a["lg"], a["ids"], a["idt"], a["wts"], None)
+
+    assert call(H=60) == _ffi.MOE_ERR_SHAPE
+    assert "multiple of 8" in _err(lib)
+    assert call(H=0) == _ffi.MOE_ERR_SHAPE
+    assert call(E=0) == _ffi.MOE_ERR_SHAPE
+    assert call(E=1025) == _ffi.MOE_ERR_LIMIT
+    assert call(k=0) == _ffi.MOE_ERR_SHAPE
+    assert call(k=17) == _ffi.MOE_ERR_SHAPE
+    assert call(E=128, k=65) == _ffi.MOE_ERR_SHAPE
+    assert call(M=-1) == _ffi.MOE_ERR_SHAPE
+    assert call(M=1 << 20) == _ffi.MOE_ERR_LIMIT
+    assert call(idt=7) == _ffi.MOE_ERR_SHAPE
+    for name in ("x", "w", "lg", "ids", "wts"):
+        assert call(**{name: None}) == _ffi.MOE_ERR_NULL, name
+    assert call(M=0, x=None, w=None, lg=None, ids=None, wts=None) == _ffi.MOE_OK

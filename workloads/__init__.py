@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     expert_matrix,
     fill_expert_weights,
+    router_weight_bf16,
     routing,
     shared_matrix,
     weight_shape,

@@ -39,6 +39,7 @@ _TAG_ZIPF_PERM = 4
 _TAG_ZIPF_DRAW = 5
 _TAG_ROUTED = {"gate": 10, "up": 11, "down": 12}
 _TAG_SHARED = {"gate": 20, "up": 21, "down": 22}
+_TAG_ROUTER = 30
 
 
 @dataclass(frozen=True)
@@ -124,6 +125,13 @@ def routing(cfg: MoeConfig) -> Tuple[np.ndarray, np.ndarray]:
     w = np.take_along_axis(p, ids, axis=1)
     w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
     return ids, w
+
+
+def router_weight_bf16(cfg: MoeConfig) -> np.ndarray:
+    """Router gate weight [E, H] as bf16 bits, N(0, 1/H): with N(0, 1)
+    activations the logits come out near N(0, 1), like the routing recipe's."""
+    z = _rng(cfg, _TAG_ROUTER).normal(0.0, 1.0 / np.sqrt(cfg.H), size=(cfg.E, cfg.H)).astype(np.float32)
+    return bf16_bits_from_f32(z)
 
 
 def weight_shape(cfg: MoeConfig, which: str, shared: bool = False) -> Tuple[int, int]:
