@@ -35,6 +35,7 @@ from .ffn import (  # noqa: F401
     dequant,
     expert_ffn,
     moe_layer,
+    shared_gate,
     silu,
 )
 from .numerics import bf16_to_f64, e4m3_table, e4m3_value  # noqa: F401

@@ -69,14 +69,29 @@ def expert_ffn(x_rows: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarra
     return act, act @ Wd.T
 
 
+def shared_gate(x_bits: np.ndarray, gate_bits: np.ndarray) -> np.ndarray:
+    """Gate of the shared expert per token: sigmoid(x[t] . g), float64.
+
+    The FP8 page's blend takes the layer input and the shared expert's gate
+    weight (a hidden-sized vector) beside the shared output, and runs ungated
+    when no gate weight is given; it does not print the formula.  Reading: the
+    shared output is scaled by the logistic sigmoid of the input's dot product
+    with the gate weight."""
+    x = bf16_to_f64(x_bits)
+    g = bf16_to_f64(np.asarray(gate_bits).reshape(-1))
+    return 1.0 / (1.0 + np.exp(-(x @ g)))
+
+
 def blend(expert_out, topk_weights: np.ndarray, token_to_perm: np.ndarray,
           sh_out: Optional[np.ndarray], tokens: Optional[Iterable[int]] = None,
-          H: Optional[int] = None) -> np.ndarray:
-    """out[t] = sum_k w[t, k] * expert_out[token_to_perm[t*top_k + k]] (+ sh_out[t]).
+          H: Optional[int] = None, sh_gate: Optional[np.ndarray] = None) -> np.ndarray:
+    """out[t] = sum_k w[t, k] * expert_out[token_to_perm[t*top_k + k]]
+    (+ sh_out[t], times sh_gate[t] when a gate is given).
 
     ``expert_out`` is indexed by sorted position (an array or a dict of rows);
-    a slot with ``token_to_perm == -1`` contributes nothing.  Returns float64
-    rows for ``tokens`` (all tokens by default)."""
+    a slot with ``token_to_perm == -1`` contributes nothing; ``sh_gate`` holds
+    one float64 gate per token (all M tokens).  Returns float64 rows for
+    ``tokens`` (all tokens by default)."""
     w = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
     M, top_k = w.shape
     tokens = list(range(M)) if tokens is None else list(tokens)
@@ -96,7 +111,7 @@ def blend(expert_out, topk_weights: np.ndarray, token_to_perm: np.ndarray,
                 continue
             acc = acc + w[t, k] * np.asarray(expert_out[pos], dtype=np.float64)
         if sh_out is not None:
-            acc = acc + sh_out[t]
+            acc = acc + (sh_out[t] if sh_gate is None else sh_gate[t] * sh_out[t])
         out[r] = acc
     return out
 
@@ -104,12 +119,13 @@ def blend(expert_out, topk_weights: np.ndarray, token_to_perm: np.ndarray,
 def moe_layer(x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray,
               E: int, BS: int, wdt: str,
               routed_weight: Callable, shared_weight: Optional[Callable] = None,
-              tokens: Optional[Iterable[int]] = None) -> dict:
+              tokens: Optional[Iterable[int]] = None, sh_gate_bits: Optional[np.ndarray] = None) -> dict:
     """The whole layer for ``tokens`` (default: all).
 
     ``routed_weight(which, e)`` and ``shared_weight(which)`` return the raw
     ``(bits, scales)`` of matrix ``which`` in {"gate", "up", "down"};
-    ``shared_weight`` is None when there is no shared expert.
+    ``shared_weight`` is None when there is no shared expert;
+    ``sh_gate_bits`` (bf16 [H]) gates it, ``shared_gate``.
 
     Expert by expert (each expert's weights are dequantised once): the rows
     routed to it are the slots with its id, in ascending flat index, and a
@@ -158,6 +174,7 @@ def moe_layer(x_bits: np.ndarray, topk_ids: np.ndarray, topk_weights: np.ndarray
     if sh_out is not None:
         sh_full = np.zeros((M, H), dtype=np.float64)
         sh_full[tokens] = sh_out
-    out = blend(y_pos, topk_weights, perm, sh_full, tokens=tokens, H=H)
+    gate = None if (sh_gate_bits is None or sh_out is None) else shared_gate(x_bits, sh_gate_bits)
+    out = blend(y_pos, topk_weights, perm, sh_full, tokens=tokens, H=H, sh_gate=gate)
     return {"out": out, "act_pos": act_pos, "y_pos": y_pos, "sh_act": sh_act,
             "sh_out": sh_out, "tables": tables, "tokens": tokens}

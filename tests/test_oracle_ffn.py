@@ -255,3 +255,38 @@ def test_token_subset_matches_full():
     full = oracle.moe_layer(x_bits, ids, w, E, 4, "bf16", routed, shared)["out"]
     part = oracle.moe_layer(x_bits, ids, w, E, 4, "bf16", routed, shared, tokens=[4, 1])["out"]
     assert np.allclose(part, full[[4, 1]], rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------------------- gated shared expert --
+
+def test_shared_gate_special_values_and_symmetry():
+    rng = np.random.default_rng(21)
+    M, H = 6, 64
+    x = bf16_bits_from_f32(rng.normal(size=(M, H)).astype(np.float32))
+    zero = bf16_bits_from_f32(np.zeros(H, dtype=np.float32))
+    assert np.array_equal(oracle.shared_gate(x, zero), np.full(M, 0.5))
+    g = bf16_bits_from_f32(rng.normal(0, 0.2, size=H).astype(np.float32))
+    neg = bf16_bits_from_f32(-oracle.bf16_to_f64(g).astype(np.float32))
+    assert np.allclose(oracle.shared_gate(x, g) + oracle.shared_gate(x, neg), 1.0, rtol=0, atol=1e-15)
+    big = bf16_bits_from_f32(np.full(H, 64.0, dtype=np.float32))
+    ones = bf16_bits_from_f32(np.ones((1, H), dtype=np.float32))
+    assert oracle.shared_gate(ones, big)[0] == 1.0
+    assert oracle.shared_gate(ones, bf16_bits_from_f32(np.full(H, -64.0, dtype=np.float32)))[0] < 1e-300
+    ref = torch.sigmoid(torch.from_numpy(oracle.bf16_to_f64(x)) @ torch.from_numpy(oracle.bf16_to_f64(g)))
+    assert np.allclose(oracle.shared_gate(x, g), ref.numpy(), rtol=1e-14, atol=0)
+
+
+def test_blend_gate_scales_only_the_shared_term():
+    rng = np.random.default_rng(22)
+    M, top_k, E, H = 7, 3, 5, 16
+    ids = np.stack([rng.choice(E, size=top_k, replace=False) for _ in range(M)]).astype(np.int64)
+    w = rng.uniform(0.1, 1, size=(M, top_k)).astype(np.float32)
+    t = oracle.align(ids, E, 4)
+    eo = rng.normal(size=(int(t["total"]), H))
+    sh = rng.normal(size=(M, H))
+    gate = rng.uniform(0, 1, size=M)
+    plain = oracle.blend(eo, w, t["token_to_perm"], None, H=H)
+    gated = oracle.blend(eo, w, t["token_to_perm"], sh, H=H, sh_gate=gate)
+    assert np.allclose(gated, plain + gate[:, None] * sh, rtol=1e-14, atol=1e-14)
+    assert np.array_equal(oracle.blend(eo, w, t["token_to_perm"], sh, H=H, sh_gate=np.ones(M)),
+                          oracle.blend(eo, w, t["token_to_perm"], sh, H=H))
