@@ -204,14 +204,18 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
                      int32_t S, int32_t E, int32_t top_k, int32_t BS, hipStream_t stream);
 
 /* out[t, :] = bf16( (sum over k = 0..top_k-1 in that order of
- * w[t*top_k+k] * expert_out[token_to_perm[t*top_k+k], :]) + sh_out[t, :] ),
+ * w[t*top_k+k] * expert_out[token_to_perm[t*top_k+k], :]) + g_t * sh_out[t, :] ),
  * float32 fused multiply-adds, a slot with token_to_perm < 0 skipped, sh_out
- * NULL for no shared expert; one round-to-nearest-even at the end.  A row's
- * bits depend only on that token's inputs (not on M).  H must be a multiple
- * of 4. */
+ * NULL for no shared expert; one round-to-nearest-even at the end.  The
+ * shared term is added as is when sh_expert_gate is NULL; else it is scaled
+ * by g_t = sigmoid(x[t] . sh_expert_gate) (bf16 x [M, H] and bf16 gate vector
+ * [H], a float32 dot product in a fixed order; fp8_moe_grouped.rs: the blend
+ * takes the layer input and the shared expert's gate weight, ungated when the
+ * weight is absent).  A row's bits depend only on that token's inputs (not on
+ * M).  H must be a multiple of 4; x must be given with a gate. */
 int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights,
-              const int32_t* token_to_perm, const float* sh_out, int64_t M, int32_t H,
-              int32_t top_k, hipStream_t stream);
+              const int32_t* token_to_perm, const float* sh_out, const void* x_bf16,
+              const void* sh_expert_gate, int64_t M, int32_t H, int32_t top_k, hipStream_t stream);
 
 /* ------------------------------------------------------------ whole layer -- */
 
@@ -227,6 +231,9 @@ typedef struct {
   moe_index_dtype idt;
   moe_weight gate, up, down;            /* routed experts                  */
   moe_weight sh_gate, sh_up, sh_down;   /* shared expert (.w NULL if none) */
+  const void* sh_expert_gate;           /* bf16 [H] gate vector of the shared
+                                           expert's output (moe_blend), or NULL:
+                                           ungated; only with S > 0      */
 } moe_layer_desc;
 
 /* The two ways moe_layer_forward runs, chosen from the descriptor's shapes
@@ -281,13 +288,15 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
  * moe_layer_partials followed by moe_layer_blend_partials on the same
  * workspace.  moe_layer_partials aligns topk_ids (writing the tables into the
  * workspace) and writes the float32 partial outputs part / sh_part;
- * moe_layer_blend_partials reads them with topk_ids and topk_weights and
+ * moe_layer_blend_partials reads them with topk_ids and topk_weights (and x,
+ * for the shared gate when d->sh_expert_gate is set; else x may be NULL) and
  * writes out (bf16 [M, H]).  Both return MOE_ERR_SHAPE when `d` does not take
  * MOE_LAYER_PATH_SINGLE_PASS; other errors as for moe_layer_forward. */
 int moe_layer_partials(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
-int moe_layer_blend_partials(const moe_layer_desc* d, const void* topk_ids, const float* topk_weights,
-                             void* out_bf16, const void* workspace, size_t workspace_bytes, hipStream_t stream);
+int moe_layer_blend_partials(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids,
+                             const float* topk_weights, void* out_bf16, const void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /* Byte offsets of the MOE_LAYER_WORKSPACE_REGIONS regions, in the order above;
  * offsets[MOE_LAYER_WORKSPACE_REGIONS] is the total size.  Returns MOE_OK or an

@@ -265,15 +265,17 @@ def moe_grouped_down(act: torch.Tensor, down: Weight, tables: AlignTables, exper
 
 
 def moe_blend(out: torch.Tensor, expert_out: torch.Tensor, topk_weights: torch.Tensor, token_to_perm: torch.Tensor,
-              sh_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """out[t] = bf16(sum_k w[t,k] expert_out[token_to_perm[t*top_k+k]] + sh_out[t])."""
+              sh_out: Optional[torch.Tensor] = None, stream=None, x: Optional[torch.Tensor] = None,
+              sh_expert_gate: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = bf16(sum_k w[t,k] expert_out[token_to_perm[t*top_k+k]] + g_t sh_out[t]),
+    g_t = sigmoid(x[t] . sh_expert_gate) when a gate vector is given, else 1."""
     M, top_k = topk_weights.shape
     H = out.shape[1]
     _need(out.dtype == torch.bfloat16 and out.shape[0] == M, "out must be bf16 [M, H]")
     _need(topk_weights.dtype == torch.float32 and topk_weights.is_contiguous(), "topk_weights must be float32")
     _need(token_to_perm.dtype == torch.int32, "token_to_perm must be int32")
     _check(lib().moe_blend(out.data_ptr(), expert_out.data_ptr(), topk_weights.data_ptr(), token_to_perm.data_ptr(),
-                           _ptr(sh_out), M, H, top_k, _stream(stream)))
+                           _ptr(sh_out), _ptr(x), _ptr(sh_expert_gate), M, H, top_k, _stream(stream)))
     return out
 
 
@@ -285,9 +287,12 @@ WORKSPACE_REGIONS = TABLE_FIELDS + ("act", "expert_out", "sh_act", "sh_out", "pa
 class MoeLayer:
     """Expert weights of one MoE layer plus the fused ``moe_layer_forward`` call."""
 
-    def __init__(self, gate, up, down, top_k: int, BS: int, sh_gate=None, sh_up=None, sh_down=None):
+    def __init__(self, gate, up, down, top_k: int, BS: int, sh_gate=None, sh_up=None, sh_down=None,
+                 sh_expert_gate: Optional[torch.Tensor] = None):
         self.gate, self.up, self.down = gate, up, down
         self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
+        # bf16 [H] gate vector of the shared expert's output (None: ungated)
+        self.sh_expert_gate = sh_expert_gate
         self.top_k, self.BS = top_k, BS
         self.E, self.I, self.H = weight_shape(gate)
         self.S = 0 if sh_gate is None else weight_shape(sh_gate)[1]
@@ -302,13 +307,18 @@ class MoeLayer:
             return None if w is None or isinstance(w, TiledWeight) else moe_tile_weights(w, stream)
 
         return MoeLayer(t(self.gate), t(self.up), t(self.down), self.top_k, self.BS,
-                        t(self.sh_gate), t(self.sh_up), t(self.sh_down))
+                        t(self.sh_gate), t(self.sh_up), t(self.sh_down), self.sh_expert_gate)
 
     def desc(self, M: int, idt: int = MOE_IDX_I64) -> MoeLayerDesc:
         none = MoeWeight(None, None)
         d = MoeLayerDesc(M, self.H, self.I, self.S, self.E, self.top_k, self.BS, self.wdt, idt,
                          _weight(self.gate), _weight(self.up), _weight(self.down),
                          _weight(self.sh_gate) or none, _weight(self.sh_up) or none, _weight(self.sh_down) or none)
+        if self.sh_expert_gate is not None:
+            g = self.sh_expert_gate
+            _need(g.dtype == torch.bfloat16 and g.numel() == self.H and g.is_contiguous(),
+                  "sh_expert_gate must be a contiguous bf16 vector of H elements")
+            d.sh_expert_gate = g.data_ptr()
         return d
 
     def workspace_bytes(self, M: int, idt: int = MOE_IDX_I64) -> int:
@@ -391,13 +401,15 @@ def moe_layer_partials(layer: MoeLayer, x, topk_ids, workspace, stream=None) -> 
                                     workspace.numel(), _stream(stream)))
 
 
-def moe_layer_blend_partials(layer: MoeLayer, topk_ids, topk_weights, out, workspace, stream=None):
-    """Second launch of the single-pass layer: sum the partials, blend into `out`."""
+def moe_layer_blend_partials(layer: MoeLayer, topk_ids, topk_weights, out, workspace, stream=None, x=None):
+    """Second launch of the single-pass layer: sum the partials, blend into `out`
+    (x is needed when the layer has a shared gate vector)."""
     M = topk_ids.shape[0]
     idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
     d = layer.desc(M, idt)
-    _check(lib().moe_layer_blend_partials(ctypes.byref(d), topk_ids.data_ptr(), topk_weights.data_ptr(),
-                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    _check(lib().moe_layer_blend_partials(ctypes.byref(d), None if x is None else x.data_ptr(), topk_ids.data_ptr(),
+                                          topk_weights.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream(stream)))
     return out
 
 

@@ -53,6 +53,7 @@ class MoeLayerDesc(ctypes.Structure):
         ("top_k", c_int32), ("BS", c_int32), ("wdt", c_int), ("idt", c_int),
         ("gate", MoeWeight), ("up", MoeWeight), ("down", MoeWeight),
         ("sh_gate", MoeWeight), ("sh_up", MoeWeight), ("sh_down", MoeWeight),
+        ("sh_expert_gate", c_void_p),
     ]
 
 
@@ -74,16 +75,16 @@ SIGNATURES = {
     "moe_grouped_down": (c_int, [c_void_p, c_int, P(MoeWeight), P(MoeAlignTables), c_void_p, P(MoeWeight),
                                  c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_int32, c_int32,
                                  c_int32, c_void_p]),
-    "moe_blend": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
-                          c_void_p]),
+    "moe_blend": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32,
+                          c_int32, c_void_p]),
     "moe_layer_workspace_bytes": (c_size_t, [P(MoeLayerDesc)]),
     "moe_layer_forward": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                   c_void_p]),
     "moe_layer_workspace_layout": (c_int, [P(MoeLayerDesc), P(c_size_t)]),
     "moe_layer_path": (c_int, [P(MoeLayerDesc)]),
     "moe_layer_partials": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-    "moe_layer_blend_partials": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
-                                         c_void_p]),
+    "moe_layer_blend_partials": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_size_t, c_void_p]),
     "moe_tiled_weight_bytes": (c_size_t, [c_int, c_int64, c_int32, c_int32]),
     "moe_stream_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]),
     "moe_router_topk": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int,

@@ -341,7 +341,8 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
 }
 
 int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights, const int32_t* token_to_perm,
-              const float* sh_out, int64_t M, int32_t H, int32_t top_k, hipStream_t stream) {
+              const float* sh_out, const void* x_bf16, const void* sh_expert_gate, int64_t M, int32_t H,
+              int32_t top_k, hipStream_t stream) {
   const char* fn = "moe_blend";
   if (M < 0 || H < 1 || top_k < 1) return fail(MOE_ERR_SHAPE, "%s: M=%lld H=%d top_k=%d", fn, (long long)M, H, top_k);
   if (H % 4) return fail(MOE_ERR_SHAPE, "%s: H=%d must be a multiple of 4", fn, H);
@@ -349,8 +350,9 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
   if (M == 0) return MOE_OK;
   if (!out_bf16 || !expert_out || !topk_weights || !token_to_perm)
     return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (sh_out && sh_expert_gate && !x_bf16) return fail(MOE_ERR_NULL, "%s: x is NULL with a shared gate", fn);
   return hip_status(moe::launch_blend(static_cast<uint16_t*>(out_bf16), expert_out, topk_weights, token_to_perm,
-                                      sh_out, (int)M, H, top_k, stream),
+                                      sh_out, x_bf16, sh_out ? sh_expert_gate : nullptr, (int)M, H, top_k, stream),
                     fn);
 }
 
@@ -418,6 +420,8 @@ int layer_setup(const char* fn, const moe_layer_desc* d, const void* workspace, 
                    (rc = check_weight(fn, "shared up", &d->sh_up, d->wdt)) ||
                    (rc = check_weight(fn, "shared down", &d->sh_down, d->wdt))))
     return rc;
+  if (d->sh_expert_gate != nullptr && d->S == 0)
+    return fail(MOE_ERR_SHAPE, "%s: a shared gate vector is given without a shared expert (S = 0)", fn);
   return MOE_OK;
 }
 
@@ -450,6 +454,7 @@ moe::FusedLayerArgs single_pass_args(const moe_layer_desc* d, char* ws, const si
     a.sw[i] = shared ? sw[i]->w : nullptr;
     a.ss[i] = shared ? sw[i]->scale : nullptr;
   }
+  a.sh_gate = shared ? d->sh_expert_gate : nullptr;
   a.topk_weights = topk_weights;
   a.out = static_cast<uint16_t*>(out_bf16);
   a.part = reinterpret_cast<float*>(ws + off[12]);
@@ -487,8 +492,9 @@ int moe_layer_partials(const moe_layer_desc* d, const void* x_bf16, const void* 
   return hip_status(moe::launch_layer_partials(a, is_fp8(d->wdt), stream), fn);
 }
 
-int moe_layer_blend_partials(const moe_layer_desc* d, const void* topk_ids, const float* topk_weights,
-                             void* out_bf16, const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int moe_layer_blend_partials(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids,
+                             const float* topk_weights, void* out_bf16, const void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
   const char* fn = "moe_layer_blend_partials";
   size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1];
   int path = 0;
@@ -498,7 +504,8 @@ int moe_layer_blend_partials(const moe_layer_desc* d, const void* topk_ids, cons
     return fail(MOE_ERR_SHAPE, "%s: this layer shape does not take the single-pass path", fn);
   if (!topk_ids || !topk_weights || !out_bf16)
     return fail(MOE_ERR_NULL, "%s: topk_ids, topk_weights or out is NULL", fn);
-  const moe::FusedLayerArgs a = single_pass_args(d, static_cast<char*>(const_cast<void*>(workspace)), off, nullptr,
+  if (d->sh_expert_gate && !x_bf16) return fail(MOE_ERR_NULL, "%s: x is NULL with a shared gate", fn);
+  const moe::FusedLayerArgs a = single_pass_args(d, static_cast<char*>(const_cast<void*>(workspace)), off, x_bf16,
                                                  topk_ids, topk_weights, out_bf16);
   return hip_status(moe::launch_blend_partials(a, stream), fn);
 }
@@ -544,7 +551,8 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   if ((rc = moe_grouped_down(act, d->wdt, &d->down, &t, expert_out, shared ? &d->sh_down : nullptr, sh_act, sh_out,
                              d->M, d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))
     return rc;
-  return moe_blend(out_bf16, expert_out, topk_weights, t.token_to_perm, sh_out, d->M, d->H, d->top_k, stream);
+  return moe_blend(out_bf16, expert_out, topk_weights, t.token_to_perm, sh_out, x_bf16,
+                   shared ? d->sh_expert_gate : nullptr, d->M, d->H, d->top_k, stream);
 }
 
 int moe_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, hipStream_t stream) {

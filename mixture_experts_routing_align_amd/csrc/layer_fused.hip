@@ -395,6 +395,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
 }
 
 // out[t] = bf16( sum_k fma(w[t,k], y_k, .) (k ascending, valid slots only) + shared ),
+// shared = the sum of the shared expert's slices, added (ungated) or through a
+// fused multiply-add with its gate sigmoid(x[t] . g) (the steps-path blend's
+// order and gate helper),
 // y_k = sum_j part[j][t*top_k+k] (j ascending from 0).  A workgroup covers 32
 // four-column groups of one token with 8 k-lanes each: k-lane kk sums the slices
 // of k = kk, kk + 8, ... (up to 16 slices' loads issued together, together with
@@ -407,9 +410,13 @@ constexpr int kBlendSlices = 16;   // slices loaded per batch
 template <typename IdT>
 __global__ __launch_bounds__(256) void blend_parts_kernel(uint16_t* __restrict__ out, const float* __restrict__ part,
                                                           int nsl, const float* __restrict__ sh_part, int nssl,
+                                                          const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ sh_gate,
                                                           const IdT* __restrict__ ids, const float* __restrict__ w,
                                                           int M, int H, int top_k, int E, int n) {
   __shared__ float4 ys[kBlendKMax][kBlendGroups];
+  __shared__ float red[256];  // the gate's dot product
+  const bool gated = nssl > 0 && sh_gate != nullptr;
   __shared__ float ws[kBlendKMax];  // the slots' weights
   __shared__ int wv[kBlendKMax];    // and whether their ids are in [0, E)
   const int g = threadIdx.x % kBlendGroups, kk = threadIdx.x / kBlendGroups;
@@ -417,6 +424,7 @@ __global__ __launch_bounds__(256) void blend_parts_kernel(uint16_t* __restrict__
   const bool col = h < H;
   const size_t slice_stride = (size_t)n * H;
   for (int t = blockIdx.y; t < M; t += gridDim.y) {
+    const float gate = gated ? mma::shared_gate256(x + (size_t)t * H, sh_gate, H, red) : 1.f;
     const size_t slot0 = (size_t)t * top_k;
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
     for (int kb = 0; kb < top_k; kb += kBlendKMax) {
@@ -473,10 +481,17 @@ __global__ __launch_bounds__(256) void blend_parts_kernel(uint16_t* __restrict__
           s2 = add_rn(s2, v.z);
           s3 = add_rn(s3, v.w);
         }
-        a0 += s0;
-        a1 += s1;
-        a2 += s2;
-        a3 += s3;
+        if (gated) {
+          a0 = fmaf(gate, s0, a0);
+          a1 = fmaf(gate, s1, a1);
+          a2 = fmaf(gate, s2, a2);
+          a3 = fmaf(gate, s3, a3);
+        } else {
+          a0 += s0;
+          a1 += s1;
+          a2 += s2;
+          a3 += s3;
+        }
       }
       uint2 packed;
       packed.x = bf16_rne_out(a0) | (bf16_rne_out(a1) << 16);
@@ -522,6 +537,7 @@ hipError_t launch_blend(const FusedLayerArgs& a, hipStream_t s) {
   const int nssl = a.sw[0] != nullptr ? (a.S + kSlice - 1) / kSlice : 0;
   const dim3 grid((a.H / 4 + kBlendGroups - 1) / kBlendGroups, a.M < 65535 ? a.M : 65535);
   hipLaunchKernelGGL(blend_parts_kernel<IdT>, grid, dim3(256), 0, s, a.out, a.part, nsl, a.sh_part, nssl,
+                     static_cast<const uint16_t*>(a.x), static_cast<const uint16_t*>(a.sh_gate),
                      static_cast<const IdT*>(a.ids), a.topk_weights, a.M, a.H, a.top_k, a.E, a.n);
   return hipGetLastError();
 }

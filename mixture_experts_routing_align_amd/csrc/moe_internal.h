@@ -100,10 +100,11 @@ struct FusedLayerArgs {
   const float* s[3];      // their FP8 scales (unused for bf16)
   const void* sw[3];      // shared expert (sw[0] == nullptr: none), tiled
   const float* ss[3];
+  const void* sh_gate;    // bf16 [H] gate vector of the shared expert, or nullptr (ungated)
   const float* topk_weights;
   uint16_t* out;          // bf16 [M, H]
-  float* part;            // [ceil(I/128)][n][H] routed partials by slot
-  float* sh_part;         // [ceil(S/128)][M][H] shared partials by token
+  float* part;            // [ceil(I/64)][n][H] routed partials by slot
+  float* sh_part;         // [ceil(S/64)][M][H] shared partials by token
   int M, H, I, S, E, top_k, BS, n, cap, max_total;
   AlignOut tables;
 };
@@ -122,6 +123,7 @@ hipError_t launch_router(const void* x, const void* w, int M, int H, int E, int 
 hipError_t launch_blend_partials(const FusedLayerArgs& a, hipStream_t s);
 
 hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,
-                        const float* sh_out, int M, int H, int top_k, hipStream_t s);
+                        const float* sh_out, const void* x, const void* sh_gate, int M, int H, int top_k,
+                        hipStream_t s);
 
 }  // namespace moe

@@ -45,12 +45,12 @@ class DeviceModel(DeviceWeights):
     def __init__(self, cfg: MoeConfig, device="cuda", keep_host: bool = True, threads: int = 8):
         super().__init__(cfg, device=device, keep_host=keep_host, threads=threads)
 
-    def layer(self):
+    def layer(self, sh_expert_gate=None):
         from mixture_experts_routing_align_amd import MoeLayer
 
         sh = self.sh or {}
         return MoeLayer(self.weight("gate"), self.weight("up"), self.weight("down"), self.cfg.top_k, self.cfg.BS,
-                        sh.get("gate"), sh.get("up"), sh.get("down"))
+                        sh.get("gate"), sh.get("up"), sh.get("down"), sh_expert_gate=sh_expert_gate)
 
     def tiled_layer(self):
         """The layer with tiled weights (built once per model)."""
@@ -69,10 +69,10 @@ class DeviceModel(DeviceWeights):
         return lambda which: self.sh_host[which]
 
 
-def oracle_layer(model: DeviceModel, x, ids, w, tokens=None):
+def oracle_layer(model: DeviceModel, x, ids, w, tokens=None, sh_gate_bits=None):
     cfg = model.cfg
     return oracle.moe_layer(x, ids, w, cfg.E, cfg.BS, cfg.wdt, model.routed_weight, model.shared_weight(),
-                            tokens=tokens)
+                            tokens=tokens, sh_gate_bits=sh_gate_bits)
 
 
 TABLE_KEYS = ("sorted_token_ids", "block_expert_ids", "expert_offsets", "expert_counts", "token_to_perm",

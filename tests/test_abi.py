@@ -113,9 +113,12 @@ def test_grouped_refusals(lib):
                                 4, 256, 100, 0, 8, 2, 16, None) == _ffi.MOE_ERR_SHAPE
     assert lib.moe_grouped_down(FAKE, 1, ctypes.byref(d), ctypes.byref(t), FAKE, None, None, None,
                                 4, 256, 128, 128, 8, 2, 16, None) == _ffi.MOE_ERR_NULL
-    assert lib.moe_blend(FAKE, FAKE, FAKE, FAKE, None, 4, 6, 2, None) == _ffi.MOE_ERR_SHAPE
-    assert lib.moe_blend(None, FAKE, FAKE, FAKE, None, 4, 8, 2, None) == _ffi.MOE_ERR_NULL
-    assert lib.moe_blend(None, None, None, None, None, 0, 8, 2, None) == _ffi.MOE_OK
+    assert lib.moe_blend(FAKE, FAKE, FAKE, FAKE, None, None, None, 4, 6, 2, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_blend(None, FAKE, FAKE, FAKE, None, None, None, 4, 8, 2, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_blend(None, None, None, None, None, None, None, 0, 8, 2, None) == _ffi.MOE_OK
+    # a shared gate needs x
+    assert lib.moe_blend(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 8, 2, None) == _ffi.MOE_ERR_NULL
+    assert "gate" in _err(lib)
 
 
 def _desc(M=8, H=2048, I=768, S=0, E=128, top_k=8, BS=16, wdt=1, idt=1):
@@ -210,7 +213,8 @@ def test_single_pass_stage_refusals(lib):
     need = lib.moe_layer_workspace_bytes(ctypes.byref(d))
     assert lib.moe_layer_partials(ctypes.byref(d), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
     assert "single-pass" in _err(lib)
-    assert lib.moe_layer_blend_partials(ctypes.byref(d), FAKE, FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_layer_blend_partials(ctypes.byref(d), None, FAKE, FAKE, FAKE, 0x100000, need,
+                                        None) == _ffi.MOE_ERR_SHAPE
     big = _tiled(_desc(M=128))                    # 1024 slots
     need = lib.moe_layer_workspace_bytes(ctypes.byref(big))
     assert lib.moe_layer_partials(ctypes.byref(big), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
@@ -218,7 +222,8 @@ def test_single_pass_stage_refusals(lib):
     need = lib.moe_layer_workspace_bytes(ctypes.byref(t))
     assert lib.moe_layer_partials(ctypes.byref(t), FAKE, FAKE, 0x100000, need - 1, None) == _ffi.MOE_ERR_WORKSPACE
     assert lib.moe_layer_partials(ctypes.byref(t), None, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_NULL
-    assert lib.moe_layer_blend_partials(ctypes.byref(t), FAKE, None, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_layer_blend_partials(ctypes.byref(t), None, FAKE, None, FAKE, 0x100000, need,
+                                        None) == _ffi.MOE_ERR_NULL
     t0 = _tiled(_desc(M=0))
     assert lib.moe_layer_partials(ctypes.byref(t0), None, None, None, 0, None) == _ffi.MOE_OK
 
@@ -257,3 +262,16 @@ def test_router_refusals(lib):
     for name in ("x", "w", "lg", "ids", "wts"):
         assert call(**{name: None}) == _ffi.MOE_ERR_NULL, name
     assert call(M=0, x=None, w=None, lg=None, ids=None, wts=None) == _ffi.MOE_OK
+
+
+def test_shared_gate_needs_a_shared_expert(lib):
+    d = _desc()                                   # S = 0
+    d.sh_expert_gate = FAKE
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(d))
+    assert lib.moe_layer_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
+    assert "shared gate" in _err(lib)
+    t = _tiled(_desc(M=4, H=256, E=8, top_k=2, I=128, S=128))   # single pass, gated: blend needs x
+    t.sh_expert_gate = FAKE
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(t))
+    assert lib.moe_layer_blend_partials(ctypes.byref(t), None, FAKE, FAKE, FAKE, 0x100000, need,
+                                        None) == _ffi.MOE_ERR_NULL

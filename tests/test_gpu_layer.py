@@ -467,3 +467,31 @@ def test_fused_layer_with_dropped_and_repeated_ids(moe):
     assert ok, (err, bound)
     sep, _ = _separate_steps(moe, model.layer(), xt, it, wt)
     assert torch.equal(out.view(torch.int16), sep.view(torch.int16))
+
+
+# ---------------------------------------------------- gated shared expert --
+
+@pytest.mark.parametrize("name", ["verify", "bf16_odd", "fp8_small"])
+def test_gated_shared_expert(moe, name):
+    """The shared expert's output scaled by sigmoid(x . g): parity with the
+    oracle on both layouts (row-major: steps path; tiled: the single pass where
+    the shape takes it), the two bit-identical, and different from ungated."""
+    cfg = workloads.CONFIGS[name] if name in workloads.CONFIGS else next(c for c in ODD if c.name == name)
+    model = model_for(name) if name in workloads.CONFIGS else DeviceModel(cfg, threads=4)
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    g_bits = workloads.shared_gate_bf16(cfg)
+    g = torch.from_numpy(g_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    log(f"gated shared expert: {name}")
+    row = model.layer(sh_expert_gate=g)
+    tiled = row.tiled()
+    a = row.forward(xt, it, wt)
+    b = tiled.forward(xt, it, wt)
+    ungated = model.layer().forward(xt, it, wt)
+    torch.cuda.synchronize()
+    ref = oracle_layer(model, x, ids, w, sh_gate_bits=g_bits)
+    ok, err, bound = tolerance_ok(bf16_to_np(a), ref["out"])
+    assert ok, (err, bound)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), ungated.view(torch.int16))
+    if name == "bf16_odd":
+        assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS

@@ -18,6 +18,7 @@ from .gen import (  # noqa: F401
     fill_expert_weights,
     router_weight_bf16,
     routing,
+    shared_gate_bf16,
     shared_matrix,
     weight_shape,
     x_bf16,

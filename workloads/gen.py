@@ -40,6 +40,7 @@ _TAG_ZIPF_DRAW = 5
 _TAG_ROUTED = {"gate": 10, "up": 11, "down": 12}
 _TAG_SHARED = {"gate": 20, "up": 21, "down": 22}
 _TAG_ROUTER = 30
+_TAG_SHARED_GATE = 31
 
 
 @dataclass(frozen=True)
@@ -131,6 +132,13 @@ def router_weight_bf16(cfg: MoeConfig) -> np.ndarray:
     """Router gate weight [E, H] as bf16 bits, N(0, 1/H): with N(0, 1)
     activations the logits come out near N(0, 1), like the routing recipe's."""
     z = _rng(cfg, _TAG_ROUTER).normal(0.0, 1.0 / np.sqrt(cfg.H), size=(cfg.E, cfg.H)).astype(np.float32)
+    return bf16_bits_from_f32(z)
+
+
+def shared_gate_bf16(cfg: MoeConfig) -> np.ndarray:
+    """Gate vector of the shared expert's output [H] as bf16 bits, N(0, 1/H):
+    with N(0, 1) activations its dot products come out near N(0, 1)."""
+    z = _rng(cfg, _TAG_SHARED_GATE).normal(0.0, 1.0 / np.sqrt(cfg.H), size=cfg.H).astype(np.float32)
     return bf16_bits_from_f32(z)
 
 
