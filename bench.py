@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-reps", type=int, default=25)
     ap.add_argument("--other-configs", default="",
-                    help="comma-separated workloads (tiny, verify, large) also timed whole-layer and reported "
+                    help="comma-separated workloads (tiny, verify, large, or decode_mN: the decode layer at "
+                         "N tokens) also timed whole-layer and reported "
                          "under other_configs (context for the headline, not the headline)")
     ap.add_argument("--only-config", default="",
                     help="time one other workload (tiny, verify or large) alone and print its line; for profiling")
@@ -134,7 +135,10 @@ def measure_config(name, dev, steps=50):
     import workloads
     from workloads.device import DeviceWeights
 
-    cfg = workloads.CONFIGS[name]
+    if name.startswith("decode_m"):  # the decode layer at a narrower width: decode_m1, decode_m2, ...
+        cfg = workloads.CONFIGS["decode"].replace(M=int(name[len("decode_m"):]), name=name)
+    else:
+        cfg = workloads.CONFIGS[name]
     G = 2 if cfg.E * cfg.I * cfg.H > (1 << 31) else 4  # the large workload: 2 copies of its 11 GB
     log(f"other config {name}: generating weights, {G} copies")
     w0 = DeviceWeights(cfg, device=dev, threads=16)

@@ -41,9 +41,10 @@ namespace layer_detail {
 
 using namespace mma;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kSlice = kWaves * kWaveCols;  // 64: intermediate columns per workgroup = down depth per workgroup
+constexpr int kColTiles = 4;                // 16-column tiles of the intermediate per workgroup
+constexpr int kSlice = kColTiles * kWaveCols;  // 64: intermediate columns per workgroup = down depth per workgroup
+constexpr int kNarrowSlots = 8;             // slot counts up to this take the 8-wave (split gate / up) kernel
+constexpr int kNarrowMinH = 1024;           // ... when H is at least this (small layers are faster on 4 waves)
 static_assert(2 * kSlice == kKC, "a slice is half of one 128-deep chunk (one FP8 scale block)");
 constexpr int kDownTiles = 4;               // 16-row tiles of H per down step
 constexpr int kMaxScaleBlocks = 128;        // FP8 depth limit of H: 128 scale blocks
@@ -51,15 +52,27 @@ constexpr size_t kLdsBudget = 96 * 1024;
 constexpr int kMaxRowCap = 64;              // rows per pass (4 row tiles) this kernel keeps in registers
 constexpr int kXFirst = 4;                  // x pieces per thread requested before the first weights
 
-__host__ __device__ constexpr size_t align_lds_bytes(int E, int n) {
-  return ((size_t)kWaves * E + E + (E + 1) + E + 2 * kWaves + 2 + n) * sizeof(int);
+__host__ __device__ constexpr size_t align_lds_bytes(int E, int n, int waves) {
+  return ((size_t)waves * E + E + (E + 1) + E + 2 * waves + 2 + n) * sizeof(int);
 }
 __host__ __device__ constexpr size_t x_lds_bytes(int rowcap, int H) { return (size_t)rowcap * (H + kPad) * 2; }
-__host__ __device__ constexpr size_t act_lds_bytes(int rowcap) { return (size_t)2 * rowcap * (kSlice + kPad) * 2; }
+// act as bf16 hi + lo, plus (8-wave kernel) the up sums handed to the gate waves
+__host__ __device__ constexpr size_t act_lds_bytes(int rowcap, bool split) {
+  return (size_t)2 * rowcap * (kSlice + kPad) * 2 + (split ? (size_t)rowcap * kSlice * 4 : 0);
+}
 
-template <bool FP8, int RT, typename IdT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void layer_kernel(
+// W = 4: wave w streams gate and up tile w of the slice.  W = 8 (narrow
+// widths, few workgroups): waves 0-3 stream the gate tiles and 4-7 the up
+// tiles, two 128-deep chunks per step, and the up sums reach the gate waves
+// through LDS; each wave then streams half the bytes, which helps when the
+// whole layer is only a few hundred workgroups.  Same arithmetic either way.
+template <bool FP8, int RT, typename IdT, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void layer_kernel(
     FusedLayerArgs p, int rowcap, size_t xs_bytes, size_t act_bytes) {
+  constexpr int kWaves = W;
+  constexpr int kThreads = W * 64;
+  constexpr bool SPLIT = W == 2 * kColTiles;
+  static_assert(W == kColTiles || SPLIT, "4 waves (gate + up per wave) or 8 (gate and up on separate waves)");
   constexpr int WL = FP8 ? 2 : 4;             // 16-byte loads per lane per 16x128 fragment
   constexpr int HL = WL / 2;                  // per 64-deep half fragment
   constexpr int NL = 2 * WL;                  // loads per lane per step (both phases)
@@ -117,7 +130,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
 
   // ---- weight streams
   const int kpH = round_up(H, kKC), kpI = round_up(NI, kKC);
-  const int nchH = kpH / kKC;                           // gate+up steps
+  const int nchH = kpH / kKC;                           // 128-deep chunks of H
   const size_t tile_g = (size_t)kpH * kWaveCols * ESZ;  // bytes of one 16-row tile of Wg / Wu
   const size_t tile_d = (size_t)kpI * kWaveCols * ESZ;  // of Wd
   const char *G, *U, *D;
@@ -145,10 +158,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
   }
   // gate+up: this wave's 16 intermediate columns (a wave past NI loads the
   // slice's first tile, multiplies nothing and leaves its act columns unused)
-  const int tg = slice * kWaves + wave;
+  const int st = SPLIT ? wave / kColTiles : 0;  // split: stream of this wave (0 gate, 1 up)
+  const int ct = SPLIT ? wave % kColTiles : wave;
+  const int tg = slice * kColTiles + ct;
   const bool gon = tg * kWaveCols < NI;
-  const char* gbase = G + (size_t)(gon ? tg : slice * kWaves) * tile_g + lane * 16;
-  const char* ubase = U + (size_t)(gon ? tg : slice * kWaves) * tile_g + lane * 16;
+  const char* gbase = (SPLIT && st ? U : G) + (size_t)(gon ? tg : slice * kColTiles) * tile_g + lane * 16;
+  const char* ubase = U + (size_t)(gon ? tg : slice * kColTiles) * tile_g + lane * 16;
+  const int ngs = SPLIT ? (nchH + 1) / 2 : nchH;  // gate/up steps (split: two chunks of one stream each)
   // down: this wave's run of 16-row tiles of H, kDownTiles per step (tiles past
   // H load the last tile again and store nothing); the slice is half `hf` of
   // chunk slice / 2 of each tile
@@ -156,22 +172,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
   const int per = round_up((ntd + kWaves - 1) / kWaves, kDownTiles);
   const int dfirst = wave * per;
   const int nd = per / kDownTiles;
-  const int nv = nchH + nd;
+  const int nv = ngs + nd;
   const int hf = slice & 1;
   const char* dbase = D + (size_t)(slice >> 1) * FB + hf * HL * 1024 + lane * 16;
 
   auto load_step = [&](int v, uint4 (&wr)[NL]) {
     v = min(v, nv - 1);
-    if (v < nchH) {
-      const char* a0 = gbase + (size_t)v * FB;
-      const char* a1 = ubase + (size_t)v * FB;
+    if (v < ngs) {
+      const char* a0 = gbase + (size_t)(SPLIT ? 2 * v : v) * FB;
+      const char* a1 = SPLIT ? gbase + (size_t)min(2 * v + 1, nchH - 1) * FB : ubase + (size_t)v * FB;
 #pragma unroll
       for (int j = 0; j < WL; ++j) {
         wr[j] = *reinterpret_cast<const uint4*>(a0 + j * 1024);
         wr[WL + j] = *reinterpret_cast<const uint4*>(a1 + j * 1024);
       }
     } else {
-      const int T0 = dfirst + kDownTiles * (v - nchH);
+      const int T0 = dfirst + kDownTiles * (v - ngs);
 #pragma unroll
       for (int u = 0; u < kDownTiles; ++u) {
         const char* a = dbase + (size_t)min(T0 + u, ntd - 1) * tile_d;
@@ -190,8 +206,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
       const int c = lane + 64 * i;
-      sg[i] = c < kbH ? SG[(size_t)(slice >> 1) * kbH + c] : 0.f;
-      su[i] = c < kbH ? SU[(size_t)(slice >> 1) * kbH + c] : 0.f;
+      sg[i] = c < kbH ? (SPLIT && st ? SU : SG)[(size_t)(slice >> 1) * kbH + c] : 0.f;
+      su[i] = c < kbH && !SPLIT ? SU[(size_t)(slice >> 1) * kbH + c] : 0.f;
     }
     if (lane < nd) sd = SD[(size_t)(min(dfirst + kDownTiles * lane, ntd - 1) / 8) * kbI + (slice >> 1)];
   }
@@ -263,37 +279,76 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
       return as_bf16x8(wc[u * HL + s]);
     };
 
-    // gate+up chunk c of this wave's 16 columns (each accumulator sees the MFMA
-    // sequence of the separate gate+up kernel)
-    auto gate_up = [&](const uint4 (&wc)[NL], int c) {
-      const float scg = FP8 ? lane_scale(sg, c) : 1.f;
-      const float scu = FP8 ? lane_scale(su, c) : 1.f;
-      const uint16_t* xb = xs + c * kKC;
+    // gate+up step v: chunk v of this wave's 16 gate and 16 up columns, or
+    // (split) chunks 2v and 2v + 1 of its one stream; each accumulator sees the
+    // MFMA sequence of the separate gate+up kernel
+    auto gate_up = [&](const uint4 (&wc)[NL], int v) {
+      if constexpr (SPLIT) {
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        if (rt < nrt) {
-          const int rowc = min(rt * 16 + r16, rowcap - 1);
-          if (FP8) {
-            f32x4 tg4 = {0.f, 0.f, 0.f, 0.f}, tu4 = {0.f, 0.f, 0.f, 0.f};
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int c = 2 * v + c2;
+          if (c < nchH) {
+            const float scg = FP8 ? lane_scale(sg, c) : 1.f;
+            const uint16_t* xb = xs + c * kKC;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
-              tg4 = mfma(gu_op(wc, 0, s), b, tg4);
-              tu4 = mfma(gu_op(wc, 1, s), b, tu4);
+            for (int rt = 0; rt < RT; ++rt) {
+              if (rt < nrt) {
+                const int rowc = min(rt * 16 + r16, rowcap - 1);
+                if (FP8) {
+                  f32x4 t4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                  for (int s = 0; s < 4; ++s) {
+                    const bf16x8 b =
+                        as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
+                    t4 = mfma(gu_op(wc, c2, s), b, t4);
+                  }
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) ag[rt][i] = fmaf(scg, t4[i], ag[rt][i]);
+                } else {
+#pragma unroll
+                  for (int s = 0; s < 4; ++s) {
+                    if (c * kKC + s * 32 < H) {
+                      const bf16x8 b =
+                          as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
+                      ag[rt] = mfma(gu_op(wc, c2, s), b, ag[rt]);
+                    }
+                  }
+                }
+              }
             }
+          }
+        }
+      } else {
+        const int c = v;
+        const float scg = FP8 ? lane_scale(sg, c) : 1.f;
+        const float scu = FP8 ? lane_scale(su, c) : 1.f;
+        const uint16_t* xb = xs + c * kKC;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ag[rt][i] = fmaf(scg, tg4[i], ag[rt][i]);
-              au[rt][i] = fmaf(scu, tu4[i], au[rt][i]);
-            }
-          } else {
+        for (int rt = 0; rt < RT; ++rt) {
+          if (rt < nrt) {
+            const int rowc = min(rt * 16 + r16, rowcap - 1);
+            if (FP8) {
+              f32x4 tg4 = {0.f, 0.f, 0.f, 0.f}, tu4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              if (c * kKC + s * 32 < H) {
-                const bf16x8 b =
-                    as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
-                ag[rt] = mfma(gu_op(wc, 0, s), b, ag[rt]);
-                au[rt] = mfma(gu_op(wc, 1, s), b, au[rt]);
+              for (int s = 0; s < 4; ++s) {
+                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
+                tg4 = mfma(gu_op(wc, 0, s), b, tg4);
+                tu4 = mfma(gu_op(wc, 1, s), b, tu4);
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                ag[rt][i] = fmaf(scg, tg4[i], ag[rt][i]);
+                au[rt][i] = fmaf(scu, tu4[i], au[rt][i]);
+              }
+            } else {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                if (c * kKC + s * 32 < H) {
+                  const bf16x8 b =
+                      as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
+                  ag[rt] = mfma(gu_op(wc, 0, s), b, ag[rt]);
+                  au[rt] = mfma(gu_op(wc, 1, s), b, au[rt]);
+                }
               }
             }
           }
@@ -301,16 +356,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
       }
     };
 
-    // act = silu(g) * u of this wave's columns into LDS as bf16 hi + lo
+    // act = silu(g) * u of this wave's columns into LDS as bf16 hi + lo (split:
+    // the up waves hand their sums over through LDS and the gate waves write
+    // act; every wave calls it then, for its barrier)
+    float* ub = reinterpret_cast<float*>(as + 2 * aplane);  // split: [rowcap][kSlice] up sums
     auto act_to_lds = [&]() {
+      if constexpr (SPLIT) {
+        if (st == 1 && gon) {
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const int r = rt * 16 + r16;
+            if (rt < nrt && r < rowcap)
+              *reinterpret_cast<f32x4*>(ub + r * kSlice + ct * kWaveCols + 4 * q) = ag[rt];
+          }
+        }
+        __syncthreads();  // the up sums are in LDS
+        if (st == 1 || !gon) return;
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int r = rt * 16 + r16;
         if (rt < nrt && r < rowcap) {
+          f32x4 u = au[rt];
+          if constexpr (SPLIT) u = *reinterpret_cast<const f32x4*>(ub + r * kSlice + ct * kWaveCols + 4 * q);
           uint16_t hi[4], lo[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float f = silu_mul(ag[rt][i], au[rt][i]);
+            const float f = silu_mul(ag[rt][i], u[i]);
             hi[i] = bf16_rne_bits(f);
             lo[i] = bf16_rne_bits(f - bf16_bits_to_f32(hi[i]));
           }
@@ -319,7 +391,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
           h2.y = hi[2] | ((uint32_t)hi[3] << 16);
           l2.x = lo[0] | ((uint32_t)lo[1] << 16);
           l2.y = lo[2] | ((uint32_t)lo[3] << 16);
-          uint16_t* d = as + r * astride + wave * kWaveCols + 4 * q;
+          uint16_t* d = as + r * astride + ct * kWaveCols + 4 * q;
           *reinterpret_cast<uint2*>(d) = h2;
           *reinterpret_cast<uint2*>(d + aplane) = l2;
         }
@@ -371,14 +443,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RT == 
     };
 
     auto step = [&](const uint4 (&wc)[NL], int v) {
-      if (v < nchH) {
+      if (v < ngs) {
         if (gon) gate_up(wc, v);
-        if (v == nchH - 1) {
-          if (gon) act_to_lds();
+        if (v == ngs - 1) {
+          if (SPLIT || gon) act_to_lds();
           __syncthreads();  // every wave's act columns are in LDS
         }
       } else {
-        down(wc, v - nchH);
+        down(wc, v - ngs);
       }
     };
 
@@ -501,11 +573,16 @@ __global__ __launch_bounds__(256) void blend_parts_kernel(uint16_t* __restrict__
   }
 }
 
-template <bool FP8, int RT, typename IdT>
+// waves per workgroup: 8 (gate and up on separate waves) for narrow widths of
+// wide layers (measured: M = 1 at top-8 over 2048 x 768 experts 6% faster; M = 2
+// even; the 256-wide layer of 8 experts 9% slower)
+inline int layer_waves(int n, int H) { return n <= kNarrowSlots && H >= kNarrowMinH ? 2 * kColTiles : kColTiles; }
+
+template <bool FP8, int RT, typename IdT, int W>
 hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
-  auto kern = layer_kernel<FP8, RT, IdT>;
-  const size_t xs = x_lds_bytes(rowcap, a.H), ab = act_lds_bytes(rowcap);
-  const size_t lds = xs + ab + align_lds_bytes(a.E, a.n);
+  auto kern = layer_kernel<FP8, RT, IdT, W>;
+  const size_t xs = x_lds_bytes(rowcap, a.H), ab = act_lds_bytes(rowcap, W == 2 * kColTiles);
+  const size_t lds = xs + ab + align_lds_bytes(a.E, a.n, W);
   static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
   if (lds > 64 * 1024 && lds > configured) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -517,17 +594,18 @@ hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
   const int nssl = a.sw[0] != nullptr ? (a.S + kSlice - 1) / kSlice : 0;
   const int groups = a.sw[0] != nullptr ? (a.M + rowcap - 1) / rowcap : 0;
   const dim3 grid(std::max(nsl, nssl), a.cap + groups);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, rowcap, xs, ab);
+  hipLaunchKernelGGL(kern, grid, dim3(W * 64), lds, s, a, rowcap, xs, ab);
   return hipGetLastError();
 }
 
 template <bool FP8, typename IdT>
 hipError_t launch_rt(const FusedLayerArgs& a, hipStream_t s) {
   const int rowcap = grouped_rows_per_pass(a.M);
+  if (layer_waves(a.n, a.H) == 2 * kColTiles) return launch_kernel<FP8, 1, IdT, 2 * kColTiles>(a, rowcap, s);
   switch (rowcap <= 16 ? 1 : rowcap / 16) {
-    case 1: return launch_kernel<FP8, 1, IdT>(a, rowcap, s);
-    case 2: return launch_kernel<FP8, 2, IdT>(a, rowcap, s);
-    default: return launch_kernel<FP8, 4, IdT>(a, rowcap, s);
+    case 1: return launch_kernel<FP8, 1, IdT, kColTiles>(a, rowcap, s);
+    case 2: return launch_kernel<FP8, 2, IdT, kColTiles>(a, rowcap, s);
+    default: return launch_kernel<FP8, 4, IdT, kColTiles>(a, rowcap, s);
   }
 }
 
@@ -553,7 +631,9 @@ bool fused_layer_fits(bool fp8, int64_t M, int H, int I, int S, int E, int top_k
   (void)S;
   const int rowcap = grouped_rows_per_pass(M);
   if (rowcap > kMaxRowCap) return false;
-  const size_t lds = x_lds_bytes(rowcap, H) + act_lds_bytes(rowcap) + align_lds_bytes(E, (int)n);
+  const int waves = layer_waves((int)n, H);
+  const size_t lds = x_lds_bytes(rowcap, H) + act_lds_bytes(rowcap, waves == 2 * kColTiles) +
+                     align_lds_bytes(E, (int)n, waves);
   return lds <= kLdsBudget;
 }
 

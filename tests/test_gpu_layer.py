@@ -181,6 +181,8 @@ ODD = [
     # 128-deep chunk and a shared expert
     workloads.MoeConfig("bf16_wide", 150, 96, 4, 2, 160, 96, 4, "bf16", "softmax_bias", bias_std=4.0, seed=10),
     workloads.MoeConfig("fp8_wide", 130, 256, 8, 2, 256, 128, 8, "fp8", "softmax_bias", bias_std=2.0, seed=11),
+    # one token over a 1024-wide layer: the single pass's 8-wave kernel, bf16, with a shared expert
+    workloads.MoeConfig("bf16_narrow", 1, 1024, 16, 4, 192, 128, 8, "bf16", "softmax", seed=12),
 ]
 
 
@@ -471,7 +473,7 @@ def test_fused_layer_with_dropped_and_repeated_ids(moe):
 
 # ---------------------------------------------------- gated shared expert --
 
-@pytest.mark.parametrize("name", ["verify", "bf16_odd", "fp8_small"])
+@pytest.mark.parametrize("name", ["verify", "bf16_odd", "fp8_small", "bf16_narrow"])
 def test_gated_shared_expert(moe, name):
     """The shared expert's output scaled by sigmoid(x . g): parity with the
     oracle on both layouts (row-major: steps path; tiled: the single pass where
@@ -495,3 +497,23 @@ def test_gated_shared_expert(moe, name):
     assert not torch.equal(a.view(torch.int16), ungated.view(torch.int16))
     if name == "bf16_odd":
         assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_narrow_width_kernel(moe, m):
+    """At up to 8 slots of a wide layer the single pass runs its 8-wave kernel
+    (gate and up on separate waves; M = 2 stays on 4 waves): oracle parity, and
+    the same bits as the steps path."""
+    model = model_for("decode")
+    (x, ids, w), (xt, it, wt) = device_inputs(model.cfg)
+    x, ids, w = x[:m], ids[:m], w[:m]
+    xt, it, wt = xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous()
+    tiled = model.tiled_layer()
+    assert tiled.path(m) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    a = tiled.forward(xt, it, wt)
+    b = model.layer().forward(xt, it, wt)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle_layer(model, x, ids, w)
+    ok, err, bound = tolerance_ok(bf16_to_np(a), ref["out"])
+    assert ok, (err, bound)
