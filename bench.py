@@ -380,16 +380,18 @@ def main():
     best_blocks = min(ceiling, key=ceiling.get)
     same_bytes_us = ceiling[best_blocks]
     big = torch.ones(1 << 30, dtype=torch.int32, device=dev)  # 4 GiB
-    sink = torch.empty(4 * 8192, dtype=torch.int32, device=dev)
-    moe.moe_stream_read_probe(big, sink, 8192, stream=stream)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(5):
-            moe.moe_stream_read_probe(big, sink, 8192, stream=stream)
-        ev1.record(stream)
-    ev1.synchronize()
-    big_gbps = 5 * big.numel() * 4 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    big_gbps = 0.0
+    for blocks in (1024, 2048, 8192):
+        sink = torch.empty(4 * blocks, dtype=torch.int32, device=dev)
+        moe.moe_stream_read_probe(big, sink, blocks, stream=stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(5):
+                moe.moe_stream_read_probe(big, sink, blocks, stream=stream)
+            ev1.record(stream)
+        ev1.synchronize()
+        big_gbps = max(big_gbps, 5 * big.numel() * 4 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9)
     del big
     stream_ceiling = {
         "kernel": "stream_read_kernel (moe_stream_read_probe: 16-byte loads, nothing else)",
