@@ -254,7 +254,7 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
   }
   const moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
   return hip_status(
-      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
+      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
 }
 
 int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void* x_bf16, moe_weight_dtype wdt,
@@ -294,7 +294,7 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
   a.max_total = (int)s.max_total;
   a.tables = to_align_out(*t);
   return hip_status(
-      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
+      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
 }
 
 int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down, const moe_align_tables* t,
@@ -337,7 +337,7 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
   a.top_k = top_k;
   a.cap = s.cap;
   return hip_status(
-      moe::launch_grouped_down(a, is_fp8(wdt), is_tiled(wdt), moe::grouped_row_tiles(M, top_k), stream), fn);
+      moe::launch_grouped_down(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
 }
 
 int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights, const int32_t* token_to_perm,

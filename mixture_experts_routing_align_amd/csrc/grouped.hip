@@ -9,10 +9,10 @@
 namespace moe {
 
 // defined in grouped_{gu,down}_{fp8,bf16}.hip
-hipError_t launch_gate_up_fp8(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s);
-hipError_t launch_gate_up_bf16(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s);
-hipError_t launch_down_fp8(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s);
-hipError_t launch_down_bf16(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s);
+hipError_t launch_gate_up_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s);
+hipError_t launch_gate_up_bf16(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s);
+hipError_t launch_down_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s);
+hipError_t launch_down_bf16(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s);
 
 namespace {
 
@@ -54,12 +54,6 @@ int grouped_rows_per_pass(int64_t M) {
   return r;
 }
 
-int grouped_row_tiles(int64_t M, int top_k) {
-  (void)M;
-  (void)top_k;
-  return 1;
-}
-
 int grouped_step_rows(int64_t M) { return std::min(grouped_rows_per_pass(M), 16); }
 
 // an expert holds at most M rows when ids are distinct within a token (with
@@ -69,14 +63,14 @@ int grouped_passes(int64_t M) {
   return (int)std::max<int64_t>(1, (M + r - 1) / r);
 }
 
-hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s) {
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, hipStream_t s) {
   const int rowcap = grouped_step_rows(a.M);
-  return fp8 ? launch_gate_up_fp8(a, row_tiles, rowcap, tiled, s) : launch_gate_up_bf16(a, row_tiles, rowcap, tiled, s);
+  return fp8 ? launch_gate_up_fp8(a, rowcap, tiled, s) : launch_gate_up_bf16(a, rowcap, tiled, s);
 }
 
-hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s) {
+hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, hipStream_t s) {
   const int rowcap = grouped_step_rows(a.M);
-  return fp8 ? launch_down_fp8(a, row_tiles, rowcap, tiled, s) : launch_down_bf16(a, row_tiles, rowcap, tiled, s);
+  return fp8 ? launch_down_fp8(a, rowcap, tiled, s) : launch_down_bf16(a, rowcap, tiled, s);
 }
 
 size_t tiled_weight_bytes(bool fp8, int64_t E, int N, int K) {

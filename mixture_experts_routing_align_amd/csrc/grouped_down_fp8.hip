@@ -3,8 +3,8 @@
 
 namespace moe {
 
-hipError_t launch_down_fp8(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s) {
-  return grouped_detail::launch<true, false>(a, rt, rowcap, tiled, s);
+hipError_t launch_down_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
+  return grouped_detail::launch<true, false>(a, rowcap, tiled, s);
 }
 
 }  // namespace moe

@@ -3,8 +3,8 @@
 
 namespace moe {
 
-hipError_t launch_gate_up_fp8(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s) {
-  return grouped_detail::launch<true, true>(a, rt, rowcap, tiled, s);
+hipError_t launch_gate_up_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
+  return grouped_detail::launch<true, true>(a, rowcap, tiled, s);
 }
 
 }  // namespace moe

@@ -621,15 +621,10 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   return launch_fused_or_not<FP8, GATE_UP, RT, false, TILED>(b, rowcap, chunked, tiles, s);
 }
 
-template <bool FP8, bool GATE_UP, bool TILED>
-hipError_t launch_layout(const GroupedArgs& a, int rt, int rowcap, hipStream_t s) {
-  (void)rt;  // one 16-row tile per pass: each pass of an expert is a workgroup of its own
-  return launch_rt<FP8, GATE_UP, 1, TILED>(a, rowcap, s);
-}
-
+// one 16-row tile per pass: each pass of an expert is a workgroup of its own
 template <bool FP8, bool GATE_UP>
-hipError_t launch(const GroupedArgs& a, int rt, int rowcap, bool tiled, hipStream_t s) {
-  return tiled ? launch_layout<FP8, GATE_UP, true>(a, rt, rowcap, s) : launch_layout<FP8, GATE_UP, false>(a, rt, rowcap, s);
+hipError_t launch(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
+  return tiled ? launch_rt<FP8, GATE_UP, 1, true>(a, rowcap, s) : launch_rt<FP8, GATE_UP, 1, false>(a, rowcap, s);
 }
 
 }  // namespace grouped_detail

@@ -72,17 +72,14 @@ constexpr int kFusedAlignMaxSlots = MOE_FUSED_ALIGN_MAX_SLOTS;
 // Chosen from the shape class, never from the routing.
 int grouped_rows_per_pass(int64_t M);
 
-// Row tiles (16 rows each) one workgroup keeps in registers per pass.
-int grouped_row_tiles(int64_t M, int top_k);
-
 // The separate grouped kernels: rows per pass (at most 16), and the passes an
 // expert holding M rows needs (1: every expert fits one pass when ids are
 // distinct within a token).
 int grouped_step_rows(int64_t M);
 int grouped_passes(int64_t M);
 
-hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
-hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, int row_tiles, hipStream_t s);
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, hipStream_t s);
 
 // The tiled (MFMA-fragment-ordered) copy of row-major [E, N, K] weights.
 size_t tiled_weight_bytes(bool fp8, int64_t E, int N, int K);
