@@ -101,3 +101,43 @@ def test_router_feeds_the_layer():
     assert torch.equal(ids.cpu(), torch.from_numpy(o_ids))
     err = (a.float() - b.float()).abs().max().item()
     assert err <= 2e-2 * b.float().pow(2).mean().sqrt().item() + 1e-3, err
+
+
+def test_router_row_invariance_and_graph_replay():
+    """A row's logits, ids and weights do not depend on the other rows (M), and
+    a captured router launch replays for new activations."""
+    import mixture_experts_routing_align_amd as moe
+
+    cfg = workloads.CONFIGS["verify"]
+    x = _dev_bf16(workloads.x_bf16(cfg))
+    w = _dev_bf16(workloads.router_weight_bf16(cfg))
+    ids, wts, logits = moe.moe_router_topk(x, w, cfg.top_k)
+    for m in (1, 7, 16, 17, 100):
+        i2, w2, l2 = moe.moe_router_topk(x[:m].contiguous(), w, cfg.top_k)
+        torch.cuda.synchronize()
+        assert torch.equal(l2, logits[:m]) and torch.equal(i2, ids[:m]) and torch.equal(w2, wts[:m]), m
+
+    xs = x[:16].clone()
+    g_ids = torch.empty(16, cfg.top_k, dtype=torch.int64, device="cuda")
+    g_w = torch.empty(16, cfg.top_k, dtype=torch.float32, device="cuda")
+    g_l = torch.empty(16, cfg.E, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def route():
+        moe._check(moe.lib().moe_router_topk(xs.data_ptr(), w.data_ptr(), 16, cfg.H, cfg.E, cfg.top_k, g_l.data_ptr(),
+                                             g_ids.data_ptr(), moe.MOE_IDX_I64, g_w.data_ptr(), stream.cuda_stream))
+
+    with torch.cuda.stream(stream):
+        route()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        route()
+    for start in (16, 48, 80):
+        xs.copy_(x[start:start + 16])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e_ids, e_w, e_l = moe.moe_router_topk(x[start:start + 16].contiguous(), w, cfg.top_k)
+        torch.cuda.synchronize()
+        assert torch.equal(g_ids, e_ids) and torch.equal(g_w, e_w) and torch.equal(g_l, e_l), start
