@@ -42,9 +42,17 @@ FP8_BLOCK = 128
 
 def dequant(bits: np.ndarray, scales: Optional[np.ndarray], wdt: str) -> np.ndarray:
     """Weight matrix [N, K] as float64.  bf16: exact widening.  fp8: e4m3 value
-    of each code times the float32 scale of its 128x128 block."""
+    of each code times the float32 scale of its 128x128 block.  fp8_rows: e4m3
+    value times the float32 scale of its row (the FP8 page's shared-expert
+    weights carry a row scale beside the codes, where the routed experts carry
+    128x128 block scales)."""
     if wdt == "bf16":
         return bf16_to_f64(bits)
+    if wdt == "fp8_rows":
+        vals = e4m3_decode(bits)
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        assert s.shape == (vals.shape[0],)
+        return vals * s[:, None]
     if wdt != "fp8":
         raise ValueError(wdt)
     vals = e4m3_decode(bits)

@@ -290,3 +290,34 @@ def test_blend_gate_scales_only_the_shared_term():
     assert np.allclose(gated, plain + gate[:, None] * sh, rtol=1e-14, atol=1e-14)
     assert np.array_equal(oracle.blend(eo, w, t["token_to_perm"], sh, H=H, sh_gate=np.ones(M)),
                           oracle.blend(eo, w, t["token_to_perm"], sh, H=H))
+
+
+# ------------------------------------------------------- per-row FP8 scales --
+
+def test_dequant_row_scales_match_torch_and_stay_in_their_row():
+    rng = np.random.default_rng(31)
+    codes, _ = _rand_fp8(rng, 256, 384)
+    s = rng.uniform(0.001, 0.01, size=256).astype(np.float32)
+    ours = oracle.dequant(codes, s, "fp8_rows")
+    ref = (torch.from_numpy(codes).view(torch.float8_e4m3fn).double() * torch.from_numpy(s).double()[:, None])
+    assert np.array_equal(ours, ref.numpy())
+    s2 = s.copy()
+    s2[17] *= 4
+    moved = oracle.dequant(codes, s2, "fp8_rows")
+    diff = np.any(moved != ours, axis=1)
+    assert np.array_equal(np.flatnonzero(diff), [17]) or not np.any(codes[17] & 0x7F)
+    assert np.array_equal(moved[17], 4 * ours[17])
+
+
+def test_row_scaled_generator_fills_each_row_to_448():
+    """The fp8_rows workload: every row's largest code is 448 (its row scale is
+    the row's amax / 448) and no dequantised value leaves the draw range
+    [-1/sqrt(K), 1/sqrt(K)]."""
+    import workloads
+    cfg = workloads.MoeConfig("rows", 2, 256, 2, 1, 128, 0, 16, "fp8_rows", "softmax", seed=5)
+    bits, sc = workloads.expert_matrix(cfg, "gate", 0)
+    assert sc.shape == (cfg.I,)
+    w = oracle.dequant(bits, sc, "fp8_rows")
+    assert np.allclose(np.abs(w).max(axis=1), 448.0 * sc, rtol=1e-7)
+    bound = 1.0 / np.sqrt(cfg.H)
+    assert np.all(np.abs(w) <= bound * (1 + 1e-6))

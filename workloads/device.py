@@ -29,7 +29,8 @@ class DeviceWeights:
     def __init__(self, cfg: MoeConfig, device="cuda", keep_host: bool = False, threads: int = 8):
         torch = _torch()
         self.cfg = cfg
-        fp8 = cfg.wdt == "fp8"
+        fp8 = cfg.wdt in ("fp8", "fp8_rows")
+        rows = cfg.wdt == "fp8_rows"  # one scale per row [E, N] instead of per 128x128 block
         wdt = torch.uint8 if fp8 else torch.bfloat16
         self.host = {} if keep_host else None
         lock = threading.Lock()
@@ -37,8 +38,8 @@ class DeviceWeights:
         for which in ("gate", "up", "down"):
             N, K = weight_shape(cfg, which)
             self.w[which] = torch.empty(cfg.E, N, K, dtype=wdt, device=device)
-            self.s[which] = (torch.empty(cfg.E, N // 128, K // 128, dtype=torch.float32, device=device)
-                             if fp8 else None)
+            sshape = (cfg.E, N) if rows else (cfg.E, N // 128, K // 128)
+            self.s[which] = torch.empty(*sshape, dtype=torch.float32, device=device) if fp8 else None
 
             def sink(e, bits, sc, which=which):
                 src = torch.from_numpy(bits) if fp8 else torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
@@ -83,12 +84,14 @@ class DeviceWeights:
         E = cfg.E
         flat = np.asarray(ids).reshape(-1)
         active = int(np.unique(flat[(flat >= 0) & (flat < E)]).size)
-        esz = 1 if cfg.wdt == "fp8" else 2
+        esz = 1 if cfg.wdt in ("fp8", "fp8_rows") else 2
 
         def mat(N, K):
             b = N * K * esz
             if cfg.wdt == "fp8":
                 b += (N // 128) * (K // 128) * 4
+            elif cfg.wdt == "fp8_rows":
+                b += N * 4
             return b
 
         gate_up = 2 * mat(cfg.I, cfg.H) * active

@@ -53,7 +53,7 @@ class MoeConfig:
     I: int          # routed expert intermediate size
     S: int          # shared expert intermediate size (0: no shared expert)
     BS: int         # alignment block size
-    wdt: Optional[str]      # "bf16" | "fp8" | None (align only)
+    wdt: Optional[str]      # "bf16" | "fp8" (128x128 block scales) | "fp8_rows" (row scales) | None
     routing: str            # "softmax" | "softmax_bias" | "zipf"
     bias_std: float = 0.0
     zipf_s: float = 0.0
@@ -155,7 +155,7 @@ def _draw_matrix(cfg: MoeConfig, rng: np.random.Generator, N: int, K: int):
     if cfg.wdt == "bf16":
         w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
         return bf16_bits_from_f32(w), None
-    if cfg.wdt != "fp8":
+    if cfg.wdt not in ("fp8", "fp8_rows"):
         raise ValueError(f"config {cfg.name} has no expert weights")
     import torch  # the float8 cast is torch's; it is the only use of torch here
 
@@ -163,6 +163,12 @@ def _draw_matrix(cfg: MoeConfig, rng: np.random.Generator, N: int, K: int):
         raise ValueError("fp8 weights need N and K in whole 128 blocks")
     a = np.float32(1.0 / np.sqrt(K))
     w = (rng.random((N, K), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)) * a
+    if cfg.wdt == "fp8_rows":  # one float32 scale per row: row amax / 448
+        amax = np.abs(w).max(axis=1)
+        scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        q = np.clip(w / scale[:, None], -448.0, 448.0)
+        codes = torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn)
+        return codes.view(torch.uint8).numpy().copy(), scale
     nb, kb = N // FP8_BLOCK, K // FP8_BLOCK
     blocks = w.reshape(nb, FP8_BLOCK, kb, FP8_BLOCK)
     amax = np.abs(blocks).max(axis=(1, 3))
