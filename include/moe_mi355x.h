@@ -36,8 +36,9 @@
  *     shared expert's are [S, H] and [H, S].  FP8 weights are OCP E4M3
  *     (e4m3fn) codes with one float32 scale per 128x128 block, row-major
  *     [E, N/128, K/128] (fp8_moe_grouped.rs, fp8_grouped_tc_shape_ok: FP8
- *     projections come in whole 128 blocks, the scale blocks).  BF16 weights
- *     take no scale.
+ *     projections come in whole 128 blocks, the scale blocks), or, with the
+ *     _ROWS weight dtypes, one float32 scale per output row, [E, N].  BF16
+ *     weights take no scale.
  *   - Activations x are bf16 [M, H]; intermediates are float32; the output is
  *     bf16 [M, H], one round-to-nearest-even of the float32 blend sum.
  */
@@ -69,12 +70,20 @@ typedef enum { MOE_IDX_I32 = 0, MOE_IDX_I64 = 1 } moe_index_dtype;
 /* Expert weight element type and layout.  The row-major forms are [E, N, K];
  * the tiled forms are the same values reordered by moe_tile_weights() so that
  * every wave streams one contiguous run (see there).  Both layouts give
- * bit-identical results. */
+ * bit-identical results.  FP8 weights carry float32 scales: one per 128x128
+ * block (the FP8 grouped GEMM page's block-wise scaling), or, in the _ROWS
+ * forms, one per output row of each expert (the FP8 page's per-row scale of
+ * its shared-expert weights, here for every expert).  A weight is the code's
+ * e4m3fn value times its scale. */
 typedef enum {
-  MOE_W_BF16 = 0,            /* bf16, row-major [E, N, K]                      */
-  MOE_W_FP8_E4M3 = 1,        /* OCP e4m3fn codes, row-major [E, N, K]          */
-  MOE_W_BF16_TILED = 2,      /* bf16, tiled by moe_tile_weights                */
-  MOE_W_FP8_E4M3_TILED = 3   /* e4m3fn codes, tiled by moe_tile_weights        */
+  MOE_W_BF16 = 0,                /* bf16, row-major [E, N, K]                  */
+  MOE_W_FP8_E4M3 = 1,            /* e4m3fn codes, row-major [E, N, K], scales
+                                    [E, N/128, K/128]                          */
+  MOE_W_BF16_TILED = 2,          /* bf16, tiled by moe_tile_weights            */
+  MOE_W_FP8_E4M3_TILED = 3,      /* e4m3fn codes, tiled; block scales as above */
+  MOE_W_FP8_E4M3_ROWS = 4,       /* e4m3fn codes, row-major [E, N, K], scales
+                                    [E, N] (16-byte aligned)                   */
+  MOE_W_FP8_E4M3_ROWS_TILED = 5  /* e4m3fn codes, tiled; row scales as above   */
 } moe_weight_dtype;
 
 /* Experts one align launch handles (fp8_moe_grouped.rs: the one-launch sort's
@@ -139,22 +148,25 @@ int moe_align(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_
  * then reads its weights as one contiguous stream (on MI355X, ~1.3x the HBM
  * bandwidth of reading 16 row-major rows side by side).  Scales are unchanged. */
 
-/* Bytes of the tiled copy of row-major weights of dtype `wdt` (MOE_W_BF16 or
- * MOE_W_FP8_E4M3) and shape [E, N, K]: E * N * roundup(K, 128) * element size.
+/* Bytes of the tiled copy of row-major weights of dtype `wdt` (MOE_W_BF16,
+ * MOE_W_FP8_E4M3 or MOE_W_FP8_E4M3_ROWS: the codes tile the same way whatever
+ * their scales) and shape [E, N, K]: E * N * roundup(K, 128) * element size.
  * Returns 0 for an invalid shape (the projection rules of the grouped calls). */
 size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K);
 
 /* Write the tiled copy of `src` (row-major, dtype `wdt`) into `dst` (device,
  * moe_tiled_weight_bytes bytes, must not overlap src) on `stream`.  The result
- * is used with MOE_W_BF16_TILED / MOE_W_FP8_E4M3_TILED. */
+ * is used with MOE_W_BF16_TILED, MOE_W_FP8_E4M3_TILED or
+ * MOE_W_FP8_E4M3_ROWS_TILED. */
 int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K,
                      hipStream_t stream);
 
 /* ---------------------------------------------------- grouped expert FFN -- */
 
 /* One projection's weights: w is [E, N, K] (bf16 or e4m3fn codes), row-major
- * or tiled as the call's weight dtype says; scale is [E, N/128, K/128] float32
- * for FP8 and ignored (may be NULL) for BF16. */
+ * or tiled as the call's weight dtype says; scale is float32, [E, N/128, K/128]
+ * for block-scaled FP8, [E, N] for row-scaled FP8, and ignored (may be NULL)
+ * for BF16.  FP8 needs N and K in whole multiples of 128 either way. */
 typedef struct {
   const void* w;
   const float* scale;
@@ -195,7 +207,7 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
  * expert e (float32 [max_total, H]; padding rows not written); with a shared
  * expert (sh_down non-NULL, S > 0) also sh_out[t, :] = W_sh_down sh_act[t, :]
  * (float32 [M, H]).  The depth is summed in 64-deep halves of 128-deep chunks,
- * ascending, from 0: each half's float32 product (times its block scale, FP8)
+ * ascending, from 0: each half's float32 product (times its block or row scale, FP8)
  * is rounded and then added, with no fused multiply-add across halves.  Shapes: FP8 needs H,
  * I, S multiples of 128; BF16 needs I, S multiples of 32 and H a multiple of 16. */
 int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down,

@@ -13,9 +13,11 @@ Entry points (same names as the C ABI): ``moe_align``,
 ``moe_tiled_weight_bytes``, ``moe_align_gate_up_silu``.
 
 Weights are passed as ``(w, scale)`` pairs: ``w`` is ``[E, N, K]``
-``torch.uint8`` e4m3fn codes with ``scale`` float32 ``[E, N/128, K/128]``, or
-``torch.bfloat16`` with ``scale`` None - or as the :class:`TiledWeight` that
-``moe_tile_weights`` makes from such a pair.
+``torch.uint8`` e4m3fn codes with ``scale`` float32 ``[E, N/128, K/128]`` (one
+per 128x128 block) or ``[E, N]`` (one per row), or ``torch.bfloat16`` with
+``scale`` None - or as the :class:`TiledWeight` that ``moe_tile_weights`` makes
+from such a pair.  A shared expert's ``[N, K]`` matrix takes ``[N/128, K/128]``
+or ``[N]`` scales.
 """
 
 from __future__ import annotations
@@ -46,6 +48,8 @@ from ._ffi import (  # noqa: F401
     MOE_W_BF16,
     MOE_W_BF16_TILED,
     MOE_W_FP8_E4M3,
+    MOE_W_FP8_E4M3_ROWS,
+    MOE_W_FP8_E4M3_ROWS_TILED,
     MOE_W_FP8_E4M3_TILED,
     TABLE_FIELDS,
     MoeAlignTables,
@@ -154,12 +158,15 @@ class TiledWeight:
 
 
 def weight_dtype(w) -> int:
+    """The weight dtype of a pair, a tiled weight or a bare tensor; FP8 scales
+    with one dimension fewer than the codes are row scales."""
+    s = None
     if isinstance(w, TiledWeight):
         return w.wdt
     if isinstance(w, tuple):
-        w = w[0]
+        w, s = w
     if w.dtype in (torch.uint8, torch.float8_e4m3fn):
-        return MOE_W_FP8_E4M3
+        return MOE_W_FP8_E4M3_ROWS if s is not None and s.dim() == w.dim() - 1 else MOE_W_FP8_E4M3
     if w.dtype == torch.bfloat16:
         return MOE_W_BF16
     raise ValueError(f"unsupported weight dtype {w.dtype}")
@@ -182,7 +189,7 @@ def _weight(wt) -> Optional[MoeWeight]:
     w, s = wt
     _need(w.is_contiguous() and (s is None or s.is_contiguous()), "weights must be contiguous")
     if weight_dtype(w) == MOE_W_FP8_E4M3:
-        _need(s is not None and s.dtype == torch.float32, "FP8 weights need float32 block scales")
+        _need(s is not None and s.dtype == torch.float32, "FP8 weights need float32 scales")
     return MoeWeight(w.data_ptr(), _ptr(s))
 
 
@@ -197,16 +204,24 @@ def moe_tile_weights(wt: Weight, stream=None) -> TiledWeight:
     """The tiled copy of a row-major ``(w, scale)`` pair (a new device buffer)."""
     w, s = wt
     _need(w.is_contiguous(), "weights must be contiguous")
-    wdt = weight_dtype(w)
+    wdt = weight_dtype(wt)
     E, N, K = weight_shape(wt)
     dst = torch.empty(moe_tiled_weight_bytes(wdt, E, N, K), dtype=torch.uint8, device=w.device)
     _check(lib().moe_tile_weights(w.data_ptr(), dst.data_ptr(), wdt, E, N, K, _stream(stream)))
-    tiled = MOE_W_FP8_E4M3_TILED if wdt == MOE_W_FP8_E4M3 else MOE_W_BF16_TILED
+    tiled = {MOE_W_FP8_E4M3: MOE_W_FP8_E4M3_TILED, MOE_W_FP8_E4M3_ROWS: MOE_W_FP8_E4M3_ROWS_TILED,
+             MOE_W_BF16: MOE_W_BF16_TILED}[wdt]
     return TiledWeight(dst, s, tiled, (E, N, K))
 
 
 def _ref(x):
     return None if x is None else ctypes.byref(x)
+
+
+def _common_dtype(*weights) -> int:
+    """The one weight dtype of the given weights (None entries skipped)."""
+    kinds = {weight_dtype(w) for w in weights if w is not None}
+    _need(len(kinds) == 1, "all weights of a call must share one dtype, layout and scale form")
+    return kinds.pop()
 
 
 def moe_grouped_gate_up_silu(x: torch.Tensor, gate: Weight, up: Weight, tables: AlignTables, act: torch.Tensor,
@@ -219,7 +234,7 @@ def moe_grouped_gate_up_silu(x: torch.Tensor, gate: Weight, up: Weight, tables: 
     _need(act.dtype == torch.float32 and act.shape[1] == I, "act must be float32 [max_total, I]")
     S = 0 if sh_gate is None else weight_shape(sh_gate)[1]
     c = tables.as_c()
-    wdt = weight_dtype(gate)
+    wdt = _common_dtype(gate, up, sh_gate, sh_up)
     _check(lib().moe_grouped_gate_up_silu(
         x.data_ptr(), wdt, ctypes.byref(_weight(gate)), ctypes.byref(_weight(up)), ctypes.byref(c),
         act.data_ptr(), _ref(_weight(sh_gate)), _ref(_weight(sh_up)), _ptr(sh_act),
@@ -243,7 +258,7 @@ def moe_align_gate_up_silu(topk_ids: torch.Tensor, x: torch.Tensor, gate, up, E:
     idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
     c = tables.as_c()
     _check(lib().moe_align_gate_up_silu(
-        topk_ids.data_ptr(), idt, x.data_ptr(), weight_dtype(gate), ctypes.byref(_weight(gate)),
+        topk_ids.data_ptr(), idt, x.data_ptr(), _common_dtype(gate, up, sh_gate, sh_up), ctypes.byref(_weight(gate)),
         ctypes.byref(_weight(up)), ctypes.byref(c), act.data_ptr(), _ref(_weight(sh_gate)), _ref(_weight(sh_up)),
         _ptr(sh_act), M, H, I, S, E, top_k, BS, _stream(stream)))
     return tables
@@ -259,7 +274,7 @@ def moe_grouped_down(act: torch.Tensor, down: Weight, tables: AlignTables, exper
     S = 0 if sh_down is None else weight_shape(sh_down)[2]
     c = tables.as_c()
     _check(lib().moe_grouped_down(
-        act.data_ptr(), weight_dtype(down), ctypes.byref(_weight(down)), ctypes.byref(c),
+        act.data_ptr(), _common_dtype(down, sh_down), ctypes.byref(_weight(down)), ctypes.byref(c),
         expert_out.data_ptr(), _ref(_weight(sh_down)), _ptr(sh_act), _ptr(sh_out),
         M, H, I, S, E, top_k, BS, _stream(stream)))
 

@@ -70,23 +70,30 @@ int check_tables(const char* fn, const moe_align_tables* t, bool all) {
   return MOE_OK;
 }
 
-bool is_fp8(moe_weight_dtype wdt) { return wdt == MOE_W_FP8_E4M3 || wdt == MOE_W_FP8_E4M3_TILED; }
-bool is_tiled(moe_weight_dtype wdt) { return wdt == MOE_W_BF16_TILED || wdt == MOE_W_FP8_E4M3_TILED; }
+bool is_rows(moe_weight_dtype wdt) { return wdt == MOE_W_FP8_E4M3_ROWS || wdt == MOE_W_FP8_E4M3_ROWS_TILED; }
+bool is_fp8(moe_weight_dtype wdt) { return wdt == MOE_W_FP8_E4M3 || wdt == MOE_W_FP8_E4M3_TILED || is_rows(wdt); }
+bool is_tiled(moe_weight_dtype wdt) {
+  return wdt == MOE_W_BF16_TILED || wdt == MOE_W_FP8_E4M3_TILED || wdt == MOE_W_FP8_E4M3_ROWS_TILED;
+}
 
 int check_weight(const char* fn, const char* name, const moe_weight* w, moe_weight_dtype wdt) {
   if (w == nullptr || w->w == nullptr) return fail(MOE_ERR_NULL, "%s: %s weights are NULL", fn, name);
-  if (is_fp8(wdt) && w->scale == nullptr) return fail(MOE_ERR_NULL, "%s: %s FP8 block scales are NULL", fn, name);
+  if (is_fp8(wdt) && w->scale == nullptr) return fail(MOE_ERR_NULL, "%s: %s FP8 scales are NULL", fn, name);
+  // per-row scales are read four rows at a time
+  if (is_rows(wdt) && reinterpret_cast<uintptr_t>(w->scale) % 16)
+    return fail(MOE_ERR_SHAPE, "%s: %s FP8 row scales are not 16-byte aligned", fn, name);
   return MOE_OK;
 }
 
 int check_wdt(const char* fn, moe_weight_dtype wdt) {
-  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3 && wdt != MOE_W_BF16_TILED && wdt != MOE_W_FP8_E4M3_TILED)
+  if (wdt < MOE_W_BF16 || wdt > MOE_W_FP8_E4M3_ROWS_TILED)
     return fail(MOE_ERR_SHAPE, "%s: unknown weight dtype %d", fn, (int)wdt);
   return MOE_OK;
 }
 
 // A projection with N output rows and depth K: FP8 needs whole 128x128 scale
-// blocks; BF16 needs K in whole 32-deep MFMA steps and N in whole 16-row tiles.
+// blocks (with per-row scales too: the kernels walk K in the same 128-deep
+// chunks); BF16 needs K in whole 32-deep MFMA steps and N in whole 16-row tiles.
 int check_projection(const char* fn, const char* name, moe_weight_dtype wdt, int32_t N, int32_t K) {
   if (N < 1 || K < 1) return fail(MOE_ERR_SHAPE, "%s: %s is %dx%d", fn, name, N, K);
   if (is_fp8(wdt)) {
@@ -147,7 +154,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // the routing): the single-pass layer for tiled weights at decode width.
 int layer_path(const moe_layer_desc* d) {
   const bool fits = is_tiled(d->wdt) &&
-                    moe::fused_layer_fits(is_fp8(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
+                    moe::fused_layer_fits(is_fp8(d->wdt), is_rows(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
   return fits ? MOE_LAYER_PATH_SINGLE_PASS : MOE_LAYER_PATH_STEPS;
 }
 
@@ -199,7 +206,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 6; }
+int32_t moe_abi_version(void) { return 7; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -252,7 +259,8 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
       return rc;
     if (sh_act == nullptr) return fail(MOE_ERR_NULL, "%s: sh_act is NULL with S > 0", fn);
   }
-  const moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
+  moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
+  a.scale_rows = is_rows(wdt);
   return hip_status(
       moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
 }
@@ -293,6 +301,7 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
   a.BS = BS;
   a.max_total = (int)s.max_total;
   a.tables = to_align_out(*t);
+  a.scale_rows = is_rows(wdt);
   return hip_status(
       moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
 }
@@ -336,6 +345,7 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
   a.M = (int)M;
   a.top_k = top_k;
   a.cap = s.cap;
+  a.scale_rows = is_rows(wdt);
   return hip_status(
       moe::launch_grouped_down(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
 }
@@ -358,7 +368,7 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
 
 size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K) {
   const char* fn = "moe_tiled_weight_bytes";
-  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3) {
+  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3 && wdt != MOE_W_FP8_E4M3_ROWS) {
     fail(MOE_ERR_SHAPE, "%s: source dtype %d is not a row-major dtype", fn, (int)wdt);
     return 0;
   }
@@ -455,6 +465,7 @@ moe::FusedLayerArgs single_pass_args(const moe_layer_desc* d, char* ws, const si
     a.ss[i] = shared ? sw[i]->scale : nullptr;
   }
   a.sh_gate = shared ? d->sh_expert_gate : nullptr;
+  a.scale_rows = is_rows(d->wdt);
   a.topk_weights = topk_weights;
   a.out = static_cast<uint16_t*>(out_bf16);
   a.part = reinterpret_cast<float*>(ws + off[12]);

@@ -4,7 +4,8 @@
 namespace moe {
 
 hipError_t launch_gate_up_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
-  return grouped_detail::launch<true, true>(a, rowcap, tiled, s);
+  return a.scale_rows ? grouped_detail::launch<true, true, true>(a, rowcap, tiled, s)
+                      : grouped_detail::launch<true, false, true>(a, rowcap, tiled, s);
 }
 
 }  // namespace moe

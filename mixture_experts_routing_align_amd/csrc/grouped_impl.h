@@ -67,7 +67,10 @@ __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
   return ((size_t)kWaves * E + E + (E + 1) + E + 2 * kWaves + 2 + n) * sizeof(int);
 }
 
-template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
+// ROWS (FP8 only): one float32 scale per weight row, [E, N], instead of one per
+// 128x128 block; it multiplies the same places the block scale does (each
+// 128-deep gate/up chunk's sum, each 64-deep down half), per output column.
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
 __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int rowcap, int ctw, size_t xs_bytes) {
   constexpr int NS = GATE_UP ? 2 : 1;   // weight streams (gate, up) or (down)
   constexpr int NX = GATE_UP ? 1 : 2;   // B planes: bf16 x, or bf16 hi + lo of act
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     W0 = static_cast<const char*>(p.w0) + (size_t)e * wstride;
     if (GATE_UP) W1 = static_cast<const char*>(p.w1) + (size_t)e * wstride;
     if (FP8) {
-      const size_t sstride = (size_t)(N / kFp8Block) * (K / kFp8Block);
+      const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
       S0 = p.s0 + (size_t)e * sstride;
       if (GATE_UP) S1 = p.s1 + (size_t)e * sstride;
     }
@@ -270,17 +273,23 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
 #pragma unroll
   for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j]);
 
-  // the FP8 scales of a tile's 16 columns of this wave, one 128-deep block per lane
+  // the FP8 scales of a tile's 16 columns of this wave: one 128-deep block per
+  // lane, or (ROWS) the scales of this lane's 4 output columns
   float sreg[NS][SL];
+  f32x4 rs[NS];
   auto load_scales = [&](int t) {
     if (!FP8) return;
     bool on;
     const int wcol = wave_col(t, on);
 #pragma unroll
     for (int st = 0; st < NS; ++st) {
-      const float* sw = (st == 0 ? S0 : S1) + (size_t)(wcol / kFp8Block) * kblocks;
+      if constexpr (ROWS) {
+        rs[st] = *reinterpret_cast<const f32x4*>((st == 0 ? S0 : S1) + wcol + 4 * q);
+      } else {
+        const float* sw = (st == 0 ? S0 : S1) + (size_t)(wcol / kFp8Block) * kblocks;
 #pragma unroll
-      for (int i = 0; i < SL; ++i) sreg[st][i] = lane + 64 * i < kblocks ? sw[lane + 64 * i] : 0.f;
+        for (int i = 0; i < SL; ++i) sreg[st][i] = lane + 64 * i < kblocks ? sw[lane + 64 * i] : 0.f;
+      }
     }
   };
   auto scale_of = [&](int st, int c) -> float {
@@ -372,10 +381,15 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
           }
         }
       float sc[NS];
-      if (FP8) {
+      if (FP8 && !ROWS) {
 #pragma unroll
         for (int st = 0; st < NS; ++st) sc[st] = scale_of(st, c);
       }
+      // the scale of output column i of this lane (a column's block or row scale)
+      auto col_scale = [&](int st, int i) -> float {
+        if constexpr (ROWS) return rs[st][i];
+        return sc[st];
+      };
       const uint16_t* xb = xs + (size_t)slot * NX * plane + kb;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -399,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
 #pragma unroll
               for (int s = 0; s < 4; ++s) t = mfma(a[st][s], b[0][s], t);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[st][rt][i] = fmaf(sc[st], t[i], acc[st][rt][i]);
+              for (int i = 0; i < 4; ++i) acc[st][rt][i] = fmaf(col_scale(st, i), t[i], acc[st][rt][i]);
             } else if (GATE_UP) {
               // bf16 depth comes in whole 32-deep steps; steps past K are skipped
 #pragma unroll
@@ -422,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
                       for (int x = 0; x < NX; ++x) t = mfma(a[st][s], b[x][s], t);
 #pragma unroll
                   for (int i = 0; i < 4; ++i)
-                    acc[st][rt][i] = add_rn(acc[st][rt][i], FP8 ? mul_rn(sc[st], t[i]) : t[i]);
+                    acc[st][rt][i] = add_rn(acc[st][rt][i], FP8 ? mul_rn(col_scale(st, i), t[i]) : t[i]);
                 }
               }
             }
@@ -554,9 +568,9 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
 hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
-  auto kern = grouped_kernel<FP8, GATE_UP, RT, RESIDENT, TILED, FUSED, IdT>;
+  auto kern = grouped_kernel<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, FUSED, IdT>;
   const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
   static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
   if (lds > 64 * 1024 && lds > configured) {
@@ -593,16 +607,17 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
   return hipGetLastError();
 }
 
-template <bool FP8, bool GATE_UP, int RT, bool RESIDENT, bool TILED>
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED>
 hipError_t launch_fused_or_not(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   if (GATE_UP && a.ids != nullptr) {
-    if (a.ids64) return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
-    return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
+    if (a.ids64)
+      return launch_one<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
+    return launch_one<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
   }
-  return launch_one<FP8, GATE_UP, RT, RESIDENT, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
+  return launch_one<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
 }
 
-template <bool FP8, bool GATE_UP, int RT, bool TILED>
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool TILED>
 hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   constexpr int NX = GATE_UP ? 1 : 2;
   const int kmax = (a.sw0 != nullptr && a.sK > a.K) ? a.sK : a.K;
@@ -617,14 +632,15 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   const int64_t n = (int64_t)a.M * a.top_k;
   b.items = (int)((n + (int64_t)a.cap * (rowcap - 1)) / rowcap);
   if (resident <= kResidentLdsBudget)
-    return launch_fused_or_not<FP8, GATE_UP, RT, true, TILED>(b, rowcap, resident, tiles, s);
-  return launch_fused_or_not<FP8, GATE_UP, RT, false, TILED>(b, rowcap, chunked, tiles, s);
+    return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, true, TILED>(b, rowcap, resident, tiles, s);
+  return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, false, TILED>(b, rowcap, chunked, tiles, s);
 }
 
 // one 16-row tile per pass: each pass of an expert is a workgroup of its own
-template <bool FP8, bool GATE_UP>
+template <bool FP8, bool ROWS, bool GATE_UP>
 hipError_t launch(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
-  return tiled ? launch_rt<FP8, GATE_UP, 1, true>(a, rowcap, s) : launch_rt<FP8, GATE_UP, 1, false>(a, rowcap, s);
+  return tiled ? launch_rt<FP8, ROWS, GATE_UP, 1, true>(a, rowcap, s)
+               : launch_rt<FP8, ROWS, GATE_UP, 1, false>(a, rowcap, s);
 }
 
 }  // namespace grouped_detail

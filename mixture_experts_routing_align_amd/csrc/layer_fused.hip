@@ -66,7 +66,11 @@ __host__ __device__ constexpr size_t act_lds_bytes(int rowcap, bool split) {
 // tiles, two 128-deep chunks per step, and the up sums reach the gate waves
 // through LDS; each wave then streams half the bytes, which helps when the
 // whole layer is only a few hundred workgroups.  Same arithmetic either way.
-template <bool FP8, int RT, typename IdT, int W>
+// ROWS (FP8 only): one float32 scale per weight row ([E, N]) instead of one
+// per 128x128 block; it multiplies where the block scale does, per output
+// column (gate/up: the lane's 4 intermediate columns; down: its 4 rows of H,
+// read from a copy of the expert's down row scales in LDS).
+template <bool FP8, bool ROWS, int RT, typename IdT, int W>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void layer_kernel(
     FusedLayerArgs p, int rowcap, size_t xs_bytes, size_t act_bytes) {
   constexpr int kWaves = W;
@@ -142,9 +146,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     D = static_cast<const char*>(p.w[2]) + (size_t)e * H * tile_d / kWaveCols;
     if (FP8) {
       const size_t ss = (size_t)(NI / kFp8Block) * (H / kFp8Block);
-      SG = p.s[0] + e * ss;
-      SU = p.s[1] + e * ss;
-      SD = p.s[2] + e * ss;
+      SG = p.s[0] + e * (ROWS ? (size_t)NI : ss);
+      SU = p.s[1] + e * (ROWS ? (size_t)NI : ss);
+      SD = p.s[2] + e * (ROWS ? (size_t)H : ss);
     }
     OUT = p.part + (size_t)slice * p.n * H;
   } else {
@@ -201,7 +205,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   // slice / 2), down per step (row block of the step's tiles, depth block =
   // slice / 2)
   float sg[SL], su[SL], sd = 0.f;
-  if (FP8) {
+  f32x4 rsg = {0.f, 0.f, 0.f, 0.f}, rsu = rsg;  // ROWS: scales of this lane's 4 gate / up columns
+  if (FP8 && ROWS) {
+    const int c0 = (gon ? tg : slice * kColTiles) * kWaveCols + 4 * q;
+    rsg = *reinterpret_cast<const f32x4*>((SPLIT && st ? SU : SG) + c0);
+    if (!SPLIT) rsu = *reinterpret_cast<const f32x4*>(SU + c0);
+  } else if (FP8) {
     const int kbH = H / kFp8Block, kbI = NI / kFp8Block;
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
@@ -220,6 +229,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   const int astride = kSlice + kPad;
   const int aplane = rowcap * astride;
   const int pieces = H / 8;  // 16-byte pieces of one x row
+  // ROWS: the expert's down row scales [H] in LDS, after act (and the up sums);
+  // the first barrier of the pass below orders them before any read
+  float* rsd = reinterpret_cast<float*>(as + 2 * aplane) + (SPLIT ? rowcap * kSlice : 0);
+  if constexpr (FP8 && ROWS) {
+    for (int i = tid; i < H / 4; i += kThreads)
+      *reinterpret_cast<f32x4*>(rsd + 4 * i) = *reinterpret_cast<const f32x4*>(SD + 4 * i);
+  }
 
   uint4 wb[NBUF][NL];
   for (int r0 = 0; r0 < rows; r0 += rowcap) {
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
         for (int c2 = 0; c2 < 2; ++c2) {
           const int c = 2 * v + c2;
           if (c < nchH) {
-            const float scg = FP8 ? lane_scale(sg, c) : 1.f;
+            const float scg = FP8 && !ROWS ? lane_scale(sg, c) : 1.f;
             const uint16_t* xb = xs + c * kKC;
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
                     t4 = mfma(gu_op(wc, c2, s), b, t4);
                   }
 #pragma unroll
-                  for (int i = 0; i < 4; ++i) ag[rt][i] = fmaf(scg, t4[i], ag[rt][i]);
+                  for (int i = 0; i < 4; ++i) ag[rt][i] = fmaf(ROWS ? rsg[i] : scg, t4[i], ag[rt][i]);
                 } else {
 #pragma unroll
                   for (int s = 0; s < 4; ++s) {
@@ -320,8 +336,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
         }
       } else {
         const int c = v;
-        const float scg = FP8 ? lane_scale(sg, c) : 1.f;
-        const float scu = FP8 ? lane_scale(su, c) : 1.f;
+        const float scg = FP8 && !ROWS ? lane_scale(sg, c) : 1.f;
+        const float scu = FP8 && !ROWS ? lane_scale(su, c) : 1.f;
         const uint16_t* xb = xs + c * kKC;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -337,8 +353,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
               }
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                ag[rt][i] = fmaf(scg, tg4[i], ag[rt][i]);
-                au[rt][i] = fmaf(scu, tu4[i], au[rt][i]);
+                ag[rt][i] = fmaf(ROWS ? rsg[i] : scg, tg4[i], ag[rt][i]);
+                au[rt][i] = fmaf(ROWS ? rsu[i] : scu, tu4[i], au[rt][i]);
               }
             } else {
 #pragma unroll
@@ -402,7 +418,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     // the MFMA sequence of one 64-deep half in the separate down kernel
     auto down = [&](const uint4 (&wc)[NL], int i) {
       const int T0 = dfirst + kDownTiles * i;
-      const float sc = FP8 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sd), i)) : 1.f;
+      const float sc = FP8 && !ROWS ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sd), i)) : 1.f;
       const int k0 = slice * kSlice;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -429,11 +445,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 #pragma unroll
             for (int u = 0; u < kDownTiles; ++u) {
               if (T0 + u < ntd) {
+                f32x4 s4 = {sc, sc, sc, sc};
+                if constexpr (ROWS) s4 = *reinterpret_cast<const f32x4*>(rsd + (T0 + u) * kWaveCols + 4 * q);
                 float4 o;
-                o.x = FP8 ? mul_rn(sc, t[u][0]) : t[u][0];
-                o.y = FP8 ? mul_rn(sc, t[u][1]) : t[u][1];
-                o.z = FP8 ? mul_rn(sc, t[u][2]) : t[u][2];
-                o.w = FP8 ? mul_rn(sc, t[u][3]) : t[u][3];
+                o.x = FP8 ? mul_rn(s4[0], t[u][0]) : t[u][0];
+                o.y = FP8 ? mul_rn(s4[1], t[u][1]) : t[u][1];
+                o.z = FP8 ? mul_rn(s4[2], t[u][2]) : t[u][2];
+                o.w = FP8 ? mul_rn(s4[3], t[u][3]) : t[u][3];
                 *reinterpret_cast<float4*>(OUT + (size_t)dst[rt] * H + (T0 + u) * kWaveCols + 4 * q) = o;
               }
             }
@@ -578,10 +596,11 @@ __global__ __launch_bounds__(256) void blend_parts_kernel(uint16_t* __restrict__
 // even; the 256-wide layer of 8 experts 9% slower)
 inline int layer_waves(int n, int H) { return n <= kNarrowSlots && H >= kNarrowMinH ? 2 * kColTiles : kColTiles; }
 
-template <bool FP8, int RT, typename IdT, int W>
+template <bool FP8, bool ROWS, int RT, typename IdT, int W>
 hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
-  auto kern = layer_kernel<FP8, RT, IdT, W>;
-  const size_t xs = x_lds_bytes(rowcap, a.H), ab = act_lds_bytes(rowcap, W == 2 * kColTiles);
+  auto kern = layer_kernel<FP8, ROWS, RT, IdT, W>;
+  const size_t xs = x_lds_bytes(rowcap, a.H);
+  const size_t ab = act_lds_bytes(rowcap, W == 2 * kColTiles) + (ROWS ? (size_t)a.H * 4 : 0);
   const size_t lds = xs + ab + align_lds_bytes(a.E, a.n, W);
   static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
   if (lds > 64 * 1024 && lds > configured) {
@@ -598,15 +617,21 @@ hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool FP8, typename IdT>
+template <bool FP8, bool ROWS, typename IdT>
 hipError_t launch_rt(const FusedLayerArgs& a, hipStream_t s) {
   const int rowcap = grouped_rows_per_pass(a.M);
-  if (layer_waves(a.n, a.H) == 2 * kColTiles) return launch_kernel<FP8, 1, IdT, 2 * kColTiles>(a, rowcap, s);
+  if (layer_waves(a.n, a.H) == 2 * kColTiles) return launch_kernel<FP8, ROWS, 1, IdT, 2 * kColTiles>(a, rowcap, s);
   switch (rowcap <= 16 ? 1 : rowcap / 16) {
-    case 1: return launch_kernel<FP8, 1, IdT, kColTiles>(a, rowcap, s);
-    case 2: return launch_kernel<FP8, 2, IdT, kColTiles>(a, rowcap, s);
-    default: return launch_kernel<FP8, 4, IdT, kColTiles>(a, rowcap, s);
+    case 1: return launch_kernel<FP8, ROWS, 1, IdT, kColTiles>(a, rowcap, s);
+    case 2: return launch_kernel<FP8, ROWS, 2, IdT, kColTiles>(a, rowcap, s);
+    default: return launch_kernel<FP8, ROWS, 4, IdT, kColTiles>(a, rowcap, s);
   }
+}
+
+template <bool FP8, typename IdT>
+hipError_t launch_scales(const FusedLayerArgs& a, hipStream_t s) {
+  if (FP8 && a.scale_rows) return launch_rt<FP8, true, IdT>(a, s);
+  return launch_rt<FP8, false, IdT>(a, s);
 }
 
 template <typename IdT>
@@ -622,7 +647,7 @@ hipError_t launch_blend(const FusedLayerArgs& a, hipStream_t s) {
 
 }  // namespace layer_detail
 
-bool fused_layer_fits(bool fp8, int64_t M, int H, int I, int S, int E, int top_k) {
+bool fused_layer_fits(bool fp8, bool scale_rows, int64_t M, int H, int I, int S, int E, int top_k) {
   using namespace layer_detail;
   const int64_t n = M * top_k;
   if (n < 1 || n > kFusedLayerMaxSlots) return false;
@@ -633,14 +658,14 @@ bool fused_layer_fits(bool fp8, int64_t M, int H, int I, int S, int E, int top_k
   if (rowcap > kMaxRowCap) return false;
   const int waves = layer_waves((int)n, H);
   const size_t lds = x_lds_bytes(rowcap, H) + act_lds_bytes(rowcap, waves == 2 * kColTiles) +
-                     align_lds_bytes(E, (int)n, waves);
+                     (fp8 && scale_rows ? (size_t)H * 4 : 0) + align_lds_bytes(E, (int)n, waves);
   return lds <= kLdsBudget;
 }
 
 hipError_t launch_layer_partials(const FusedLayerArgs& a, bool fp8, hipStream_t s) {
   using namespace layer_detail;
-  if (fp8) return a.ids64 ? launch_rt<true, int64_t>(a, s) : launch_rt<true, int32_t>(a, s);
-  return a.ids64 ? launch_rt<false, int64_t>(a, s) : launch_rt<false, int32_t>(a, s);
+  if (fp8) return a.ids64 ? launch_scales<true, int64_t>(a, s) : launch_scales<true, int32_t>(a, s);
+  return a.ids64 ? launch_scales<false, int64_t>(a, s) : launch_scales<false, int32_t>(a, s);
 }
 
 hipError_t launch_blend_partials(const FusedLayerArgs& a, hipStream_t s) {

@@ -54,6 +54,7 @@ struct GroupedArgs {
   const int32_t* active_experts;
   const int32_t* active_count;
   int M, top_k, cap;
+  int scale_rows;  // FP8 scales are one per weight row, [E, N] (else per 128x128 block)
   int items;    // routed work items (rowcap-row passes of active experts) the grid covers; set at launch
   int sgroups;  // shared-expert row groups, ahead of the routed items; set at launch
   // fused alignment (gate+up only; ids != nullptr): every routed workgroup
@@ -98,6 +99,7 @@ struct FusedLayerArgs {
   const void* sw[3];      // shared expert (sw[0] == nullptr: none), tiled
   const float* ss[3];
   const void* sh_gate;    // bf16 [H] gate vector of the shared expert, or nullptr (ungated)
+  int scale_rows;         // FP8 scales are one per weight row, [E, N] (else per 128x128 block)
   const float* topk_weights;
   uint16_t* out;          // bf16 [M, H]
   float* part;            // [ceil(I/64)][n][H] routed partials by slot
@@ -111,7 +113,7 @@ constexpr int kFusedLayerMaxSlots = 256;
 
 // Whether the single-pass layer runs this shape (tiled weights assumed): slot
 // count, depth limits and the LDS it needs.
-bool fused_layer_fits(bool fp8, int64_t M, int H, int I, int S, int E, int top_k);
+bool fused_layer_fits(bool fp8, bool scale_rows, int64_t M, int H, int I, int S, int E, int top_k);
 // the first launch (align, gate+up+SiLU, down partials) and the second (sum + blend)
 hipError_t launch_layer_partials(const FusedLayerArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);

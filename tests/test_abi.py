@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -101,7 +101,18 @@ def test_grouped_refusals(lib):
     assert gu(I=64) == _ffi.MOE_ERR_SHAPE
     assert gu(wdt=0, H=48) == _ffi.MOE_ERR_SHAPE    # BF16 needs K % 32
     assert gu(wdt=0, I=24) == _ffi.MOE_ERR_SHAPE    # and N % 16
-    assert gu(wdt=5) == _ffi.MOE_ERR_SHAPE
+    assert gu(wdt=6) == _ffi.MOE_ERR_SHAPE          # no such weight dtype
+    assert gu(wdt=-1) == _ffi.MOE_ERR_SHAPE
+    # FP8 with row scales keeps the 128-multiple shapes, and reads its scales 16 bytes at a time
+    assert gu(wdt=_ffi.MOE_W_FP8_E4M3_ROWS, H=200) == _ffi.MOE_ERR_SHAPE
+    assert gu(wdt=_ffi.MOE_W_FP8_E4M3_ROWS_TILED, I=64) == _ffi.MOE_ERR_SHAPE
+    odd = _ffi.MoeWeight(FAKE, FAKE + 4)
+    for wdt in (_ffi.MOE_W_FP8_E4M3_ROWS, _ffi.MOE_W_FP8_E4M3_ROWS_TILED):
+        assert lib.moe_grouped_gate_up_silu(FAKE, wdt, ctypes.byref(odd), ctypes.byref(u), ctypes.byref(t), FAKE,
+                                            None, None, None, 4, 256, 128, 0, 8, 2, 16, None) == _ffi.MOE_ERR_SHAPE
+        assert "16-byte" in _err(lib)
+        assert lib.moe_grouped_down(FAKE, wdt, ctypes.byref(odd), ctypes.byref(t), FAKE, None, None, None,
+                                    4, 256, 128, 0, 8, 2, 16, None) == _ffi.MOE_ERR_SHAPE
     assert gu(S=128) == _ffi.MOE_ERR_NULL           # shared expert without weights
     assert gu(E=2000) == _ffi.MOE_ERR_LIMIT
     assert gu(M=0) == _ffi.MOE_OK
@@ -275,3 +286,26 @@ def test_shared_gate_needs_a_shared_expert(lib):
     need = lib.moe_layer_workspace_bytes(ctypes.byref(t))
     assert lib.moe_layer_blend_partials(ctypes.byref(t), None, FAKE, FAKE, FAKE, 0x100000, need,
                                         None) == _ffi.MOE_ERR_NULL
+
+
+def test_row_scaled_fp8_dtypes(lib):
+    """Row-scaled FP8 codes tile exactly like block-scaled ones; the binding
+    tells the two scale forms apart by the scales' rank."""
+    import torch
+
+    import mixture_experts_routing_align_amd as moe
+
+    for E, N, K in ((1, 128, 256), (8, 384, 1024)):
+        assert lib.moe_tiled_weight_bytes(_ffi.MOE_W_FP8_E4M3_ROWS, E, N, K) == \
+            lib.moe_tiled_weight_bytes(_ffi.MOE_W_FP8_E4M3, E, N, K) == E * N * K
+    assert lib.moe_tiled_weight_bytes(_ffi.MOE_W_FP8_E4M3_ROWS_TILED, 1, 128, 128) == 0  # not a source dtype
+    assert lib.moe_tiled_weight_bytes(_ffi.MOE_W_FP8_E4M3_ROWS, 1, 128, 100) == 0
+    w3 = torch.zeros(4, 256, 128, dtype=torch.uint8)
+    w2 = torch.zeros(256, 128, dtype=torch.uint8)
+    assert moe.weight_dtype((w3, torch.ones(4, 2, 1))) == _ffi.MOE_W_FP8_E4M3
+    assert moe.weight_dtype((w3, torch.ones(4, 256))) == _ffi.MOE_W_FP8_E4M3_ROWS
+    assert moe.weight_dtype((w2, torch.ones(2, 1))) == _ffi.MOE_W_FP8_E4M3
+    assert moe.weight_dtype((w2, torch.ones(256))) == _ffi.MOE_W_FP8_E4M3_ROWS
+    assert moe.weight_dtype((w3.to(torch.bfloat16), None)) == _ffi.MOE_W_BF16
+    with pytest.raises(ValueError):
+        moe._common_dtype((w3, torch.ones(4, 256)), (w3, torch.ones(4, 2, 1)))

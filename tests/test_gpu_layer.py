@@ -183,6 +183,13 @@ ODD = [
     workloads.MoeConfig("fp8_wide", 130, 256, 8, 2, 256, 128, 8, "fp8", "softmax_bias", bias_std=2.0, seed=11),
     # one token over a 1024-wide layer: the single pass's 8-wave kernel, bf16, with a shared expert
     workloads.MoeConfig("bf16_narrow", 1, 1024, 16, 4, 192, 128, 8, "bf16", "softmax", seed=12),
+    # FP8 with one scale per weight row: 36 slots (tiled: the single pass), many passes
+    # (steps path only), one token over a 1024-wide layer (tiled: the 8-wave single pass)
+    workloads.MoeConfig("fp8_rows_small", 9, 256, 16, 4, 384, 128, 8, "fp8_rows", "softmax_bias", bias_std=2.0,
+                        seed=15),
+    workloads.MoeConfig("fp8_rows_wide", 130, 256, 8, 2, 256, 128, 8, "fp8_rows", "softmax_bias", bias_std=2.0,
+                        seed=16),
+    workloads.MoeConfig("fp8_rows_narrow", 1, 1024, 16, 4, 256, 128, 8, "fp8_rows", "softmax", seed=17),
 ]
 
 
@@ -473,7 +480,7 @@ def test_fused_layer_with_dropped_and_repeated_ids(moe):
 
 # ---------------------------------------------------- gated shared expert --
 
-@pytest.mark.parametrize("name", ["verify", "bf16_odd", "fp8_small", "bf16_narrow"])
+@pytest.mark.parametrize("name", ["verify", "bf16_odd", "fp8_small", "bf16_narrow", "fp8_rows_narrow"])
 def test_gated_shared_expert(moe, name):
     """The shared expert's output scaled by sigmoid(x . g): parity with the
     oracle on both layouts (row-major: steps path; tiled: the single pass where
@@ -516,4 +523,24 @@ def test_narrow_width_kernel(moe, m):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     ref = oracle_layer(model, x, ids, w)
     ok, err, bound = tolerance_ok(bf16_to_np(a), ref["out"])
+    assert ok, (err, bound)
+
+
+# ------------------------------------------------------ FP8 row scales --
+
+@pytest.mark.parametrize("name", ["fp8_rows_small", "fp8_rows_narrow"])
+def test_row_scales_single_pass(moe, name):
+    """FP8 with one scale per weight row through the single-pass layer (tiled
+    weights; the narrow case on its 8-wave kernel): tables bit-exact, output
+    within tolerance of the oracle."""
+    cfg = next(c for c in ODD if c.name == name)
+    model = DeviceModel(cfg, threads=4)
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    assert model.tiled_layer().wdt == moe.MOE_W_FP8_E4M3_ROWS_TILED
+    log(f"row-scale single pass: {cfg}")
+    out, views = _run_layer(moe, model, xt, it, wt, tiled=True)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
     assert ok, (err, bound)
