@@ -15,9 +15,11 @@ remainder) for exactly K steps, bracketed by device syncs.
 
 Printed (one JSON line): layer rows/s (the value), weight-stream GB/s and its
 fraction of the 8 TB/s HBM peak, per-kernel times from HIP events, the
-roofline of the dominant kernel (gate+up), the align latency on the
-prefill-scale align workload (n = 32768 int64 ids, 256 experts, BS 64), and the
-float64 CPU oracle timed on the host as a reference baseline.
+roofline of the dominant kernel (the single-pass layer kernel: align, gate+up
++SiLU and the down slices), the align latency on the prefill-scale align
+workload (n = 32768 int64 ids, 256 experts, BS 64), the router latency, the
+plain streaming-read ceiling for the same bytes, and the float64 CPU oracle
+timed on the host as a reference baseline (24 seeded decode routings).
 """
 
 from __future__ import annotations
@@ -52,7 +54,8 @@ def parse():
     ap.add_argument("--breakdown-reps", type=int, default=25)
     ap.add_argument("--other-configs", default="",
                     help="comma-separated workloads (tiny, verify, large, or decode_mN: the decode layer at "
-                         "N tokens) also timed whole-layer and reported "
+                         "N tokens; a _rows suffix: the same with per-row FP8 scales) also timed whole-layer and "
+                         "reported "
                          "under other_configs (context for the headline, not the headline)")
     ap.add_argument("--only-config", default="",
                     help="time one other workload (tiny, verify or large) alone and print its line; for profiling")
@@ -135,10 +138,13 @@ def measure_config(name, dev, steps=50):
     import workloads
     from workloads.device import DeviceWeights
 
-    if name.startswith("decode_m"):  # the decode layer at a narrower width: decode_m1, decode_m2, ...
-        cfg = workloads.CONFIGS["decode"].replace(M=int(name[len("decode_m"):]), name=name)
+    base, rows = (name[:-len("_rows")], True) if name.endswith("_rows") else (name, False)
+    if base.startswith("decode_m"):  # the decode layer at a narrower width: decode_m1, decode_m2, ...
+        cfg = workloads.CONFIGS["decode"].replace(M=int(base[len("decode_m"):]), name=name)
     else:
-        cfg = workloads.CONFIGS[name]
+        cfg = workloads.CONFIGS[base]
+    if rows:  # the same layer with FP8 weights scaled per row instead of per 128x128 block
+        cfg = cfg.replace(wdt="fp8_rows", name=name)
     G = 2 if cfg.E * cfg.I * cfg.H > (1 << 31) else 4  # the large workload: 2 copies of its 11 GB
     log(f"other config {name}: generating weights, {G} copies")
     w0 = DeviceWeights(cfg, device=dev, threads=16)
@@ -158,8 +164,12 @@ def measure_config(name, dev, steps=50):
     wss = [layers[i].alloc_workspace(cfg.M) for i in range(G)]
     sh_bytes = 0
     if cfg.S:
-        esz = 1 if cfg.wdt == "fp8" else 2
-        sh_bytes = 3 * cfg.S * cfg.H * esz + (3 * (cfg.S // 128) * (cfg.H // 128) * 4 if cfg.wdt == "fp8" else 0)
+        esz = 1 if cfg.wdt in ("fp8", "fp8_rows") else 2
+        sh_bytes = 3 * cfg.S * cfg.H * esz
+        if cfg.wdt == "fp8":
+            sh_bytes += 3 * (cfg.S // 128) * (cfg.H // 128) * 4
+        elif cfg.wdt == "fp8_rows":
+            sh_bytes += (2 * cfg.S + cfg.H) * 4
     per = [w0.algorithmic_bytes(ids)["total"] for ids, _ in routings]
     stream = torch.cuda.Stream(device=dev)
     multi = graph_of(lambda: [layers[i].forward(xt, ids_d[i], w_d[i], out=outs[i], workspace=wss[i])
@@ -178,6 +188,9 @@ def measure_config(name, dev, steps=50):
     del layers, wss, outs, w0
     torch.cuda.empty_cache()
     return res
+
+
+CPU_ROUTINGS = 24  # decode routings in the CPU baseline sample (8 rows each)
 
 
 def cpu_baseline(cfg, routings):
@@ -455,7 +468,9 @@ def main():
         result["other_configs"] = {name: measure_config(name, dev) for name in args.other_configs.split(",") if name}
     if not args.no_cpu_baseline:
         log("cpu baseline: float64 oracle")
-        result["cpu_baseline"] = cpu_baseline(cfg, routings)
+        # the timed routings plus more seeded ones of the same recipe: about 10 s of oracle work
+        extra = [workloads.routing(cfg.replace(seed=cfg.seed + r)) for r in range(len(routings), CPU_ROUTINGS)]
+        result["cpu_baseline"] = cpu_baseline(cfg, list(routings) + extra)
     print(json.dumps(result))
 
 
