@@ -544,3 +544,23 @@ def test_row_scales_single_pass(moe, name):
     compare_tables(views, ref["tables"])
     ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
     assert ok, (err, bound)
+
+
+@pytest.mark.parametrize("name", ["decode", "verify"])
+def test_row_scales_full_size(moe, name):
+    """The decode and verify layers at full size with per-row FP8 scales:
+    row-major weights (the steps path) against the oracle, tables bit-exact,
+    and tiled weights (decode: the single pass) with the same bits."""
+    cfg = workloads.CONFIGS[name].replace(wdt="fp8_rows", name=name + "_rows")
+    log(f"row-scale full size: {cfg}")
+    model = DeviceModel(cfg, threads=16)
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    out, views = _run_layer(moe, model, xt, it, wt)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    log(f"  out: max err {err:.3e} bound {bound:.3e}")
+    assert ok, (err, bound)
+    tiled, _ = _run_layer(moe, model, xt, it, wt, tiled=True)
+    assert (model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS) == (name == "decode")
+    assert torch.equal(tiled.view(torch.int16), out.view(torch.int16))
