@@ -48,6 +48,10 @@ ADVERSARIAL = [
     ("below_blocks_4095", lambda r: r.integers(0, 64, size=(4095, 1)), 64, 16),
     ("blocks_ragged_tail", lambda r: r.integers(-2, 40, size=(2047, 3)), 37, 5),
     ("blocks_bs1", lambda r: r.integers(0, 200, size=(3000, 4)), 200, 1),
+    ("blocks_65536", lambda r: r.integers(-1, 300, size=(8192, 8)), 300, 16),
+    ("blocks_1024_experts_20000", lambda r: r.integers(0, 1024, size=(2500, 8)), 1024, 4),
+    ("blocks_65537_ragged", lambda r: r.integers(0, 256, size=(65537, 1)), 256, 64),
+    ("blocks_skewed_72000", lambda r: np.minimum(r.geometric(0.02, size=(9000, 8)), 255), 256, 64),
 ]
 
 
