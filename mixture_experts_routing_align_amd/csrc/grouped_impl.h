@@ -572,27 +572,17 @@ template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED, 
 hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   auto kern = grouped_kernel<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, FUSED, IdT>;
   const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
-  static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
-  if (lds > 64 * 1024 && lds > configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    configured = lds;
-  }
+  static std::atomic<size_t> allowed[kMaxCachedDevices];
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, allowed);
+  if (e != hipSuccess) return e;
   // column tiles per workgroup: the fewest that let every workgroup of the
   // worst case (every item busy) be resident at once, but at most
   // kMaxTilesPerGroup, so a wide grid (many experts, large M) keeps its
   // parallelism instead of serialising the columns inside few workgroups
-  static size_t occ_lds = (size_t)-1;  // occupancy of this kernel at the last LDS size asked
-  static int occ_per_cu = 0;
-  if (occ_lds != lds) {
-    int per_cu = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
-                                                                      kThreads, lds);
-    if (e != hipSuccess) return e;
-    occ_per_cu = per_cu;
-    occ_lds = lds;
-  }
+  static std::atomic<uint64_t> occupancy[kMaxCachedDevices];
+  int occ_per_cu = 0;
+  e = occupancy_per_cu(reinterpret_cast<const void*>(kern), kThreads, lds, occupancy, occ_per_cu);
+  if (e != hipSuccess) return e;
   const int slots = std::max(1, occ_per_cu) * device_cus();
   // (the shared and routed items may have different column counts: `tiles` is the larger)
   const int items = a.sgroups + a.items;

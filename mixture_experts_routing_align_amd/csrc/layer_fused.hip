@@ -602,13 +602,9 @@ hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
   const size_t xs = x_lds_bytes(rowcap, a.H);
   const size_t ab = act_lds_bytes(rowcap, W == 2 * kColTiles) + (ROWS ? (size_t)a.H * 4 : 0);
   const size_t lds = xs + ab + align_lds_bytes(a.E, a.n, W);
-  static size_t configured = 0;  // dynamic LDS above 64 KB must be allowed once per kernel
-  if (lds > 64 * 1024 && lds > configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    configured = lds;
-  }
+  static std::atomic<size_t> allowed[kMaxCachedDevices];
+  const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, allowed);
+  if (e != hipSuccess) return e;
   const int nsl = (a.I + kSlice - 1) / kSlice;
   const int nssl = a.sw[0] != nullptr ? (a.S + kSlice - 1) / kSlice : 0;
   const int groups = a.sw[0] != nullptr ? (a.M + rowcap - 1) / rowcap : 0;

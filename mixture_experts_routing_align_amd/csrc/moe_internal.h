@@ -4,11 +4,62 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_runtime_api.h>
 
 #include "moe_mi355x.h"
 
 namespace moe {
+
+// ---- host-side launch helpers (caches kept per device, safe across threads)
+constexpr int kMaxCachedDevices = 64;
+
+// The current device, or -1 when it cannot be cached (the helpers then ask HIP every time).
+inline int cached_device() {
+  int d = 0;
+  return hipGetDevice(&d) == hipSuccess && d >= 0 && d < kMaxCachedDevices ? d : -1;
+}
+
+// Dynamic LDS above 64 KB per workgroup must be allowed per kernel and device.
+// `allowed` (one array per kernel) holds the largest size allowed so far on each
+// device; the attribute only ever grows, so concurrent launchers never shrink
+// it under one another.
+inline hipError_t allow_dynamic_lds(const void* kern, size_t lds, std::atomic<size_t> (&allowed)[kMaxCachedDevices]) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  const int dev = cached_device();
+  if (dev < 0) return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds <= allowed[dev].load(std::memory_order_acquire)) return hipSuccess;
+  static std::mutex m;
+  std::lock_guard<std::mutex> g(m);
+  if (lds <= allowed[dev].load(std::memory_order_relaxed)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) allowed[dev].store(lds, std::memory_order_release);
+  return e;
+}
+
+// Workgroups of `kern` one compute unit holds at `lds` bytes of dynamic LDS on
+// the current device; `cache` (one array per kernel) keeps the last size asked
+// and its answer per device, packed in one word.
+inline hipError_t occupancy_per_cu(const void* kern, int threads, size_t lds,
+                                   std::atomic<uint64_t> (&cache)[kMaxCachedDevices], int& per_cu) {
+  const int dev = cached_device();
+  const uint64_t key = ((uint64_t)lds + 1) << 16;
+  if (dev >= 0) {
+    const uint64_t v = cache[dev].load(std::memory_order_relaxed);
+    if ((v & ~(uint64_t)0xffff) == key) {
+      per_cu = (int)(v & 0xffff);
+      return hipSuccess;
+    }
+  }
+  int n = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, threads, lds);
+  if (e != hipSuccess) return e;
+  if (dev >= 0) cache[dev].store(key | (uint64_t)(n & 0xffff), std::memory_order_relaxed);
+  per_cu = n;
+  return hipSuccess;
+}
 
 constexpr int kFp8Block = 128;   // FP8 scale block edge (both N and K)
 
