@@ -41,6 +41,12 @@
  *     weights take no scale.
  *   - Activations x are bf16 [M, H]; intermediates are float32; the output is
  *     bf16 [M, H], one round-to-nearest-even of the float32 blend sum.
+ *   - Alignment: the kernels move weights (tiled or row-major), x, the router
+ *     weight, act, sh_act, expert_out and sh_out 16 bytes per lane, and the
+ *     bf16 output 8 bytes per lane.  Those pointers must be 16-byte (output:
+ *     8-byte) aligned; any other is refused with MOE_ERR_SHAPE before any
+ *     launch.  Ids, routing weights, block scales and the shared-expert gate
+ *     vector need only their element alignment.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

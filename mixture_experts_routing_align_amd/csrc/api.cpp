@@ -76,8 +76,19 @@ bool is_tiled(moe_weight_dtype wdt) {
   return wdt == MOE_W_BF16_TILED || wdt == MOE_W_FP8_E4M3_TILED || wdt == MOE_W_FP8_E4M3_ROWS_TILED;
 }
 
+// The kernels move weights, x, act and the float32 intermediates 16 bytes per
+// lane and the bf16 output 8 bytes per lane: a pointer off that alignment is
+// refused (NULL is checked elsewhere).
+int check_aligned(const char* fn, const char* what, const void* p, uintptr_t bytes) {
+  if (p != nullptr && reinterpret_cast<uintptr_t>(p) % bytes)
+    return fail(MOE_ERR_SHAPE, "%s: %s is not %d-byte aligned", fn, what, (int)bytes);
+  return MOE_OK;
+}
+
 int check_weight(const char* fn, const char* name, const moe_weight* w, moe_weight_dtype wdt) {
   if (w == nullptr || w->w == nullptr) return fail(MOE_ERR_NULL, "%s: %s weights are NULL", fn, name);
+  if (reinterpret_cast<uintptr_t>(w->w) % 16)
+    return fail(MOE_ERR_SHAPE, "%s: %s weights are not 16-byte aligned", fn, name);
   if (is_fp8(wdt) && w->scale == nullptr) return fail(MOE_ERR_NULL, "%s: %s FP8 scales are NULL", fn, name);
   // per-row scales are read four rows at a time
   if (is_rows(wdt) && reinterpret_cast<uintptr_t>(w->scale) % 16)
@@ -252,6 +263,9 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
   if (S > 0 && (rc = check_projection(fn, "shared gate/up", wdt, S, H))) return rc;
   if (M == 0) return MOE_OK;
   if (x_bf16 == nullptr || act == nullptr) return fail(MOE_ERR_NULL, "%s: x or act is NULL", fn);
+  if ((rc = check_aligned(fn, "x", x_bf16, 16)) || (rc = check_aligned(fn, "act", act, 16)) ||
+      (rc = check_aligned(fn, "sh_act", sh_act, 16)))
+    return rc;
   if ((rc = check_weight(fn, "gate", gate, wdt)) || (rc = check_weight(fn, "up", up, wdt))) return rc;
   if ((rc = check_tables(fn, t, false))) return rc;
   if (S > 0) {
@@ -286,6 +300,9 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
   if (M == 0) return MOE_OK;
   if (topk_ids == nullptr || x_bf16 == nullptr || act == nullptr)
     return fail(MOE_ERR_NULL, "%s: topk_ids, x or act is NULL", fn);
+  if ((rc = check_aligned(fn, "x", x_bf16, 16)) || (rc = check_aligned(fn, "act", act, 16)) ||
+      (rc = check_aligned(fn, "sh_act", sh_act, 16)))
+    return rc;
   if ((rc = check_weight(fn, "gate", gate, wdt)) || (rc = check_weight(fn, "up", up, wdt))) return rc;
   if ((rc = check_tables(fn, t, true))) return rc;
   if (S > 0) {
@@ -319,6 +336,9 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
   if (S > 0 && (rc = check_projection(fn, "shared down", wdt, H, S))) return rc;
   if (M == 0) return MOE_OK;
   if (act == nullptr || expert_out == nullptr) return fail(MOE_ERR_NULL, "%s: act or expert_out is NULL", fn);
+  if ((rc = check_aligned(fn, "act", act, 16)) || (rc = check_aligned(fn, "expert_out", expert_out, 16)) ||
+      (rc = check_aligned(fn, "sh_act", sh_act, 16)) || (rc = check_aligned(fn, "sh_out", sh_out, 16)))
+    return rc;
   if ((rc = check_weight(fn, "down", down, wdt))) return rc;
   if ((rc = check_tables(fn, t, false))) return rc;
   if (S > 0) {
@@ -361,6 +381,10 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
   if (!out_bf16 || !expert_out || !topk_weights || !token_to_perm)
     return fail(MOE_ERR_NULL, "%s: a required pointer is NULL", fn);
   if (sh_out && sh_expert_gate && !x_bf16) return fail(MOE_ERR_NULL, "%s: x is NULL with a shared gate", fn);
+  int rc;
+  if ((rc = check_aligned(fn, "out", out_bf16, 8)) || (rc = check_aligned(fn, "expert_out", expert_out, 16)) ||
+      (rc = check_aligned(fn, "sh_out", sh_out, 16)))
+    return rc;
   return hip_status(moe::launch_blend(static_cast<uint16_t*>(out_bf16), expert_out, topk_weights, token_to_perm,
                                       sh_out, x_bf16, sh_out ? sh_expert_gate : nullptr, (int)M, H, top_k, stream),
                     fn);
@@ -385,6 +409,8 @@ int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E
   if (moe_tiled_weight_bytes(wdt, E, N, K) == 0) return MOE_ERR_SHAPE;
   if (src == nullptr || dst == nullptr) return fail(MOE_ERR_NULL, "%s: src or dst is NULL", fn);
   if (src == dst) return fail(MOE_ERR_SHAPE, "%s: src and dst must not alias", fn);
+  int rc;
+  if ((rc = check_aligned(fn, "src", src, 16)) || (rc = check_aligned(fn, "dst", dst, 16))) return rc;
   return hip_status(moe::launch_tile_weights(src, dst, is_fp8(wdt), E, N, K, stream), fn);
 }
 
@@ -498,6 +524,7 @@ int moe_layer_partials(const moe_layer_desc* d, const void* x_bf16, const void* 
   if (path != MOE_LAYER_PATH_SINGLE_PASS)
     return fail(MOE_ERR_SHAPE, "%s: this layer shape does not take the single-pass path", fn);
   if (!x_bf16 || !topk_ids) return fail(MOE_ERR_NULL, "%s: x or topk_ids is NULL", fn);
+  if ((rc = check_aligned(fn, "x", x_bf16, 16))) return rc;
   const moe::FusedLayerArgs a =
       single_pass_args(d, static_cast<char*>(workspace), off, x_bf16, topk_ids, nullptr, nullptr);
   return hip_status(moe::launch_layer_partials(a, is_fp8(d->wdt), stream), fn);
@@ -516,6 +543,7 @@ int moe_layer_blend_partials(const moe_layer_desc* d, const void* x_bf16, const 
   if (!topk_ids || !topk_weights || !out_bf16)
     return fail(MOE_ERR_NULL, "%s: topk_ids, topk_weights or out is NULL", fn);
   if (d->sh_expert_gate && !x_bf16) return fail(MOE_ERR_NULL, "%s: x is NULL with a shared gate", fn);
+  if ((rc = check_aligned(fn, "out", out_bf16, 8))) return rc;
   const moe::FusedLayerArgs a = single_pass_args(d, static_cast<char*>(const_cast<void*>(workspace)), off, x_bf16,
                                                  topk_ids, topk_weights, out_bf16);
   return hip_status(moe::launch_blend_partials(a, stream), fn);
@@ -530,6 +558,7 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   if (rc || d->M == 0) return rc;
   if (!x_bf16 || !topk_ids || !topk_weights || !out_bf16)
     return fail(MOE_ERR_NULL, "%s: x, topk_ids, topk_weights or out is NULL", fn);
+  if ((rc = check_aligned(fn, "x", x_bf16, 16)) || (rc = check_aligned(fn, "out", out_bf16, 8))) return rc;
   char* ws = static_cast<char*>(workspace);
   if (path == MOE_LAYER_PATH_SINGLE_PASS) {
     const moe::FusedLayerArgs a = single_pass_args(d, ws, off, x_bf16, topk_ids, topk_weights, out_bf16);
@@ -592,6 +621,9 @@ int moe_router_topk(const void* x_bf16, const void* router_w_bf16, int64_t M, in
   if (M == 0) return MOE_OK;
   if (!x_bf16 || !router_w_bf16 || !logits || !topk_ids || !topk_weights)
     return fail(MOE_ERR_NULL, "%s: x, router weight, logits, topk_ids or topk_weights is NULL", fn);
+  int rc;
+  if ((rc = check_aligned(fn, "x", x_bf16, 16)) || (rc = check_aligned(fn, "router weight", router_w_bf16, 16)))
+    return rc;
   return hip_status(moe::launch_router(x_bf16, router_w_bf16, (int)M, H, E, top_k, logits, topk_ids,
                                        idt == MOE_IDX_I64, topk_weights, stream),
                     fn);

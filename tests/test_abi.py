@@ -309,3 +309,52 @@ def test_row_scaled_fp8_dtypes(lib):
     assert moe.weight_dtype((w3.to(torch.bfloat16), None)) == _ffi.MOE_W_BF16
     with pytest.raises(ValueError):
         moe._common_dtype((w3, torch.ones(4, 256)), (w3, torch.ones(4, 2, 1)))
+
+
+def test_misaligned_pointers_refused(lib):
+    """Every pointer the kernels move 16 bytes per lane (the bf16 output: 8) is
+    refused off that alignment, before any launch."""
+    t = _tables()
+    g, u = _w(), _w()
+    odd = FAKE + 8    # 8-byte but not 16-byte aligned
+    odder = FAKE + 4  # not 8-byte aligned
+
+    def refused(rc, what, bytes_=16):
+        msg = _err(lib)
+        assert rc == _ffi.MOE_ERR_SHAPE and what in msg and f"{bytes_}-byte" in msg, (rc, msg)
+
+    def gu(x=FAKE, act=FAKE, w=None):
+        return lib.moe_grouped_gate_up_silu(x, 1, ctypes.byref(w or g), ctypes.byref(u), ctypes.byref(t), act,
+                                            None, None, None, 4, 256, 128, 0, 8, 2, 16, None)
+
+    refused(gu(x=odd), "x")
+    refused(gu(act=odd), "act")
+    refused(gu(w=_ffi.MoeWeight(odd, FAKE)), "gate weights")
+    refused(lib.moe_align_gate_up_silu(FAKE, 1, odd, 1, ctypes.byref(g), ctypes.byref(u), ctypes.byref(t), FAKE,
+                                       None, None, None, 4, 256, 128, 0, 8, 2, 16, None), "x")
+    d = _w()
+    refused(lib.moe_grouped_down(odd, 1, ctypes.byref(d), ctypes.byref(t), FAKE, None, None, None,
+                                 4, 256, 128, 0, 8, 2, 16, None), "act")
+    refused(lib.moe_grouped_down(FAKE, 1, ctypes.byref(d), ctypes.byref(t), odd, None, None, None,
+                                 4, 256, 128, 0, 8, 2, 16, None), "expert_out")
+    refused(lib.moe_blend(odder, FAKE, FAKE, FAKE, None, None, None, 4, 8, 2, None), "out", 8)
+    refused(lib.moe_blend(FAKE, odd, FAKE, FAKE, None, None, None, 4, 8, 2, None), "expert_out")
+    refused(lib.moe_blend(FAKE, FAKE, FAKE, FAKE, odd, None, None, 4, 8, 2, None), "sh_out")
+
+    desc = _desc()
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(desc))
+    refused(lib.moe_layer_forward(ctypes.byref(desc), odd, FAKE, FAKE, FAKE, 0x100000, need, None), "x")
+    refused(lib.moe_layer_forward(ctypes.byref(desc), FAKE, FAKE, FAKE, odder, 0x100000, need, None), "out", 8)
+    wodd = _desc()
+    wodd.down = _ffi.MoeWeight(odd, FAKE)
+    refused(lib.moe_layer_forward(ctypes.byref(wodd), FAKE, FAKE, FAKE, FAKE, 0x100000, need, None), "down weights")
+    single = _tiled(_desc())
+    need1 = lib.moe_layer_workspace_bytes(ctypes.byref(single))
+    assert lib.moe_layer_path(ctypes.byref(single)) == _ffi.MOE_LAYER_PATH_SINGLE_PASS
+    refused(lib.moe_layer_partials(ctypes.byref(single), odd, FAKE, 0x100000, need1, None), "x")
+    refused(lib.moe_layer_blend_partials(ctypes.byref(single), FAKE, FAKE, FAKE, odder, 0x100000, need1, None),
+            "out", 8)
+    refused(lib.moe_tile_weights(odd, FAKE, 1, 2, 256, 128, None), "src")
+    refused(lib.moe_tile_weights(FAKE, odd, 1, 2, 256, 128, None), "dst")
+    refused(lib.moe_router_topk(odd, FAKE, 8, 2048, 128, 8, FAKE, FAKE, 1, FAKE, None), "x")
+    refused(lib.moe_router_topk(FAKE, odd, 8, 2048, 128, 8, FAKE, FAKE, 1, FAKE, None), "router weight")
