@@ -167,47 +167,98 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_blocks(int n, int G,
 
 // launch 3: the stable scatter of the block's slots from its bases; besides,
 // wave w of block b writes the padding sentinels and block owners of experts
-// b + G * (w + kBlockWaves * i), lanes over consecutive entries
+// b + G * (w + kBlockWaves * i), lanes over consecutive entries.  Everything
+// the block reads (its bases, its ids, the first padded expert's offsets and
+// count) is requested before any of it is used, and the ids stay in registers
+// from the count to the scatter.
+constexpr int kScatterChunks = (2 * kChunk / kBlockWaves + 63) / 64;  // 64-slot chunks of a wave (the last block's too)
 template <typename IdT>
 __global__ __launch_bounds__(kBlockThreads) void align_scatter_blocks(const IdT* __restrict__ ids, int n, int G, int E,
                                                                      int BS, int nbits, AlignOut o) {
   __shared__ int cnt[kBlockWaves * kMaxExperts];
   __shared__ int base[kMaxExperts];
+  constexpr int kBaseLoads = kMaxExperts / kBlockThreads;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int lo, hi;
   block_range(n, G, lo, hi);
-  for (int e = threadIdx.x; e < E; e += kBlockThreads) base[e] = o.token_to_perm[lo + e];
-  block_counts(ids, lo, hi, E, nbits, cnt);  // its first barrier: every base is read before any slot is written
-  for (int e = threadIdx.x; e < E; e += kBlockThreads) {
+  const int per = (((hi - lo + kBlockWaves - 1) / kBlockWaves) + 63) & ~63;
+  const int beg = min(hi, lo + w * per), end = min(hi, beg + per);
+
+  int bv[kBaseLoads];
+#pragma unroll
+  for (int u = 0; u < kBaseLoads; ++u) {
+    const int e = u * kBlockThreads + tid;
+    bv[u] = e < E ? o.token_to_perm[lo + e] : 0;
+  }
+  IdT iv[kScatterChunks];
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) iv[c] = beg + 64 * c < end ? ids[min(beg + 64 * c + lane, end - 1)] : (IdT)-1;
+  const int e_first = blockIdx.x + G * w;  // the first expert whose padding this wave writes
+  int f_lo = 0, f_hi = 0, f_cnt = 0;
+  if (e_first < E) {
+    f_lo = o.expert_offsets[e_first];
+    f_hi = o.expert_offsets[e_first + 1];
+    f_cnt = o.expert_counts[e_first];
+  }
+
+#pragma unroll
+  for (int u = 0; u < kBaseLoads; ++u) {
+    const int e = u * kBlockThreads + tid;
+    if (e < E) base[e] = bv[u];
+  }
+  for (int i = tid; i < kBlockWaves * E; i += kBlockThreads) cnt[i] = 0;
+  __syncthreads();  // every base is read (above) before any slot is written
+  int* my = cnt + w * E;
+  auto id_of = [&](int c, bool& valid) -> int {
+    const IdT v = iv[c];
+    valid = beg + 64 * c + lane < end && v >= 0 && v < (IdT)E;
+    return valid ? (int)v : -1;
+  };
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) {
+    if (beg + 64 * c < end) {  // wave-uniform
+      bool valid;
+      const int id = id_of(c, valid);
+      const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+      if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kBlockThreads) {
     int run = base[e];
-    for (int w = 0; w < kBlockWaves; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = run;
+    for (int k = 0; k < kBlockWaves; ++k) {
+      const int c = cnt[k * E + e];
+      cnt[k * E + e] = run;
       run += c;
     }
   }
   __syncthreads();
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (((hi - lo + kBlockWaves - 1) / kBlockWaves) + 63) & ~63;
-  const int beg = min(hi, lo + w * per), end = min(hi, beg + per);
-  int* my = cnt + w * E;
-  for (int c = beg; c < end; c += 64) {
-    const int i = c + lane;
-    bool valid;
-    const int id = align_dev::load_id(ids, i, end, E, valid);
-    const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
-    if (valid) {
-      const int pos = my[id] + __popcll(m & align_dev::lanes_below(lane));
-      o.sorted_token_ids[pos] = i;
-      o.token_to_perm[i] = pos;
-    } else if (i < end) {
-      o.token_to_perm[i] = -1;
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) {
+    if (beg + 64 * c < end) {  // wave-uniform
+      const int i = beg + 64 * c + lane;
+      bool valid;
+      const int id = id_of(c, valid);
+      const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+      if (valid) {
+        const int pos = my[id] + __popcll(m & align_dev::lanes_below(lane));
+        o.sorted_token_ids[pos] = i;
+        o.token_to_perm[i] = pos;
+      } else if (i < end) {
+        o.token_to_perm[i] = -1;
+      }
+      // every lane has read its base above (a wave's LDS operations run in order)
+      if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
     }
-    // every lane has read its base above (a wave's LDS operations run in order)
-    if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
   }
-  for (int e = blockIdx.x + G * w; e < E; e += G * kBlockWaves) {
-    const int e_lo = o.expert_offsets[e], e_hi = o.expert_offsets[e + 1];
-    for (int p = e_lo + o.expert_counts[e] + lane; p < e_hi; p += 64) o.sorted_token_ids[p] = n;
+  for (int e = e_first; e < E; e += G * kBlockWaves) {
+    int e_lo = f_lo, e_hi = f_hi, e_cnt = f_cnt;
+    if (e != e_first) {
+      e_lo = o.expert_offsets[e];
+      e_hi = o.expert_offsets[e + 1];
+      e_cnt = o.expert_counts[e];
+    }
+    for (int p = e_lo + e_cnt + lane; p < e_hi; p += 64) o.sorted_token_ids[p] = n;
     for (int b = e_lo / BS + lane; b < e_hi / BS; b += 64) o.block_expert_ids[b] = e;
   }
 }
