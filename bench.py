@@ -322,10 +322,16 @@ def main():
     aids, _ = workloads.routing(acfg)
     aids_d = torch.from_numpy(aids).to(dev)
     atab = moe.AlignTables.allocate(acfg.M, acfg.top_k, acfg.E, acfg.BS, dev)
+    awork = torch.empty(max(moe.moe_align_workspace_bytes(acfg.M, acfg.top_k, acfg.E), 16) // 4,
+                        dtype=torch.int32, device=dev)
     # AR aligns back to back in one graph; HIP events on the replay stream
-    # bracket 10 replays, so the time per align carries no graph-launch cost
+    # bracket 10 replays, so the time per align carries no graph-launch cost.
+    # moe_align_ws (count, then scan + scatter: two launches) is the align the
+    # layer runs at this size; moe_align (three launches, no workspace) beside it
     AR = 20
-    ag = graph_of(lambda: [moe.moe_align(aids_d, acfg.E, acfg.BS, atab, stream=stream) for _ in range(AR)], stream)
+    ag = graph_of(lambda: [moe.moe_align_ws(aids_d, acfg.E, acfg.BS, awork, atab, stream=stream)
+                           for _ in range(AR)], stream)
+    ag3 = graph_of(lambda: [moe.moe_align(aids_d, acfg.E, acfg.BS, atab, stream=stream) for _ in range(AR)], stream)
     z = torch.zeros(1, device=dev)
     fg = graph_of(lambda: [z.add_(1.0) for _ in range(AR)], stream)
 
@@ -341,13 +347,14 @@ def main():
         return ev0.elapsed_time(ev1) * 1e3 / (reps * AR)
 
     align_us = per_call_us(ag)
+    align3_us = per_call_us(ag3)
     floor_us = per_call_us(fg)
     areps = 200
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         ev0.record(stream)
         for _ in range(areps):
-            moe.moe_align(aids_d, acfg.E, acfg.BS, atab, stream=stream)
+            moe.moe_align_ws(aids_d, acfg.E, acfg.BS, awork, atab, stream=stream)
         ev1.record(stream)
     ev1.synchronize()
     align_ev_us = ev0.elapsed_time(ev1) * 1e3 / areps
@@ -457,7 +464,10 @@ def main():
         },
         "align_us": align_us,
         "align_us_events": align_ev_us,
-        "align_workload": "n = 4096 x 8 int64 ids, Zipf(1.1), 256 experts, BS 64 (20 aligns per graph, HIP events)",
+        "align_us_tables_only": align3_us,
+        "align_workload": "n = 4096 x 8 int64 ids, Zipf(1.1), 256 experts, BS 64 (20 aligns per graph, HIP events); "
+                          "align_us: moe_align_ws (count + scan/scatter, 2 launches, 32 KB workspace); "
+                          "align_us_tables_only: moe_align (count, scan, scatter: 3 launches)",
         "launch_floor_us": floor_us,
         "router_us": router_us,
         "router_workload": "M=8 tokens, H=2048, E=128 bf16 gate, top-8 (logits GEMV + top-k softmax, 2 launches; "

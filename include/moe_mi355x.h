@@ -144,6 +144,27 @@ typedef struct {
 int moe_align(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k,
               int32_t E, int32_t BS, const moe_align_tables* out, hipStream_t stream);
 
+/* Bytes of device workspace moe_align_ws needs for n = M*top_k slots over E
+ * experts: 4*E per block of 1024 slots from 4096 slots on, else 0 (also 0 for
+ * arguments moe_align would refuse). */
+size_t moe_align_workspace_bytes(int64_t M, int32_t top_k, int32_t E);
+
+/* moe_align with a caller-owned workspace for the per-block expert counts
+ * (`workspace_bytes` >= moe_align_workspace_bytes(M, top_k, E), 16-byte
+ * aligned; it may be NULL when that size is 0).  Without it the counts of the
+ * blocks of 1024 slots must live in token_to_perm until the scatter overwrites
+ * them, which takes three launches (count, one-workgroup scan, scatter); with
+ * it, two: count, then a scatter in which every block forms the offsets and its
+ * own bases from all blocks' counts.  The tables are bit-identical to
+ * moe_align's (the same stable order; still no atomics), and the workspace
+ * holds nothing after the call that the caller needs.  Below 4096 slots this
+ * is moe_align (one workgroup).  Errors as for moe_align, plus MOE_ERR_NULL
+ * (workspace NULL when needed), MOE_ERR_WORKSPACE (too small), MOE_ERR_SHAPE
+ * (misaligned). */
+int moe_align_ws(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k,
+                 int32_t E, int32_t BS, const moe_align_tables* out, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------- weight tiling --
  * A one-time, load-time reordering of an expert weight tensor (the source pages
  * describe such a load-time repack for their lean tensor-core kernels:

@@ -131,9 +131,16 @@ class AlignTables:
         return MoeAlignTables(*[getattr(self, f).data_ptr() for f in TABLE_FIELDS])
 
 
+def moe_align_workspace_bytes(M: int, top_k: int, E: int) -> int:
+    """Bytes of workspace moe_align takes for its two-launch form (0: none needed)."""
+    return int(lib().moe_align_workspace_bytes(M, top_k, E))
+
+
 def moe_align(topk_ids: torch.Tensor, E: int, BS: int, tables: Optional[AlignTables] = None,
-              stream=None) -> AlignTables:
-    """Align the [M, top_k] ids (int32 or int64, device); returns the tables."""
+              stream=None, workspace: Optional[torch.Tensor] = None) -> AlignTables:
+    """Align the [M, top_k] ids (int32 or int64, device); returns the tables.
+    With `workspace` (a device buffer of at least moe_align_workspace_bytes
+    bytes) the C call is moe_align_ws, else moe_align; the tables are the same."""
     _need(topk_ids.dim() == 2 and topk_ids.is_contiguous(), "topk_ids must be a contiguous [M, top_k] tensor")
     _need(topk_ids.dtype in (torch.int32, torch.int64), "topk_ids must be int32 or int64")
     M, top_k = topk_ids.shape
@@ -141,8 +148,19 @@ def moe_align(topk_ids: torch.Tensor, E: int, BS: int, tables: Optional[AlignTab
         tables = AlignTables.allocate(M, top_k, E, BS, topk_ids.device)
     idt = MOE_IDX_I64 if topk_ids.dtype == torch.int64 else MOE_IDX_I32
     c = tables.as_c()
-    _check(lib().moe_align(topk_ids.data_ptr(), idt, M, top_k, E, BS, ctypes.byref(c), _stream(stream)))
+    if workspace is None:
+        _check(lib().moe_align(topk_ids.data_ptr(), idt, M, top_k, E, BS, ctypes.byref(c), _stream(stream)))
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(lib().moe_align_ws(topk_ids.data_ptr(), idt, M, top_k, E, BS, ctypes.byref(c), workspace.data_ptr(),
+                                  nbytes, _stream(stream)))
     return tables
+
+
+def moe_align_ws(topk_ids: torch.Tensor, E: int, BS: int, workspace: torch.Tensor,
+                 tables: Optional[AlignTables] = None, stream=None) -> AlignTables:
+    """moe_align with a workspace for its blocks' counts (two launches instead of three)."""
+    return moe_align(topk_ids, E, BS, tables=tables, stream=stream, workspace=workspace)
 
 
 # ------------------------------------------------------------ grouped FFN --

@@ -68,6 +68,9 @@ SIGNATURES = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_abi_version": (c_int32, []),
     "moe_align": (c_int, [c_void_p, c_int, c_int64, c_int32, c_int32, c_int32, P(MoeAlignTables), c_void_p]),
+    "moe_align_workspace_bytes": (c_size_t, [c_int64, c_int32, c_int32]),
+    "moe_align_ws": (c_int, [c_void_p, c_int, c_int64, c_int32, c_int32, c_int32, P(MoeAlignTables), c_void_p,
+                             c_size_t, c_void_p]),
     "moe_grouped_gate_up_silu": (c_int, [c_void_p, c_int, P(MoeWeight), P(MoeWeight), P(MoeAlignTables),
                                          c_void_p, P(MoeWeight), P(MoeWeight), c_void_p, c_int64, c_int32,
                                          c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p]),

@@ -74,10 +74,12 @@ __device__ void block_counts(const IdT* __restrict__ ids, int lo, int hi, int E,
   __syncthreads();
 }
 
-// launch 1: the block's count of every expert -> token_to_perm[lo + e]
+// launch 1: the block's count of every expert -> dst[blockIdx.x * stride + e]
+// (token_to_perm[lo + e] with stride kChunk; a caller's workspace [G][E] with
+// stride E)
 template <typename IdT>
 __global__ __launch_bounds__(kBlockThreads) void align_count_blocks(const IdT* __restrict__ ids, int n, int G, int E,
-                                                                   int nbits, int32_t* token_to_perm) {
+                                                                   int nbits, int32_t* dst, int stride) {
   __shared__ int cnt[kBlockWaves * kMaxExperts];
   int lo, hi;
   block_range(n, G, lo, hi);
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(kBlockThreads) void align_count_blocks(const IdT* _
   for (int e = threadIdx.x; e < E; e += kBlockThreads) {
     int s = 0;
     for (int w = 0; w < kBlockWaves; ++w) s += cnt[w * E + e];
-    token_to_perm[lo + e] = s;
+    dst[(size_t)blockIdx.x * stride + e] = s;
   }
 }
 
@@ -263,6 +265,147 @@ __global__ __launch_bounds__(kBlockThreads) void align_scatter_blocks(const IdT*
   }
 }
 
+// ---- with a workspace for the block counts: two launches -----------------
+//
+// Launch 1 is align_count_blocks writing block b's counts to counts[b][e].
+// Launch 2: every block reads all G x E counts and forms the totals, padded
+// offsets and active list itself (the same block scan in every block), and its
+// own bases (each expert's offset plus the counts of the blocks before it);
+// then it counts and scatters its slots exactly as align_scatter_blocks does.
+// Besides, wave w of block b writes the padding of experts b + G * (w + 8 i),
+// the blocks share the tail past the total, and block 0 writes the counts,
+// offsets, active list and scalars.  The workspace only separates the counts
+// from the tables the scatter overwrites; nothing is shared in any other way.
+constexpr int kScanBatch = 16;                                           // block counts loaded together
+constexpr int kExpertsPerThread = (kMaxExperts + kBlockThreads - 1) / kBlockThreads;  // a thread's run of experts
+template <typename IdT>
+__global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const IdT* __restrict__ ids, int n, int G,
+                                                                          int E, int BS, int max_total, int cap,
+                                                                          int nbits, const int32_t* __restrict__ counts,
+                                                                          AlignOut o) {
+  __shared__ int cnt[kBlockWaves * kMaxExperts];
+  __shared__ int s_tot[kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_active[kMaxExperts];
+  __shared__ int s_wa[kBlockWaves], s_wb[kBlockWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.x;
+  int lo, hi;
+  block_range(n, G, lo, hi);
+  const int per = (((hi - lo + kBlockWaves - 1) / kBlockWaves) + 63) & ~63;
+  const int beg = min(hi, lo + w * per), end = min(hi, beg + per);
+
+  // the block's ids first (they do not depend on the counts)
+  IdT iv[kScatterChunks];
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) iv[c] = beg + 64 * c < end ? ids[min(beg + 64 * c + lane, end - 1)] : (IdT)-1;
+
+  // thread t owns experts [t * kExpertsPerThread, ...): all blocks' counts of
+  // each, summed in block order (and up to this block, for the base)
+  int tot[kExpertsPerThread], bef[kExpertsPerThread];
+  int sum_pad = 0, sum_act = 0;
+#pragma unroll
+  for (int k = 0; k < kExpertsPerThread; ++k) {
+    const int e = tid * kExpertsPerThread + k;
+    tot[k] = bef[k] = 0;
+    if (e < E) {
+      for (int c0 = 0; c0 < G; c0 += kScanBatch) {
+        int v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) v[j] = c0 + j < G ? counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+          if (c0 + j < b) bef[k] += v[j];
+          tot[k] += v[j];
+        }
+      }
+    }
+    sum_pad += (tot[k] + BS - 1) / BS * BS;
+    sum_act += tot[k] > 0 ? 1 : 0;
+  }
+  int ex_pad, ex_act, total, nact;
+  align_dev::block_scan2<kBlockWaves>(sum_pad, sum_act, s_wa, s_wb, ex_pad, ex_act, total, nact);
+#pragma unroll
+  for (int k = 0; k < kExpertsPerThread; ++k) {
+    const int e = tid * kExpertsPerThread + k;
+    if (e < E) {
+      s_off[e] = ex_pad;
+      s_tot[e] = tot[k];
+      s_base[e] = ex_pad + bef[k];
+      if (tot[k] > 0) s_active[ex_act++] = e;
+      ex_pad += (tot[k] + BS - 1) / BS * BS;
+    }
+  }
+  if (tid == 0) s_off[E] = total;
+  for (int i = tid; i < kBlockWaves * E; i += kBlockThreads) cnt[i] = 0;
+  __syncthreads();
+
+  int* my = cnt + w * E;
+  auto id_of = [&](int c, bool& valid) -> int {
+    const IdT v = iv[c];
+    valid = beg + 64 * c + lane < end && v >= 0 && v < (IdT)E;
+    return valid ? (int)v : -1;
+  };
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) {
+    if (beg + 64 * c < end) {  // wave-uniform
+      bool valid;
+      const int id = id_of(c, valid);
+      const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+      if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kBlockThreads) {
+    int run = s_base[e];
+    for (int k = 0; k < kBlockWaves; ++k) {
+      const int c = cnt[k * E + e];
+      cnt[k * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) {
+    if (beg + 64 * c < end) {  // wave-uniform
+      const int i = beg + 64 * c + lane;
+      bool valid;
+      const int id = id_of(c, valid);
+      const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+      if (valid) {
+        const int pos = my[id] + __popcll(m & align_dev::lanes_below(lane));
+        o.sorted_token_ids[pos] = i;
+        o.token_to_perm[i] = pos;
+      } else if (i < end) {
+        o.token_to_perm[i] = -1;
+      }
+      // every lane has read its base above (a wave's LDS operations run in order)
+      if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
+    }
+  }
+  for (int e = b + G * w; e < E; e += G * kBlockWaves) {
+    const int e_lo = s_off[e], e_hi = s_off[e + 1];
+    for (int p = e_lo + s_tot[e] + lane; p < e_hi; p += 64) o.sorted_token_ids[p] = n;
+    for (int q = e_lo / BS + lane; q < e_hi / BS; q += 64) o.block_expert_ids[q] = e;
+  }
+  for (int p = total + b * kBlockThreads + tid; p < max_total; p += G * kBlockThreads) o.sorted_token_ids[p] = n;
+  for (int q = total / BS + b * kBlockThreads + tid; q < max_total / BS; q += G * kBlockThreads)
+    o.block_expert_ids[q] = -1;
+  if (b == 0) {
+    for (int e = tid; e < E; e += kBlockThreads) {
+      o.expert_counts[e] = s_tot[e];
+      o.expert_offsets[e] = s_off[e];
+    }
+    for (int j = tid; j < cap; j += kBlockThreads) o.active_experts[j] = j < nact ? s_active[j] : -1;
+    if (tid == 0) {
+      o.expert_offsets[E] = total;
+      *o.total = total;
+      *o.active_count = nact;
+    }
+  }
+}
+
 }  // namespace
 
 int align_blocks(int n) { return n >= kAlignBlocksMinSlots ? n / kChunk : 0; }
@@ -274,10 +417,10 @@ hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int m
   if (G > 0) {  // many slots: count, scan, scatter over G blocks
     if (ids64)
       hipLaunchKernelGGL(align_count_blocks<int64_t>, dim3(G), dim3(kBlockThreads), 0, s,
-                         static_cast<const int64_t*>(ids), n, G, E, nbits, o.token_to_perm);
+                         static_cast<const int64_t*>(ids), n, G, E, nbits, o.token_to_perm, kChunk);
     else
       hipLaunchKernelGGL(align_count_blocks<int32_t>, dim3(G), dim3(kBlockThreads), 0, s,
-                         static_cast<const int32_t*>(ids), n, G, E, nbits, o.token_to_perm);
+                         static_cast<const int32_t*>(ids), n, G, E, nbits, o.token_to_perm, kChunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(align_scan_blocks, dim3(1), dim3(kAlignThreads), 0, s, n, G, E, BS, max_total, cap, o);
@@ -297,6 +440,30 @@ hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int m
   else
     hipLaunchKernelGGL(align_kernel<int32_t>, dim3(1), dim3(kAlignThreads), 0, s,
                        static_cast<const int32_t*>(ids), n, E, BS, max_total, cap, nbits, o);
+  return hipGetLastError();
+}
+
+size_t align_workspace_bytes(int n, int E) { return (size_t)align_blocks(n) * E * sizeof(int32_t); }
+
+hipError_t launch_align_ws(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap, int32_t* ws,
+                           const AlignOut& o, hipStream_t s) {
+  const int G = align_blocks(n);
+  if (G == 0) return launch_align(ids, ids64, n, E, BS, max_total, cap, o, s);
+  const int nbits = align_dev::id_bits(E);
+  if (ids64)
+    hipLaunchKernelGGL(align_count_blocks<int64_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                       static_cast<const int64_t*>(ids), n, G, E, nbits, ws, E);
+  else
+    hipLaunchKernelGGL(align_count_blocks<int32_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                       static_cast<const int32_t*>(ids), n, G, E, nbits, ws, E);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ids64)
+    hipLaunchKernelGGL(align_scan_scatter_blocks<int64_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                       static_cast<const int64_t*>(ids), n, G, E, BS, max_total, cap, nbits, ws, o);
+  else
+    hipLaunchKernelGGL(align_scan_scatter_blocks<int32_t>, dim3(G), dim3(kBlockThreads), 0, s,
+                       static_cast<const int32_t*>(ids), n, G, E, BS, max_total, cap, nbits, ws, o);
   return hipGetLastError();
 }
 

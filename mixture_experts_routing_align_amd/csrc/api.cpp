@@ -217,7 +217,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 7; }
+int32_t moe_abi_version(void) { return 8; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -245,6 +245,35 @@ int moe_align(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_
   if ((rc = check_tables(fn, out, true))) return rc;
   return hip_status(moe::launch_align(topk_ids, idt == MOE_IDX_I64, (int)s.n, E, BS, (int)s.max_total,
                                       s.cap, to_align_out(*out), stream),
+                    fn);
+}
+
+size_t moe_align_workspace_bytes(int64_t M, int32_t top_k, int32_t E) {
+  AlignShape s;
+  if (check_routing_shape("moe_align_workspace_bytes", M, top_k, E, 1, &s)) return 0;
+  return moe::align_workspace_bytes((int)s.n, E);
+}
+
+int moe_align_ws(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k, int32_t E, int32_t BS,
+                 const moe_align_tables* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "moe_align_ws";
+  AlignShape s;
+  int rc = check_routing_shape(fn, M, top_k, E, BS, &s);
+  if (rc) return rc;
+  if (idt != MOE_IDX_I32 && idt != MOE_IDX_I64)
+    return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)idt);
+  if (M == 0) return MOE_OK;
+  if (topk_ids == nullptr) return fail(MOE_ERR_NULL, "%s: topk_ids is NULL", fn);
+  if ((rc = check_tables(fn, out, true))) return rc;
+  const size_t need = moe::align_workspace_bytes((int)s.n, E);
+  if (need > 0) {
+    if (workspace == nullptr) return fail(MOE_ERR_NULL, "%s: workspace is NULL (%zu bytes needed)", fn, need);
+    if (workspace_bytes < need)
+      return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    if ((rc = check_aligned(fn, "workspace", workspace, 16))) return rc;
+  }
+  return hip_status(moe::launch_align_ws(topk_ids, idt == MOE_IDX_I64, (int)s.n, E, BS, (int)s.max_total, s.cap,
+                                         static_cast<int32_t*>(workspace), to_align_out(*out), stream),
                     fn);
 }
 
@@ -582,7 +611,12 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
                                      d->H, d->I, d->S, d->E, d->top_k, d->BS, stream)))
       return rc;
   } else {
-    if ((rc = moe_align(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, stream))) return rc;
+    // the blocks' expert counts of the two-launch align go to the expert_out
+    // region, which only the down projection writes, later on the stream
+    const size_t need = moe::align_workspace_bytes((int)n, d->E), room = off[10] - off[9];
+    if ((rc = need <= room ? moe_align_ws(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, expert_out, room, stream)
+                           : moe_align(topk_ids, d->idt, d->M, d->top_k, d->E, d->BS, &t, stream)))
+      return rc;
     if ((rc = moe_grouped_gate_up_silu(x_bf16, d->wdt, &d->gate, &d->up, &t, act, shared ? &d->sh_gate : nullptr,
                                        shared ? &d->sh_up : nullptr, sh_act, d->M, d->H, d->I, d->S, d->E, d->top_k,
                                        d->BS, stream)))

@@ -79,6 +79,12 @@ struct AlignOut {
 int align_blocks(int n);
 hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap,
                         const AlignOut& o, hipStream_t s);
+// The same tables in two launches (count, then scan + scatter in every block)
+// when the blocks' counts get a workspace of align_workspace_bytes(n, E)
+// bytes (0 below the block threshold, where this is launch_align).
+size_t align_workspace_bytes(int n, int E);
+hipError_t launch_align_ws(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap, int32_t* ws,
+                           const AlignOut& o, hipStream_t s);
 
 // Operands of one grouped projection launch (routed experts + optional shared expert).
 struct GroupedArgs {

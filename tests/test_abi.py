@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -80,6 +80,23 @@ def test_align_refusals(lib):
     assert lib.moe_align(FAKE, 1, 2 ** 17, 8, 1024, 2 ** 21, ctypes.byref(t), None) == _ffi.MOE_ERR_LIMIT
     # M = 0: nothing to do, nothing launched
     assert lib.moe_align(None, 1, 0, 2, 8, 16, None, None) == _ffi.MOE_OK
+
+
+def test_align_ws_refusals(lib):
+    t = _tables()
+    need = lib.moe_align_workspace_bytes(512, 8, 256)  # 4096 slots: 4 blocks of 1024
+    assert need == 4 * 256 * 4
+    assert lib.moe_align_workspace_bytes(511, 8, 256) == 0  # one workgroup, no workspace
+    assert lib.moe_align_workspace_bytes(-1, 8, 256) == 0
+    assert lib.moe_align_workspace_bytes(512, 8, 2000) == 0  # moe_align refuses E > 1024
+    assert lib.moe_align_ws(FAKE, 1, 512, 8, 256, 64, ctypes.byref(t), None, need, None) == _ffi.MOE_ERR_NULL
+    assert "workspace" in _err(lib)
+    assert lib.moe_align_ws(FAKE, 1, 512, 8, 256, 64, ctypes.byref(t), FAKE, need - 1, None) == _ffi.MOE_ERR_WORKSPACE
+    assert lib.moe_align_ws(FAKE, 1, 512, 8, 256, 64, ctypes.byref(t), FAKE + 4, need, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_align_ws(FAKE, 1, 512, 8, 1025, 64, ctypes.byref(t), FAKE, need, None) == _ffi.MOE_ERR_LIMIT
+    assert lib.moe_align_ws(None, 1, 512, 8, 256, 64, ctypes.byref(t), FAKE, need, None) == _ffi.MOE_ERR_NULL
+    assert lib.moe_align_ws(FAKE, 9, 512, 8, 256, 64, ctypes.byref(t), FAKE, need, None) == _ffi.MOE_ERR_SHAPE
+    assert lib.moe_align_ws(None, 1, 0, 8, 256, 64, None, None, 0, None) == _ffi.MOE_OK
 
 
 def _w(scale=True):

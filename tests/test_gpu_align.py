@@ -11,22 +11,31 @@ from moe_testlib import compare_tables, log
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_align(ids_np, E, BS, dtype=torch.int64):
+def _gpu_align(ids_np, E, BS, dtype=torch.int64, ws=False):
+    """moe_align, or (ws) moe_align_ws with a workspace pre-filled with garbage:
+    the tables may not depend on what it held."""
     import mixture_experts_routing_align_amd as moe
 
     ids = torch.from_numpy(np.ascontiguousarray(ids_np)).to(dtype).cuda()
-    t = moe.moe_align(ids, E, BS)
+    if ws:
+        M, top_k = ids.shape
+        nbytes = moe.moe_align_workspace_bytes(M, top_k, E)
+        work = torch.full((max(nbytes, 16) // 4,), -12345, dtype=torch.int32, device="cuda")
+        t = moe.moe_align_ws(ids, E, BS, work)
+    else:
+        t = moe.moe_align(ids, E, BS)
     torch.cuda.synchronize()
     return {k: getattr(t, k) for k in moe.TABLE_FIELDS}
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "verify", "align", "large"])
 @pytest.mark.parametrize("dtype", [torch.int64, torch.int32])
-def test_align_configs_bit_exact(name, dtype):
+@pytest.mark.parametrize("ws", [False, True], ids=["tables_only", "workspace"])
+def test_align_configs_bit_exact(name, dtype, ws):
     cfg = workloads.CONFIGS[name]
-    log(f"align parity: config {name} n={cfg.n} E={cfg.E} BS={cfg.BS} ids {dtype}")
+    log(f"align parity: config {name} n={cfg.n} E={cfg.E} BS={cfg.BS} ids {dtype} workspace={ws}")
     ids, _ = workloads.routing(cfg)
-    compare_tables(_gpu_align(ids, cfg.E, cfg.BS, dtype), oracle.align(ids, cfg.E, cfg.BS))
+    compare_tables(_gpu_align(ids, cfg.E, cfg.BS, dtype, ws), oracle.align(ids, cfg.E, cfg.BS))
 
 
 ADVERSARIAL = [
@@ -56,11 +65,12 @@ ADVERSARIAL = [
 
 
 @pytest.mark.parametrize("case", ADVERSARIAL, ids=lambda c: c[0])
-def test_align_adversarial(case):
+@pytest.mark.parametrize("ws", [False, True], ids=["tables_only", "workspace"])
+def test_align_adversarial(case, ws):
     name, make, E, BS = case
     ids = make(np.random.default_rng(99)).astype(np.int64)
-    log(f"align adversarial: {name} shape={ids.shape} E={E} BS={BS}")
-    compare_tables(_gpu_align(ids, E, BS), oracle.align(ids, E, BS))
+    log(f"align adversarial: {name} shape={ids.shape} E={E} BS={BS} workspace={ws}")
+    compare_tables(_gpu_align(ids, E, BS, ws=ws), oracle.align(ids, E, BS))
 
 
 def test_align_int64_ids_beyond_int32():
@@ -87,5 +97,33 @@ def test_align_random_shapes(seed):
     M = int(rng.integers(1, 3000 if seed < 4 else 6000))
     top_k = int(rng.integers(1, 9))
     ids = rng.integers(-1, E + 1, size=(M, top_k))
-    log(f"align random: seed={seed} M={M} top_k={top_k} E={E} BS={BS}")
-    compare_tables(_gpu_align(ids, E, BS, torch.int32 if seed % 2 else torch.int64), oracle.align(ids, E, BS))
+    ws = seed % 4 >= 2
+    log(f"align random: seed={seed} M={M} top_k={top_k} E={E} BS={BS} workspace={ws}")
+    compare_tables(_gpu_align(ids, E, BS, torch.int32 if seed % 2 else torch.int64, ws), oracle.align(ids, E, BS))
+
+
+def test_align_ws_graph_replay_and_reuse():
+    """The two-launch align captured once and replayed over new ids (the
+    workspace keeps the previous call's counts) matches the oracle each time."""
+    import mixture_experts_routing_align_amd as moe
+
+    cfg = workloads.CONFIGS["align"]
+    M, top_k, E, BS = cfg.M, cfg.top_k, cfg.E, cfg.BS
+    routings = [workloads.routing(cfg.replace(seed=cfg.seed + r))[0] for r in range(3)]
+    ids = torch.from_numpy(routings[0]).cuda()
+    work = torch.empty(moe.moe_align_workspace_bytes(M, top_k, E) // 4, dtype=torch.int32, device="cuda")
+    tables = moe.AlignTables.allocate(M, top_k, E, BS)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        moe.moe_align_ws(ids, E, BS, work, tables=tables)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_align_ws(ids, E, BS, work, tables=tables)
+    for r in (1, 2, 0, 1):
+        ids.copy_(torch.from_numpy(routings[r]))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"align workspace graph replay: routing {r}")
+        compare_tables({k: getattr(tables, k) for k in moe.TABLE_FIELDS}, oracle.align(routings[r], E, BS))

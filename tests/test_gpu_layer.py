@@ -206,6 +206,25 @@ def test_layer_odd_shapes(moe, cfg):
 
 
 @pytest.mark.parametrize("tiled", [False, True])
+def test_layer_prefill_width_two_launch_align(moe, tiled):
+    """4800 slots: past the fused align and past 4096 slots, so the layer aligns
+    in two launches with the blocks' counts in its workspace (the expert_out
+    region, written later by the down projection); tables bit-exact, output
+    within the bound."""
+    cfg = workloads.MoeConfig("bf16_prefill", 600, 96, 32, 8, 64, 0, 16, "bf16", "softmax_bias", bias_std=2.0,
+                              seed=21)
+    assert cfg.M * cfg.top_k >= 4096
+    model = DeviceModel(cfg, threads=4)
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    log(f"prefill-width layer parity: {cfg} tiled={tiled}")
+    out, views = _run_layer(moe, model, xt, it, wt, tiled=tiled)
+    ref = oracle_layer(model, x, ids, w)
+    compare_tables(views, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
+    assert ok, (err, bound)
+
+
+@pytest.mark.parametrize("tiled", [False, True])
 def test_layer_repeated_ids_multi_pass(moe, tiled):
     """Every slot of every token on one expert (ids repeat within a token): 96
     rows on expert 2, more than one pass of row tiles for M=48 (tiled: the
