@@ -301,26 +301,54 @@ __global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const
 #pragma unroll
   for (int c = 0; c < kScatterChunks; ++c) iv[c] = beg + 64 * c < end ? ids[min(beg + 64 * c + lane, end - 1)] : (IdT)-1;
 
-  // thread t owns experts [t * kExpertsPerThread, ...): all blocks' counts of
-  // each, summed in block order (and up to this block, for the base)
+  // every block's count of each expert, summed in block order (and up to this
+  // block, for the base).  Up to kBlockThreads experts: J = kBlockThreads / E
+  // threads per expert each sum a run of blocks (one batch of loads at the
+  // sizes measured), then thread t takes expert t's sums; above that, thread t
+  // sums experts 2t and 2t + 1 alone.  Either way a thread owns a contiguous
+  // run of kExpertsPerThread (or 1) experts for the scan.
+  __shared__ int s_pt[kBlockThreads], s_pb[kBlockThreads];
+  const int run = E <= kBlockThreads ? 1 : kExpertsPerThread;
   int tot[kExpertsPerThread], bef[kExpertsPerThread];
+#pragma unroll
+  for (int k = 0; k < kExpertsPerThread; ++k) tot[k] = bef[k] = 0;
+  auto sum_blocks = [&](int e, int c_lo, int c_hi, int& t_sum, int& b_sum) {
+    for (int c0 = c_lo; c0 < c_hi; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) v[j] = c0 + j < c_hi ? counts[(size_t)(c0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (c0 + j < b) b_sum += v[j];
+        t_sum += v[j];
+      }
+    }
+  };
+  if (run == 1) {
+    const int J = kBlockThreads / E;
+    const int ex = tid % E, jx = tid / E;
+    const int per = (G + J - 1) / J;
+    int pt = 0, pb = 0;
+    if (jx < J) sum_blocks(ex, min(G, jx * per), min(G, jx * per + per), pt, pb);
+    s_pt[tid] = pt;
+    s_pb[tid] = pb;
+    __syncthreads();
+    if (tid < E) {
+      for (int j = 0; j < J; ++j) {  // the runs in block order
+        tot[0] += s_pt[j * E + tid];
+        bef[0] += s_pb[j * E + tid];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kExpertsPerThread; ++k) {
+      const int e = tid * kExpertsPerThread + k;
+      if (e < E) sum_blocks(e, 0, G, tot[k], bef[k]);
+    }
+  }
   int sum_pad = 0, sum_act = 0;
 #pragma unroll
   for (int k = 0; k < kExpertsPerThread; ++k) {
-    const int e = tid * kExpertsPerThread + k;
-    tot[k] = bef[k] = 0;
-    if (e < E) {
-      for (int c0 = 0; c0 < G; c0 += kScanBatch) {
-        int v[kScanBatch];
-#pragma unroll
-        for (int j = 0; j < kScanBatch; ++j) v[j] = c0 + j < G ? counts[(size_t)(c0 + j) * E + e] : 0;
-#pragma unroll
-        for (int j = 0; j < kScanBatch; ++j) {
-          if (c0 + j < b) bef[k] += v[j];
-          tot[k] += v[j];
-        }
-      }
-    }
     sum_pad += (tot[k] + BS - 1) / BS * BS;
     sum_act += tot[k] > 0 ? 1 : 0;
   }
@@ -328,8 +356,8 @@ __global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const
   align_dev::block_scan2<kBlockWaves>(sum_pad, sum_act, s_wa, s_wb, ex_pad, ex_act, total, nact);
 #pragma unroll
   for (int k = 0; k < kExpertsPerThread; ++k) {
-    const int e = tid * kExpertsPerThread + k;
-    if (e < E) {
+    const int e = tid * run + k;
+    if (k < run && e < E) {
       s_off[e] = ex_pad;
       s_tot[e] = tot[k];
       s_base[e] = ex_pad + bef[k];
