@@ -277,9 +277,12 @@ typedef struct {
 
 /* The two ways moe_layer_forward runs, chosen from the descriptor's shapes
  * (never from the routing, so a captured graph stays valid for any routing):
- *  - MOE_LAYER_PATH_STEPS: align (or align fused into gate+up for at most
- *    MOE_FUSED_ALIGN_MAX_SLOTS slots), gate+up+SiLU, down and blend, the same
- *    kernels the four entry points above launch;
+ *  - MOE_LAYER_PATH_STEPS: align (fused into gate+up for at most
+ *    MOE_FUSED_ALIGN_MAX_SLOTS slots when every expert fits one pass; from
+ *    4096 slots the two-launch moe_align_ws, its block counts held in the
+ *    expert_out region until the down projection overwrites it),
+ *    gate+up+SiLU, down and blend, the same kernels the entry points above
+ *    launch;
  *  - MOE_LAYER_PATH_SINGLE_PASS: tiled weights and at most
  *    MOE_FUSED_LAYER_MAX_SLOTS slots (decode width).  One launch aligns and, per
  *    active expert and 64-wide slice j of the intermediate, runs gate+up+SiLU
