@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const
   // sums experts 2t and 2t + 1 alone.  Either way a thread owns a contiguous
   // run of kExpertsPerThread (or 1) experts for the scan.
   __shared__ int s_pt[kBlockThreads], s_pb[kBlockThreads];
-  const int run = E <= kBlockThreads ? 1 : kExpertsPerThread;
+  const int ept = E <= kBlockThreads ? 1 : kExpertsPerThread;  // experts per thread in the scan
   int tot[kExpertsPerThread], bef[kExpertsPerThread];
 #pragma unroll
   for (int k = 0; k < kExpertsPerThread; ++k) tot[k] = bef[k] = 0;
@@ -324,12 +324,45 @@ __global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const
       }
     }
   };
-  if (run == 1) {
-    const int J = kBlockThreads / E;
-    const int ex = tid % E, jx = tid / E;
-    const int per = (G + J - 1) / J;
+  // ept == 1: this thread's first batch of block counts is requested now and
+  // stays in flight while the block counts its own slots (the ids are already
+  // in registers); the sums then take it first, in block order as always
+  const int J = ept == 1 ? kBlockThreads / E : 1;
+  const int ex = tid % E, jx = tid / E;
+  const int bper = (G + J - 1) / J;  // blocks per thread
+  const int c_lo = ept == 1 && jx < J ? min(G, jx * bper) : 0;
+  const int c_hi = ept == 1 && jx < J ? min(G, c_lo + bper) : 0;
+  int pv[kScanBatch];
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j) pv[j] = c_lo + j < c_hi ? counts[(size_t)(c_lo + j) * E + ex] : 0;
+
+  // the block's own slots, per wave
+  for (int i = tid; i < kBlockWaves * E; i += kBlockThreads) cnt[i] = 0;
+  __syncthreads();
+  int* my = cnt + w * E;
+  auto id_of = [&](int c, bool& valid) -> int {
+    const IdT v = iv[c];
+    valid = beg + 64 * c + lane < end && v >= 0 && v < (IdT)E;
+    return valid ? (int)v : -1;
+  };
+#pragma unroll
+  for (int c = 0; c < kScatterChunks; ++c) {
+    if (beg + 64 * c < end) {  // wave-uniform
+      bool valid;
+      const int id = id_of(c, valid);
+      const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
+      if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
+    }
+  }
+
+  if (ept == 1) {
     int pt = 0, pb = 0;
-    if (jx < J) sum_blocks(ex, min(G, jx * per), min(G, jx * per + per), pt, pb);
+#pragma unroll
+    for (int j = 0; j < kScanBatch; ++j) {
+      if (c_lo + j < b) pb += pv[j];
+      pt += pv[j];
+    }
+    if (c_lo + kScanBatch < c_hi) sum_blocks(ex, c_lo + kScanBatch, c_hi, pt, pb);
     s_pt[tid] = pt;
     s_pb[tid] = pb;
     __syncthreads();
@@ -356,8 +389,8 @@ __global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const
   align_dev::block_scan2<kBlockWaves>(sum_pad, sum_act, s_wa, s_wb, ex_pad, ex_act, total, nact);
 #pragma unroll
   for (int k = 0; k < kExpertsPerThread; ++k) {
-    const int e = tid * run + k;
-    if (k < run && e < E) {
+    const int e = tid * ept + k;
+    if (k < ept && e < E) {
       s_off[e] = ex_pad;
       s_tot[e] = tot[k];
       s_base[e] = ex_pad + bef[k];
@@ -366,25 +399,7 @@ __global__ __launch_bounds__(kBlockThreads) void align_scan_scatter_blocks(const
     }
   }
   if (tid == 0) s_off[E] = total;
-  for (int i = tid; i < kBlockWaves * E; i += kBlockThreads) cnt[i] = 0;
-  __syncthreads();
-
-  int* my = cnt + w * E;
-  auto id_of = [&](int c, bool& valid) -> int {
-    const IdT v = iv[c];
-    valid = beg + 64 * c + lane < end && v >= 0 && v < (IdT)E;
-    return valid ? (int)v : -1;
-  };
-#pragma unroll
-  for (int c = 0; c < kScatterChunks; ++c) {
-    if (beg + 64 * c < end) {  // wave-uniform
-      bool valid;
-      const int id = id_of(c, valid);
-      const uint64_t m = align_dev::same_expert_mask(id, valid, nbits);
-      if (valid && align_dev::is_leader(m, lane)) my[id] += __popcll(m);
-    }
-  }
-  __syncthreads();
+  __syncthreads();  // the bases (and the block's own counts, counted above) are in LDS
   for (int e = tid; e < E; e += kBlockThreads) {
     int run = s_base[e];
     for (int k = 0; k < kBlockWaves; ++k) {
