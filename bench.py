@@ -18,8 +18,10 @@ fraction of the 8 TB/s HBM peak, per-kernel times from HIP events, the
 roofline of the dominant kernel (the single-pass layer kernel: align, gate+up
 +SiLU and the down slices), the align latency on the prefill-scale align
 workload (n = 32768 int64 ids, 256 experts, BS 64), the router latency, the
-plain streaming-read ceiling for the same bytes, and the float64 CPU oracle
-timed on the host as a reference baseline (24 seeded decode routings).
+plain streaming-read ceiling for the same bytes, the verify-width layer
+(M=128 with a shared expert; --other-configs) as context, and the float64
+CPU oracle timed on the host as a reference baseline (24 seeded decode
+routings).
 """
 
 from __future__ import annotations
@@ -52,7 +54,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="weight copies / routings cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-reps", type=int, default=25)
-    ap.add_argument("--other-configs", default="",
+    ap.add_argument("--other-configs", default="verify",
                     help="comma-separated workloads (tiny, verify, large, or decode_mN: the decode layer at "
                          "N tokens; a _rows suffix: the same with per-row FP8 scales) also timed whole-layer and "
                          "reported "
@@ -436,7 +438,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        # FP8 e4m3 weight codes widened exactly to bf16 in registers, bf16 x, bf16 MFMA, fp32 accumulation
+        "dtype": "fp8_e4m3 weights, bf16 mfma, fp32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": "decode MoE layer: M=8, hidden 2048, 128 experts, top-8, inter 768, BS 16, no shared "

@@ -258,6 +258,40 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
 
 /* ------------------------------------------------------------ whole layer -- */
 
+/* The two ways moe_layer_forward runs.  A descriptor asks for one with its
+ * `path` field; MOE_LAYER_PATH_AUTO (0) lets the library choose from the
+ * descriptor's shapes (never from the routing, so a captured graph stays valid
+ * for any routing): the single pass where it fits, else the steps.  (The FP8
+ * page picks its decode kernel pair the same way, from the shape and a kill
+ * switch read once: metrale forward_nvfp4_grouped_decode.rs,
+ * nvfp4_grouped_tc_enabled.)
+ *  - MOE_LAYER_PATH_STEPS: align (fused into gate+up for at most
+ *    MOE_FUSED_ALIGN_MAX_SLOTS slots when every expert fits one pass; from
+ *    4096 slots the two-launch moe_align_ws, its block counts held in the
+ *    expert_out region until the down projection overwrites it),
+ *    gate+up+SiLU, down and blend, the same kernels the entry points above
+ *    launch.  Runs every valid descriptor.
+ *  - MOE_LAYER_PATH_SINGLE_PASS: tiled weights and at most
+ *    MOE_FUSED_LAYER_MAX_SLOTS slots (decode width).  One launch aligns and, per
+ *    active expert and 64-wide slice j of the intermediate, runs gate+up+SiLU
+ *    into LDS and then the 64-deep slice j of down, writing float32 partial
+ *    outputs part[j][slot][:]; a second launch forms each slot's expert output
+ *    as the sum of its slices (j ascending, from 0) and blends.  The separate
+ *    down projection sums the 64-deep halves of its chunks in the same order,
+ *    so both paths give the same bits.  (The decomposition of the layer into gate+up then down
+ *    per expert is metrale forward_nvfp4_grouped_decode.rs's; the per-slice
+ *    split is this library's.)  Forcing it on a descriptor it does not fit
+ *    (row-major weights, more slots, LDS) is refused with MOE_ERR_SHAPE.
+ * Environment, read once per process:
+ *  - MOE_FORCE_PATH=steps | single_pass replaces MOE_LAYER_PATH_AUTO in every
+ *    descriptor (an explicit `path` wins); any other value is ignored;
+ *  - MOE_LOG=1 prints one line to stderr the first time moe_layer_forward runs
+ *    each path in the process, naming the path and the layer's shapes. */
+typedef enum {
+  MOE_LAYER_PATH_AUTO = 0,
+  MOE_LAYER_PATH_STEPS = 1,
+  MOE_LAYER_PATH_SINGLE_PASS = 2
+} moe_layer_path_kind;
 typedef struct {
   int64_t M;          /* tokens                                       */
   int32_t H;          /* hidden size                                  */
@@ -273,27 +307,10 @@ typedef struct {
   const void* sh_expert_gate;           /* bf16 [H] gate vector of the shared
                                            expert's output (moe_blend), or NULL:
                                            ungated; only with S > 0      */
+  moe_layer_path_kind path;             /* MOE_LAYER_PATH_AUTO (0: a zeroed
+                                           descriptor) or a forced path   */
 } moe_layer_desc;
 
-/* The two ways moe_layer_forward runs, chosen from the descriptor's shapes
- * (never from the routing, so a captured graph stays valid for any routing):
- *  - MOE_LAYER_PATH_STEPS: align (fused into gate+up for at most
- *    MOE_FUSED_ALIGN_MAX_SLOTS slots when every expert fits one pass; from
- *    4096 slots the two-launch moe_align_ws, its block counts held in the
- *    expert_out region until the down projection overwrites it),
- *    gate+up+SiLU, down and blend, the same kernels the entry points above
- *    launch;
- *  - MOE_LAYER_PATH_SINGLE_PASS: tiled weights and at most
- *    MOE_FUSED_LAYER_MAX_SLOTS slots (decode width).  One launch aligns and, per
- *    active expert and 64-wide slice j of the intermediate, runs gate+up+SiLU
- *    into LDS and then the 64-deep slice j of down, writing float32 partial
- *    outputs part[j][slot][:]; a second launch forms each slot's expert output
- *    as the sum of its slices (j ascending, from 0) and blends.  The separate
- *    down projection sums the 64-deep halves of its chunks in the same order,
- *    so both paths give the same bits.  (The decomposition of the layer into gate+up then down
- *    per expert is metrale forward_nvfp4_grouped_decode.rs's; the per-slice
- *    split is this library's.) */
-typedef enum { MOE_LAYER_PATH_STEPS = 0, MOE_LAYER_PATH_SINGLE_PASS = 1 } moe_layer_path_kind;
 #define MOE_FUSED_LAYER_MAX_SLOTS 256
 
 /* Workspace regions of moe_layer_forward, in this order: sorted_token_ids,
@@ -310,8 +327,9 @@ typedef enum { MOE_LAYER_PATH_STEPS = 0, MOE_LAYER_PATH_SINGLE_PASS = 1 } moe_la
  * an invalid descriptor (moe_last_error says why). */
 size_t moe_layer_workspace_bytes(const moe_layer_desc* d);
 
-/* The moe_layer_path_kind moe_layer_forward takes for `d`, or a negative
- * moe_status for an invalid descriptor. */
+/* The moe_layer_path_kind (STEPS or SINGLE_PASS) moe_layer_forward takes for
+ * `d`, or a negative moe_status for an invalid descriptor or a forced path
+ * that does not fit it. */
 int moe_layer_path(const moe_layer_desc* d);
 
 /* The whole layer on `stream`: align, gate+up+SiLU, down, blend, with no host

@@ -39,6 +39,7 @@ from ._ffi import (  # noqa: F401
     MOE_IDX_I64,
     MOE_FUSED_ALIGN_MAX_SLOTS,
     MOE_FUSED_LAYER_MAX_SLOTS,
+    MOE_LAYER_PATH_AUTO,
     MOE_LAYER_PATH_SINGLE_PASS,
     MOE_LAYER_PATH_STEPS,
     MOE_LAYER_WORKSPACE_REGIONS,
@@ -321,8 +322,10 @@ class MoeLayer:
     """Expert weights of one MoE layer plus the fused ``moe_layer_forward`` call."""
 
     def __init__(self, gate, up, down, top_k: int, BS: int, sh_gate=None, sh_up=None, sh_down=None,
-                 sh_expert_gate: Optional[torch.Tensor] = None):
+                 sh_expert_gate: Optional[torch.Tensor] = None, path: int = MOE_LAYER_PATH_AUTO):
         self.gate, self.up, self.down = gate, up, down
+        # the path the descriptor asks for (MOE_LAYER_PATH_AUTO: chosen from the shapes)
+        self.path_request = path
         self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
         # bf16 [H] gate vector of the shared expert's output (None: ungated)
         self.sh_expert_gate = sh_expert_gate
@@ -340,13 +343,20 @@ class MoeLayer:
             return None if w is None or isinstance(w, TiledWeight) else moe_tile_weights(w, stream)
 
         return MoeLayer(t(self.gate), t(self.up), t(self.down), self.top_k, self.BS,
-                        t(self.sh_gate), t(self.sh_up), t(self.sh_down), self.sh_expert_gate)
+                        t(self.sh_gate), t(self.sh_up), t(self.sh_down), self.sh_expert_gate, self.path_request)
+
+    def with_path(self, path: int) -> "MoeLayer":
+        """The same weights with the descriptor asking for `path` (a
+        MOE_LAYER_PATH_* value; AUTO lets the library choose)."""
+        return MoeLayer(self.gate, self.up, self.down, self.top_k, self.BS, self.sh_gate, self.sh_up, self.sh_down,
+                        self.sh_expert_gate, path)
 
     def desc(self, M: int, idt: int = MOE_IDX_I64) -> MoeLayerDesc:
         none = MoeWeight(None, None)
         d = MoeLayerDesc(M, self.H, self.I, self.S, self.E, self.top_k, self.BS, self.wdt, idt,
                          _weight(self.gate), _weight(self.up), _weight(self.down),
                          _weight(self.sh_gate) or none, _weight(self.sh_up) or none, _weight(self.sh_down) or none)
+        d.path = self.path_request
         if self.sh_expert_gate is not None:
             g = self.sh_expert_gate
             _need(g.dtype == torch.bfloat16 and g.numel() == self.H and g.is_contiguous(),

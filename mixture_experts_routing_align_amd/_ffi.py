@@ -27,8 +27,9 @@ MOE_MAX_EXPERTS = 1024
 MOE_ROUTER_MAX_TOP_K = 64
 MOE_FUSED_ALIGN_MAX_SLOTS = 2048
 MOE_FUSED_LAYER_MAX_SLOTS = 256
-MOE_LAYER_PATH_STEPS = 0
-MOE_LAYER_PATH_SINGLE_PASS = 1
+MOE_LAYER_PATH_AUTO = 0
+MOE_LAYER_PATH_STEPS = 1
+MOE_LAYER_PATH_SINGLE_PASS = 2
 MOE_LAYER_WORKSPACE_REGIONS = 14
 
 c_void_p = ctypes.c_void_p
@@ -55,7 +56,7 @@ class MoeLayerDesc(ctypes.Structure):
         ("top_k", c_int32), ("BS", c_int32), ("wdt", c_int), ("idt", c_int),
         ("gate", MoeWeight), ("up", MoeWeight), ("down", MoeWeight),
         ("sh_gate", MoeWeight), ("sh_up", MoeWeight), ("sh_down", MoeWeight),
-        ("sh_expert_gate", c_void_p),
+        ("sh_expert_gate", c_void_p), ("path", c_int),
     ]
 
 

@@ -8,8 +8,11 @@
 // experts).  Nothing here allocates, synchronises or reads device memory.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <string>
 
 #include "moe_internal.h"
@@ -28,6 +31,20 @@ int fail(int code, const char* fmt, ...) {
   g_last_error = buf;
   return code;
 }
+
+}  // namespace
+
+int moe::fail_status(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+namespace {
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MOE_OK;
@@ -161,12 +178,55 @@ moe::GroupedArgs gate_up_args(const void* x_bf16, const moe_weight* gate, const 
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// MOE_FORCE_PATH, read once per process: the path that replaces
+// MOE_LAYER_PATH_AUTO ("steps" or "single_pass"; anything else: none).
+int forced_path() {
+  static const int forced = [] {
+    const char* v = getenv("MOE_FORCE_PATH");
+    if (v == nullptr) return (int)MOE_LAYER_PATH_AUTO;
+    if (!strcmp(v, "steps")) return (int)MOE_LAYER_PATH_STEPS;
+    if (!strcmp(v, "single_pass")) return (int)MOE_LAYER_PATH_SINGLE_PASS;
+    return (int)MOE_LAYER_PATH_AUTO;
+  }();
+  return forced;
+}
+
 // The path moe_layer_forward takes for a checked descriptor (shape only, never
-// the routing): the single-pass layer for tiled weights at decode width.
-int layer_path(const moe_layer_desc* d) {
+// the routing): the one the descriptor (else MOE_FORCE_PATH) asks for, or by
+// default the single-pass layer where it fits (tiled weights at decode width).
+// A forced single pass that does not fit is refused.
+int layer_path(const char* fn, const moe_layer_desc* d) {
   const bool fits = is_tiled(d->wdt) &&
                     moe::fused_layer_fits(is_fp8(d->wdt), is_rows(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
+  const int want = d->path != MOE_LAYER_PATH_AUTO ? (int)d->path : forced_path();
+  if (want == MOE_LAYER_PATH_STEPS) return MOE_LAYER_PATH_STEPS;
+  if (want == MOE_LAYER_PATH_SINGLE_PASS && !fits)
+    return fail(MOE_ERR_SHAPE,
+                "%s: the single-pass path needs tiled weights, at most %d slots (M*top_k = %lld) and its LDS "
+                "budget",
+                fn, MOE_FUSED_LAYER_MAX_SLOTS, (long long)(d->M * d->top_k));
   return fits ? MOE_LAYER_PATH_SINGLE_PASS : MOE_LAYER_PATH_STEPS;
+}
+
+// MOE_LOG=1 (read once per process): one line on stderr the first time the
+// layer runs each path.
+void log_path_once(const moe_layer_desc* d, int path) {
+  static const bool on = [] {
+    const char* v = getenv("MOE_LOG");
+    return v != nullptr && !strcmp(v, "1");
+  }();
+  if (!on) return;
+  static std::atomic<unsigned> logged{0};
+  const unsigned bit = 1u << path;
+  if (logged.fetch_or(bit) & bit) return;
+  static const char* names[] = {"auto", "steps", "single_pass"};
+  static const char* wnames[] = {"bf16", "fp8_e4m3", "bf16_tiled", "fp8_e4m3_tiled", "fp8_e4m3_rows",
+                                 "fp8_e4m3_rows_tiled"};
+  fprintf(stderr,
+          "moe_mi355x: moe_layer_forward path %s (M=%lld H=%d I=%d S=%d E=%d top_k=%d BS=%d weights %s%s)\n",
+          names[path], (long long)d->M, d->H, d->I, d->S, d->E, d->top_k, d->BS, wnames[d->wdt],
+          d->path != MOE_LAYER_PATH_AUTO ? ", forced by the descriptor"
+                                         : (forced_path() != MOE_LAYER_PATH_AUTO ? ", forced by MOE_FORCE_PATH" : ""));
 }
 
 int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1], int* path = nullptr) {
@@ -179,13 +239,16 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
   if (d->idt != MOE_IDX_I32 && d->idt != MOE_IDX_I64)
     return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)d->idt);
   if (d->S < 0) return fail(MOE_ERR_SHAPE, "%s: S=%d is negative", fn, d->S);
+  if (d->path < MOE_LAYER_PATH_AUTO || d->path > MOE_LAYER_PATH_SINGLE_PASS)
+    return fail(MOE_ERR_SHAPE, "%s: unknown path %d", fn, (int)d->path);
   if ((rc = check_projection(fn, "gate/up", d->wdt, d->I, d->H))) return rc;
   if ((rc = check_projection(fn, "down", d->wdt, d->H, d->I))) return rc;
   if (d->S > 0) {
     if ((rc = check_projection(fn, "shared gate/up", d->wdt, d->S, d->H))) return rc;
     if ((rc = check_projection(fn, "shared down", d->wdt, d->H, d->S))) return rc;
   }
-  const int lp = layer_path(d);
+  const int lp = layer_path(fn, d);
+  if (lp < 0) return lp;
   if (path) *path = lp;
   const bool single = lp == MOE_LAYER_PATH_SINGLE_PASS;
   const size_t mt = (size_t)s.max_total, n = (size_t)s.n, M = (size_t)d->M, H = (size_t)d->H;
@@ -217,7 +280,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 8; }
+int32_t moe_abi_version(void) { return 9; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -588,6 +651,7 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   if (!x_bf16 || !topk_ids || !topk_weights || !out_bf16)
     return fail(MOE_ERR_NULL, "%s: x, topk_ids, topk_weights or out is NULL", fn);
   if ((rc = check_aligned(fn, "x", x_bf16, 16)) || (rc = check_aligned(fn, "out", out_bf16, 8))) return rc;
+  log_path_once(d, path);
   char* ws = static_cast<char*>(workspace);
   if (path == MOE_LAYER_PATH_SINGLE_PASS) {
     const moe::FusedLayerArgs a = single_pass_args(d, ws, off, x_bf16, topk_ids, topk_weights, out_bf16);

@@ -63,6 +63,9 @@ inline hipError_t occupancy_per_cu(const void* kern, int threads, size_t lds,
 
 constexpr int kFp8Block = 128;   // FP8 scale block edge (both N and K)
 
+// Record a failure for moe_last_error() and return `code` (api.cpp).
+int fail_status(int code, const char* fmt, ...);
+
 struct AlignOut {
   int32_t* sorted_token_ids;
   int32_t* block_expert_ids;

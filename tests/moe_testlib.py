@@ -59,9 +59,17 @@ class DeviceModel(DeviceWeights):
         return self._tiled
 
     def routed_weight(self, which, e):
+        """The generated (bits, scales) of expert e's matrix `which`: kept on the
+        host for small configs; for large ones read back from the row-major
+        device copy, which holds exactly the generator's bits (torch copied
+        them there; no kernel of the library wrote them)."""
         if self.host is not None:
             return self.host[(which, e)]
-        return workloads.expert_matrix(self.cfg, which, e)
+        w, s = self.weight(which)
+        bits = w[e].cpu().numpy()
+        if w.dtype == torch.bfloat16:
+            bits = w[e].view(torch.int16).cpu().numpy().view(np.uint16)
+        return bits, (None if s is None else s[e].cpu().numpy())
 
     def shared_weight(self):
         if not self.cfg.S:

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 8
+    assert lib.moe_abi_version() == 9
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -255,6 +255,72 @@ def test_single_pass_stage_refusals(lib):
     t0 = _tiled(_desc(M=0))
     assert lib.moe_layer_partials(ctypes.byref(t0), None, None, None, 0, None) == _ffi.MOE_OK
 
+
+
+def test_path_control(lib):
+    """The descriptor's `path` field: AUTO chooses from the shapes, STEPS runs
+    every valid descriptor, SINGLE_PASS is refused where it does not fit; the
+    workspace follows the chosen path."""
+    P = _ffi
+    t = _tiled(_desc())                                 # decode, tiled: AUTO takes the single pass
+    assert lib.moe_layer_path(ctypes.byref(t)) == P.MOE_LAYER_PATH_SINGLE_PASS
+    auto_bytes = lib.moe_layer_workspace_bytes(ctypes.byref(t))
+    t.path = P.MOE_LAYER_PATH_STEPS
+    assert lib.moe_layer_path(ctypes.byref(t)) == P.MOE_LAYER_PATH_STEPS
+    steps_bytes = lib.moe_layer_workspace_bytes(ctypes.byref(t))
+    assert steps_bytes > 0 and steps_bytes != auto_bytes
+    need = steps_bytes
+    # the stage calls of the single pass refuse a descriptor forced onto the steps path
+    assert lib.moe_layer_partials(ctypes.byref(t), FAKE, FAKE, 0x100000, need, None) == P.MOE_ERR_SHAPE
+    t.path = P.MOE_LAYER_PATH_SINGLE_PASS
+    assert lib.moe_layer_path(ctypes.byref(t)) == P.MOE_LAYER_PATH_SINGLE_PASS
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(t)) == auto_bytes
+    r = _desc()                                         # row-major: no single pass
+    assert lib.moe_layer_path(ctypes.byref(r)) == P.MOE_LAYER_PATH_STEPS
+    r.path = P.MOE_LAYER_PATH_SINGLE_PASS
+    assert lib.moe_layer_path(ctypes.byref(r)) == P.MOE_ERR_SHAPE
+    assert "single-pass" in _err(lib)
+    assert lib.moe_layer_workspace_bytes(ctypes.byref(r)) == 0
+    rc = lib.moe_layer_forward(ctypes.byref(r), FAKE, FAKE, FAKE, FAKE, 0x100000, 1 << 40, None)
+    assert rc == P.MOE_ERR_SHAPE
+    v = _tiled(_desc(M=128, S=2048))                    # 1024 slots: no single pass even when tiled
+    v.path = P.MOE_LAYER_PATH_SINGLE_PASS
+    assert lib.moe_layer_path(ctypes.byref(v)) == P.MOE_ERR_SHAPE
+    bad = _desc()
+    bad.path = 7
+    assert lib.moe_layer_path(ctypes.byref(bad)) == P.MOE_ERR_SHAPE
+    assert "path" in _err(lib)
+
+
+FORCE_SCRIPT = """
+import ctypes, sys
+sys.path.insert(0, {root!r})
+from mixture_experts_routing_align_amd import _ffi
+from tests.test_abi import _desc, _tiled
+lib = _ffi.load()
+t = _tiled(_desc())
+auto = lib.moe_layer_path(ctypes.byref(t))
+t.path = _ffi.MOE_LAYER_PATH_SINGLE_PASS
+explicit = lib.moe_layer_path(ctypes.byref(t))
+r = _desc()
+print(auto, explicit, lib.moe_layer_path(ctypes.byref(r)))
+"""
+
+
+@pytest.mark.parametrize("env,want", [("steps", (1, 2, 1)), ("single_pass", (2, 2, -2)), ("bogus", (2, 2, 1))])
+def test_force_path_environment(env, want):
+    """MOE_FORCE_PATH replaces AUTO in every descriptor (an explicit path wins;
+    a forced single pass that does not fit is refused); read once, so each case
+    runs in a fresh process.  Host sizing calls only: no GPU is touched."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    e = dict(os.environ, MOE_FORCE_PATH=env)
+    out = subprocess.run([sys.executable, "-c", FORCE_SCRIPT.format(root=root)], env=e, cwd=root,
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert tuple(int(v) for v in out.stdout.split()) == want
 
 
 def test_stream_read_probe_refusals(lib):

@@ -110,9 +110,34 @@ def test_layer_verify(moe):
     _check_layer(moe, "verify")
 
 
+# the large layer's oracle sample: 4 tokens from each 16-token row group of the
+# shared expert (its passes), first and last token included
+LARGE_TOKENS = [0, 5, 10, 15, 16, 22, 27, 31, 32, 37, 42, 47, 48, 53, 58, 63]
+
+
 def test_layer_large_sampled(moe):
-    # full size; the oracle computes a sample of tokens one by one (first, last, two inside)
-    _check_layer(moe, "large", tokens=[0, 17, 42, 63])
+    # full size; the oracle computes a sample of tokens one by one
+    _check_layer(moe, "large", tokens=LARGE_TOKENS)
+
+
+def test_layer_large_tiled(moe):
+    """The large layer with tiled weights (the form the benchmark times): its
+    gate+up stages x 128 deep at a time (the 7168-deep rows do not stay
+    resident in LDS).  Bit-identical to the row-major run, and within the
+    tolerance of the oracle on the sampled tokens."""
+    model = model_for("large")
+    cfg = model.cfg
+    (x, ids, w), (xt, it, wt) = device_inputs(cfg)
+    log(f"large layer, tiled weights: M={cfg.M} H={cfg.H} E={cfg.E} I={cfg.I} S={cfg.S}")
+    a, views = _run_layer(moe, model, xt, it, wt)
+    b, tviews = _run_layer(moe, model, xt, it, wt, tiled=True)
+    assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_STEPS
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle_layer(model, x, ids, w, tokens=LARGE_TOKENS)
+    compare_tables(tviews, ref["tables"])
+    ok, err, bound = tolerance_ok(bf16_to_np(b)[LARGE_TOKENS], ref["out"])
+    log(f"  out: max err {err:.3e} bound {bound:.3e}")
+    assert ok, (err, bound)
 
 
 def test_layer_int32_ids_same_bits(moe):

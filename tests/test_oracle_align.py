@@ -68,16 +68,17 @@ def test_hand_worked_examples(case):
 
 
 def test_brute_force_tiny():
-    """Every id vector over {-1, 0..E} for E<=3, n<=4 and BS in 1..4."""
+    """Every id vector over {-1, 0..E} (one invalid id on each side) for E<=3,
+    n<=6 and BS in 1..5."""
     checked = 0
     for E in (1, 2, 3):
-        for n in range(1, 5):
+        for n in range(1, 7):
             for ids in itertools.product(range(-1, E + 1), repeat=n):
-                for BS in (1, 2, 3, 4):
+                for BS in (1, 2, 3, 4, 5):
                     got = oracle.align(np.array(ids, dtype=np.int64), E, BS)
                     _check_equal(got, _second_formulation(list(ids), E, BS))
                     checked += 1
-    assert checked > 3000
+    assert checked == 5 * sum((E + 2) ** n for E in (1, 2, 3) for n in range(1, 7))
 
 
 def test_bs1_is_library_stable_argsort():
