@@ -343,6 +343,23 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
                       const float* topk_weights, void* out_bf16, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_forward with its workspace in a device array the library owns,
+ * MOE_NOALLOC_WORKSPACE_BYTES bytes on each GPU it runs on, held from the
+ * module's load until the process ends.  The caller still passes x, topk_ids,
+ * topk_weights and out.  The call allocates nothing; the array's device
+ * address is looked up once per device, on the first call with that device
+ * current.  Every call on one GPU shares that GPU's array and leaves its
+ * tables and intermediates there (nothing in it has to start at zero), so calls
+ * that overlap on one GPU (several streams or threads at once) race: serialize
+ * them.  Errors: those of moe_layer_forward, plus MOE_ERR_WORKSPACE when
+ * moe_layer_workspace_bytes(d) exceeds the array (64 MiB: the tiny, decode and
+ * verify-width layers fit; the 7168-wide layer does not). */
+#define MOE_NOALLOC_WORKSPACE_BYTES (64u << 20)
+int moe_layer_forward_noalloc(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids,
+                              const float* topk_weights, void* out_bf16, hipStream_t stream);
+
 /* The two launches of the single-pass path, callable one at a time (for
  * example to time each); moe_layer_forward on that path is exactly
  * moe_layer_partials followed by moe_layer_blend_partials on the same

@@ -31,6 +31,7 @@ MOE_LAYER_PATH_AUTO = 0
 MOE_LAYER_PATH_STEPS = 1
 MOE_LAYER_PATH_SINGLE_PASS = 2
 MOE_LAYER_WORKSPACE_REGIONS = 14
+MOE_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 c_void_p = ctypes.c_void_p
 c_int = ctypes.c_int
@@ -96,6 +97,7 @@ SIGNATURES = {
     "moe_router_topk": (c_int, [c_void_p, c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int,
                                 c_void_p, c_void_p]),
     "moe_tile_weights": (c_int, [c_void_p, c_void_p, c_int, c_int64, c_int32, c_int32, c_void_p]),
+    "moe_layer_forward_noalloc": (c_int, [P(MoeLayerDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
 }
 
 _LIB = None

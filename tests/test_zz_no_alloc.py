@@ -1,0 +1,59 @@
+"""moe_layer_forward_noalloc (the library's own workspace array) against
+moe_layer_forward with a caller workspace, through the C ABI: the same output
+bits, on two calls in a row with the second smaller, on both layer paths."""
+
+import ctypes
+
+import pytest
+import torch
+
+import workloads
+from moe_testlib import DeviceModel, device_inputs, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import mixture_experts_routing_align_amd as m
+
+    return m
+
+
+def _noalloc(moe, layer, xt, it, wt):
+    M = xt.shape[0]
+    idt = moe.MOE_IDX_I64 if it.dtype == torch.int64 else moe.MOE_IDX_I32
+    d = layer.desc(M, idt)
+    out = torch.full((M, layer.H), float("nan"), dtype=torch.bfloat16, device=xt.device)
+    rc = moe.lib().moe_layer_forward_noalloc(ctypes.byref(d), xt.data_ptr(), it.data_ptr(), wt.data_ptr(),
+                                             out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == moe.MOE_OK, moe.lib().moe_last_error().decode()
+    return out
+
+
+@pytest.mark.parametrize("name,tiled,ms", [("verify", False, (128, 37)), ("decode", True, (8, 3)),
+                                           ("tiny", False, (4, 1))])
+def test_noalloc_equals_forward(moe, name, tiled, ms):
+    cfg = workloads.CONFIGS[name]
+    model = DeviceModel(cfg, threads=16)
+    layer = model.tiled_layer() if tiled else model.layer()
+    _, (xt, it, wt) = device_inputs(cfg)
+    assert layer.workspace_bytes(cfg.M) <= moe._ffi.MOE_NOALLOC_WORKSPACE_BYTES
+    for m in ms:  # two calls in a row, the second on fewer tokens
+        log(f"no-alloc layer: {name} tiled={tiled} M={m}")
+        x, i, w = xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous()
+        a = _noalloc(moe, layer, x, i, w)
+        b = layer.forward(x, i, w)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), m
+
+
+def test_noalloc_refuses_large_layer(moe):
+    """The 7168-wide layer needs more workspace than the array holds: refused
+    before any launch, with the reason."""
+    cfg = workloads.CONFIGS["large"]
+    d = moe._ffi.MoeLayerDesc(cfg.M, cfg.H, cfg.I, cfg.S, cfg.E, cfg.top_k, cfg.BS, moe.MOE_W_FP8_E4M3,
+                              moe.MOE_IDX_I64, *([moe._ffi.MoeWeight(0x1000, 0x1000)] * 6))
+    rc = moe.lib().moe_layer_forward_noalloc(ctypes.byref(d), 0x1000, 0x1000, 0x1000, 0x1000, None)
+    assert rc == moe.MOE_ERR_WORKSPACE
+    assert "workspace" in moe.lib().moe_last_error().decode()
