@@ -61,6 +61,8 @@ def parse():
                          "under other_configs (context for the headline, not the headline)")
     ap.add_argument("--only-config", default="",
                     help="time one other workload (tiny, verify or large) alone and print its line; for profiling")
+    ap.add_argument("--path", default="auto", choices=["auto", "steps", "single_pass"],
+                    help="layer path the descriptors ask for (auto: the library's choice)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (counter calibration) and exit")
     return ap.parse_args()
@@ -267,8 +269,10 @@ def main():
     ids_d = [torch.from_numpy(ids).to(dev) for ids, _ in routings]
     w_d = [torch.from_numpy(w).to(dev) for _, w in routings]
     # the expert weights in the tiled layout (a one-time load-time reordering)
+    want = {"auto": moe.MOE_LAYER_PATH_AUTO, "steps": moe.MOE_LAYER_PATH_STEPS,
+            "single_pass": moe.MOE_LAYER_PATH_SINGLE_PASS}[args.path]
     layers = [moe.MoeLayer(c.weight("gate"), c.weight("up"), c.weight("down"), cfg.top_k, cfg.BS).tiled()
-              for c in copies]
+              .with_path(want) for c in copies]
     del copies
     torch.cuda.empty_cache()
     outs = [torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device=dev) for _ in range(G)]
@@ -294,7 +298,7 @@ def main():
     # times back to back in one graph; HIP events on the replay stream bracket
     # each replay
     log("per-kernel breakdown")
-    assert all(l.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS for l in layers)
+    path = layers[0].path(cfg.M)
     R = max(1, args.breakdown_reps)
 
     def k_partials(i):
@@ -303,8 +307,16 @@ def main():
     def k_blend(i):
         moe.moe_layer_blend_partials(layers[i], ids_d[i], w_d[i], outs[i], wss[i], stream=stream)
 
+    if path == moe.MOE_LAYER_PATH_SINGLE_PASS:
+        launches = (("layer_partials", k_partials), ("blend_partials", k_blend))
+        dominant = "layer_partials"
+        dominant_kernel = "layer_kernel<fp8> (moe_layer_partials: align + gate+up+SiLU + down slices)"
+    else:
+        launches = (("layer_steps", step),)
+        dominant = "layer_steps"
+        dominant_kernel = "the steps path's launches together (align, gate+up, down, blend)"
     kernels_us = {}
-    for name, fn in (("layer_partials", k_partials), ("blend_partials", k_blend)):
+    for name, fn in launches:
         g = graph_of(lambda fn=fn: [fn(i) for _ in range(R) for i in range(G)], stream)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(stream):
@@ -316,7 +328,7 @@ def main():
         ev1.synchronize()
         kernels_us[name] = ev0.elapsed_time(ev1) * 1e3 / (3 * R * G)
     layer_bytes = float(np.mean([b["total"] for b in bytes_per]))
-    part_gbps = layer_bytes / (kernels_us["layer_partials"] * 1e-6) / 1e9
+    part_gbps = layer_bytes / (kernels_us[dominant] * 1e-6) / 1e9
 
     # align latency on the prefill-scale align workload, graph-replayed
     log("align latency (n=32768, E=256, BS=64)")
@@ -422,7 +434,7 @@ def main():
         "same_bytes_blocks": best_blocks,
         "us_by_blocks": {str(k): v for k, v in ceiling.items()},
         "gib4_gbps": big_gbps,
-        "layer_partials_frac_of_same_bytes": same_bytes_us / kernels_us["layer_partials"],
+        "dominant_frac_of_same_bytes": same_bytes_us / kernels_us[dominant],
     }
 
     digest = source_digest()
@@ -453,9 +465,10 @@ def main():
         "active_experts_mean": float(np.mean([b["active"] for b in bytes_per])),
         "weight_bytes_per_step_mean": float(np.mean([b["total"] for b in bytes_per])),
         "kernels_us": kernels_us,
-        "kernel_gbps": {"layer_partials": part_gbps},
+        "kernel_gbps": {dominant: part_gbps},
+        "path": {moe.MOE_LAYER_PATH_STEPS: "steps", moe.MOE_LAYER_PATH_SINGLE_PASS: "single_pass"}[path],
         "roofline": {
-            "kernel": "layer_kernel<fp8> (moe_layer_partials: align + gate+up+SiLU + down slices)",
+            "kernel": dominant_kernel,
             "bound": "hbm",
             "achieved": part_gbps,
             "peak": HBM_PEAK_GBPS,
