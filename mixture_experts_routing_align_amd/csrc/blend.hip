@@ -41,15 +41,30 @@ __global__ __launch_bounds__(256) void blend_kernel(uint16_t* __restrict__ out,
   if (h >= H) continue;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   const size_t slot0 = (size_t)t * top_k;
-  for (int k = 0; k < top_k; ++k) {
-    const int p = perm[slot0 + k];
-    if (p < 0) continue;
-    const float wk = w[slot0 + k];
-    const float4 y = *reinterpret_cast<const float4*>(expert_out + (size_t)p * H + h);
-    a0 = fmaf(wk, y.x, a0);
-    a1 = fmaf(wk, y.y, a1);
-    a2 = fmaf(wk, y.z, a2);
-    a3 = fmaf(wk, y.w, a3);
+  // kKB slots at a time: their positions and weights, then their rows, all
+  // requested before the first is used; summed in k order
+  constexpr int kKB = 8;
+  for (int k0 = 0; k0 < top_k; k0 += kKB) {
+    int pk[kKB];
+    float wk[kKB];
+#pragma unroll
+    for (int j = 0; j < kKB; ++j) {
+      const int k = min(k0 + j, top_k - 1);
+      pk[j] = k0 + j < top_k ? perm[slot0 + k] : -1;
+      wk[j] = w[slot0 + k];
+    }
+    float4 y[kKB];
+#pragma unroll
+    for (int j = 0; j < kKB; ++j)
+      y[j] = *reinterpret_cast<const float4*>(expert_out + (size_t)(pk[j] < 0 ? 0 : pk[j]) * H + h);
+#pragma unroll
+    for (int j = 0; j < kKB; ++j) {
+      if (pk[j] < 0) continue;
+      a0 = fmaf(wk[j], y[j].x, a0);
+      a1 = fmaf(wk[j], y[j].y, a1);
+      a2 = fmaf(wk[j], y[j].z, a2);
+      a3 = fmaf(wk[j], y[j].w, a3);
+    }
   }
   if (sh_out != nullptr) {
     const float4 s = *reinterpret_cast<const float4*>(sh_out + (size_t)t * H + h);

@@ -61,6 +61,7 @@ constexpr int kMaxRowCap = 128; // most rows one pass stages
 constexpr size_t kResidentLdsBudget = 80 * 1024;
 constexpr int kMaxScaleBlocks = 128;  // FP8 depth limit: 128 scale blocks = 16384
 constexpr int kMaxTilesPerGroup = 2;  // most 64-column tiles one workgroup runs in a row
+constexpr int kStaged = 0, kResident = 1, kRoutedResident = 2;  // activation staging modes
 
 // LDS bytes of the fused alignment region for E experts and n slots.
 __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
@@ -70,13 +71,17 @@ __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
 // ROWS (FP8 only): one float32 scale per weight row, [E, N], instead of one per
 // 128x128 block; it multiplies the same places the block scale does (each
 // 128-deep gate/up chunk's sum, each 64-deep down half), per output column.
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
+// RES: how a workgroup stages its rows' activations: kStaged (128 deep at a
+// time, one barrier per chunk), kResident (the whole depth at once, no barrier
+// in the weight stream), or kRoutedResident (routed items resident, the shared
+// expert's deeper rows staged; chosen when only the routed depth fits in LDS).
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
 __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int rowcap, int ctw, size_t xs_bytes) {
   constexpr int NS = GATE_UP ? 2 : 1;   // weight streams (gate, up) or (down)
   constexpr int NX = GATE_UP ? 1 : 2;   // B planes: bf16 x, or bf16 hi + lo of act
   constexpr int WL = FP8 ? 2 : 4;       // 16-byte weight loads per lane per chunk
   constexpr int ESZ = FP8 ? 1 : 2;      // weight element bytes
-  constexpr int NBUF = RESIDENT ? 3 : 2;  // weight chunks in the register ring
+  constexpr int NBUF = RES == kStaged ? 2 : 3;  // weight chunks in the register ring
   constexpr int EPP = GATE_UP ? 8 : 4;  // source elements per 16-byte staging piece
   constexpr int SL = kMaxScaleBlocks / 64;  // scale registers per stream (one scale per lane)
 
@@ -297,9 +302,10 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sreg[st][SL - 1]), c & 63));
   };
 
-  const int stride = (RESIDENT ? K : kKC) + kPad;     // staged row length (bf16 elements)
+  const bool resident = RES == kResident || (RES == kRoutedResident && routed);
+  const int stride = (resident ? K : kKC) + kPad;     // staged row length (bf16 elements)
   const int plane = rowcap * stride;                  // elements per B plane
-  const int pieces = (RESIDENT ? K : kKC) / EPP;      // 16-byte pieces per staged row
+  const int pieces = (resident ? K : kKC) / EPP;      // 16-byte pieces per staged row
 
   // one 16-byte piece of a source row, as loaded (bf16 x) or as fp32 act
   auto load_piece = [&](int src, int kk) -> uint4 {
@@ -489,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       }
     };
 
-    if (RESIDENT) {
+    if (resident) {
       // every row of this pass, the whole depth
       const int total = nr * pieces;
       for (int base = 0; base < total; base += 8 * kThreads) {
@@ -568,9 +574,9 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED, bool FUSED, typename IdT>
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
 hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
-  auto kern = grouped_kernel<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, FUSED, IdT>;
+  auto kern = grouped_kernel<FP8, ROWS, GATE_UP, RT, RES, TILED, FUSED, IdT>;
   const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
   static std::atomic<size_t> allowed[kMaxCachedDevices];
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, allowed);
@@ -597,14 +603,14 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
   return hipGetLastError();
 }
 
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool RESIDENT, bool TILED>
+template <bool FP8, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED>
 hipError_t launch_fused_or_not(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   if (GATE_UP && a.ids != nullptr) {
     if (a.ids64)
-      return launch_one<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
-    return launch_one<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
+      return launch_one<FP8, ROWS, GATE_UP, RT, RES, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
+    return launch_one<FP8, ROWS, GATE_UP, RT, RES, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
   }
-  return launch_one<FP8, ROWS, GATE_UP, RT, RESIDENT, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
+  return launch_one<FP8, ROWS, GATE_UP, RT, RES, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
 }
 
 template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool TILED>
@@ -612,6 +618,7 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   constexpr int NX = GATE_UP ? 1 : 2;
   const int kmax = (a.sw0 != nullptr && a.sK > a.K) ? a.sK : a.K;
   const size_t resident = (size_t)NX * rowcap * (kmax + kPad) * 2;
+  const size_t routed_resident = (size_t)NX * rowcap * (a.K + kPad) * 2;
   const size_t chunked = (size_t)2 * NX * rowcap * (kKC + kPad) * 2;
   const int nmax = (a.sw0 != nullptr && a.sN > a.N) ? a.sN : a.N;
   const int tiles = (nmax + kTileCols - 1) / kTileCols;
@@ -622,8 +629,13 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   const int64_t n = (int64_t)a.M * a.top_k;
   b.items = (int)((n + (int64_t)a.cap * (rowcap - 1)) / rowcap);
   if (resident <= kResidentLdsBudget)
-    return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, true, TILED>(b, rowcap, resident, tiles, s);
-  return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, false, TILED>(b, rowcap, chunked, tiles, s);
+    return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, kResident, TILED>(b, rowcap, resident, tiles, s);
+  // only the shared expert's depth is too deep: its items stage 128 deep at a
+  // time while the routed items keep their rows resident
+  if (routed_resident <= kResidentLdsBudget)
+    return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, kRoutedResident, TILED>(
+        b, rowcap, std::max(routed_resident, chunked), tiles, s);
+  return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, kStaged, TILED>(b, rowcap, chunked, tiles, s);
 }
 
 // one 16-row tile per pass: each pass of an expert is a workgroup of its own
