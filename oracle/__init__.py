@@ -38,5 +38,6 @@ from .ffn import (  # noqa: F401
     shared_gate,
     silu,
 )
-from .numerics import bf16_to_f64, e4m3_table, e4m3_value  # noqa: F401
+from .numerics import bf16_to_f64, e2m1_table, e2m1_value, e4m3_table, e4m3_value, e8m0_value  # noqa: F401
+from .numerics import mxfp4_decode  # noqa: F401
 from .router import router_logits, topk_softmax  # noqa: F401

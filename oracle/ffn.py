@@ -35,7 +35,7 @@ from typing import Callable, Iterable, Optional
 import numpy as np
 
 from .align import align
-from .numerics import bf16_to_f64, e4m3_decode
+from .numerics import bf16_to_f64, e4m3_decode, mxfp4_decode
 
 FP8_BLOCK = 128
 
@@ -45,7 +45,8 @@ def dequant(bits: np.ndarray, scales: Optional[np.ndarray], wdt: str) -> np.ndar
     of each code times the float32 scale of its 128x128 block.  fp8_rows: e4m3
     value times the float32 scale of its row (the FP8 page's shared-expert
     weights carry a row scale beside the codes, where the routed experts carry
-    128x128 block scales)."""
+    128x128 block scales).  mxfp4: packed E2M1 codes [N, K/2] times the E8M0
+    scale of each row's 32-column block (``mxfp4_decode``)."""
     if wdt == "bf16":
         return bf16_to_f64(bits)
     if wdt == "fp8_rows":
@@ -53,6 +54,8 @@ def dequant(bits: np.ndarray, scales: Optional[np.ndarray], wdt: str) -> np.ndar
         s = np.asarray(scales, dtype=np.float32).astype(np.float64)
         assert s.shape == (vals.shape[0],)
         return vals * s[:, None]
+    if wdt == "mxfp4":
+        return mxfp4_decode(bits, scales)
     if wdt != "fp8":
         raise ValueError(wdt)
     vals = e4m3_decode(bits)

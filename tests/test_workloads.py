@@ -80,3 +80,27 @@ def test_bf16_weights():
     assert sc is None and bits.dtype == np.uint16 and bits.shape == (128, 256)
     v = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
     assert 0.015 < v.std() < 0.025
+
+
+def test_mxfp4_weights_quantisation():
+    """Each 32-column block's scale puts the block's largest magnitude at E2M1
+    4 or 6 (amax / scale in [4, 8), rounded, saturating at 6), no element
+    exceeds 6 times its scale, and the same seed gives the same bits."""
+    import oracle
+    import workloads
+
+    cfg = workloads.CONFIGS["decode"].replace(wdt="mxfp4", name="decode_mxfp4")
+    packed, scales = workloads.expert_matrix(cfg, "gate", 5)
+    N, K = workloads.weight_shape(cfg, "gate")
+    assert packed.shape == (N, K // 2) and scales.shape == (N, K // 32)
+    assert packed.dtype == np.uint8 and scales.dtype == np.uint8
+    w = oracle.mxfp4_decode(packed, scales)
+    scale = 2.0 ** (scales.astype(np.float64) - 127)
+    blocks = np.abs(w).reshape(N, K // 32, 32) / scale[:, :, None]
+    assert blocks.max() <= 6.0
+    assert np.all(np.isin(blocks.max(axis=2), [4.0, 6.0]))
+    bound = 1.0 / np.sqrt(K)
+    assert np.abs(w).max() <= 6.0 / 4.0 * bound * 1.0001
+    # same seed, same bits
+    p2, s2 = workloads.expert_matrix(cfg, "gate", 5)
+    assert np.array_equal(p2, packed) and np.array_equal(s2, scales)

@@ -29,17 +29,19 @@ class DeviceWeights:
     def __init__(self, cfg: MoeConfig, device="cuda", keep_host: bool = False, threads: int = 8):
         torch = _torch()
         self.cfg = cfg
-        fp8 = cfg.wdt in ("fp8", "fp8_rows")
+        fp8 = cfg.wdt in ("fp8", "fp8_rows", "mxfp4")  # byte-coded weights with scales
         rows = cfg.wdt == "fp8_rows"  # one scale per row [E, N] instead of per 128x128 block
+        mx = cfg.wdt == "mxfp4"       # packed 4-bit codes [E, N, K/2], E8M0 bytes [E, N, K/32]
         wdt = torch.uint8 if fp8 else torch.bfloat16
         self.host = {} if keep_host else None
         lock = threading.Lock()
         self.w, self.s = {}, {}
         for which in ("gate", "up", "down"):
             N, K = weight_shape(cfg, which)
-            self.w[which] = torch.empty(cfg.E, N, K, dtype=wdt, device=device)
-            sshape = (cfg.E, N) if rows else (cfg.E, N // 128, K // 128)
-            self.s[which] = torch.empty(*sshape, dtype=torch.float32, device=device) if fp8 else None
+            self.w[which] = torch.empty(cfg.E, N, K // 2 if mx else K, dtype=wdt, device=device)
+            sshape = (cfg.E, N) if rows else ((cfg.E, N, K // 32) if mx else (cfg.E, N // 128, K // 128))
+            sdt = torch.uint8 if mx else torch.float32
+            self.s[which] = torch.empty(*sshape, dtype=sdt, device=device) if fp8 else None
 
             def sink(e, bits, sc, which=which):
                 src = torch.from_numpy(bits) if fp8 else torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
@@ -84,14 +86,16 @@ class DeviceWeights:
         E = cfg.E
         flat = np.asarray(ids).reshape(-1)
         active = int(np.unique(flat[(flat >= 0) & (flat < E)]).size)
-        esz = 1 if cfg.wdt in ("fp8", "fp8_rows") else 2
+        esz = {"fp8": 1.0, "fp8_rows": 1.0, "mxfp4": 0.5}.get(cfg.wdt, 2.0)
 
         def mat(N, K):
-            b = N * K * esz
+            b = int(N * K * esz)
             if cfg.wdt == "fp8":
                 b += (N // 128) * (K // 128) * 4
             elif cfg.wdt == "fp8_rows":
                 b += N * 4
+            elif cfg.wdt == "mxfp4":
+                b += N * (K // 32)
             return b
 
         gate_up = 2 * mat(cfg.I, cfg.H) * active

@@ -14,7 +14,9 @@ are recorded in the design notes):
 * fp8 expert weights: U(-1/sqrt(K), 1/sqrt(K)) float32 draws for a K-deep
   matrix, one float32 scale per 128x128 block equal to the block's absolute
   maximum over 448 (1 for an all-zero block), codes = OCP e4m3fn of
-  ``w / scale`` rounded to nearest even (torch's float8_e4m3fn cast).
+  ``w / scale`` rounded to nearest even (torch's float8_e4m3fn cast);
+* mxfp4 expert weights: the same draws, OCP microscaling quantisation (E2M1
+  codes, one E8M0 scale per 32 columns of a row, see ``_draw_mxfp4``).
 
 Weight matrices are row-major ``[N, K]`` (output rows, input columns): gate and
 up are ``[I, H]``, down is ``[H, I]``; a shared expert uses ``S`` for ``I``.
@@ -155,6 +157,8 @@ def _draw_matrix(cfg: MoeConfig, rng: np.random.Generator, N: int, K: int):
     if cfg.wdt == "bf16":
         w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
         return bf16_bits_from_f32(w), None
+    if cfg.wdt == "mxfp4":
+        return _draw_mxfp4(rng, N, K)
     if cfg.wdt not in ("fp8", "fp8_rows"):
         raise ValueError(f"config {cfg.name} has no expert weights")
     import torch  # the float8 cast is torch's; it is the only use of torch here
@@ -179,9 +183,45 @@ def _draw_matrix(cfg: MoeConfig, rng: np.random.Generator, N: int, K: int):
     return codes.view(torch.uint8).numpy().copy(), scale
 
 
+# magnitudes of the E2M1 codes 0..7 (codes 8..15 are their negatives)
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+MX_BLOCK = 32
+
+
+def _draw_mxfp4(rng: np.random.Generator, N: int, K: int):
+    """U(-1/sqrt(K), 1/sqrt(K)) draws quantised the OCP microscaling way: per
+    32-column block of a row, scale exponent floor(log2(amax)) - 2 (2 is the
+    largest E2M1 exponent, so the block's amax lands in [4, 8)); elements
+    divided by the scale and rounded to the nearest E2M1 value (ties to the
+    even code), saturating at 6.  Returns (packed codes uint8 [N, K/2], lower
+    nibble = even column; E8M0 scale bytes uint8 [N, K/32]); an all-zero block
+    gets scale byte 127 (1.0)."""
+    if N % 128 or K % 128:
+        raise ValueError("mxfp4 weights need N and K in whole 128 blocks")
+    a = np.float32(1.0 / np.sqrt(K))
+    w = ((rng.random((N, K), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)) * a).astype(np.float64)
+    blocks = w.reshape(N, K // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    exp = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
+    exp = np.clip(exp, -127, 127)
+    q = np.abs(blocks) / np.exp2(exp)[:, :, None]
+    # nearest magnitude, ties to the even code
+    idx = np.searchsorted(_E2M1_MAG, q)  # first magnitude >= q
+    idx = np.clip(idx, 1, 7)
+    lo, hi = _E2M1_MAG[idx - 1], _E2M1_MAG[idx]
+    pick_hi = (q - lo > hi - q) | ((q - lo == hi - q) & (idx % 2 == 0))
+    code = np.where(q >= 6.0, 7, np.where(pick_hi, idx, idx - 1)).astype(np.uint8)
+    code = code | np.where(blocks < 0, 8, 0).astype(np.uint8)
+    code = code.reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(packed), (exp + 127).astype(np.uint8)
+
+
 def expert_matrix(cfg: MoeConfig, which: str, e: int):
     """Routed expert ``e``'s ``which`` matrix: (bits [N, K], scales [N/128, K/128] or None).
-    bf16 weights come as uint16 bits, fp8 weights as uint8 e4m3fn codes."""
+    bf16 weights come as uint16 bits, fp8 weights as uint8 e4m3fn codes (row
+    scales [N] for fp8_rows), mxfp4 weights as packed uint8 codes [N, K/2] with
+    E8M0 scale bytes [N, K/32]."""
     N, K = weight_shape(cfg, which)
     return _draw_matrix(cfg, _rng(cfg, _TAG_ROUTED[which], e), N, K)
 
