@@ -80,7 +80,12 @@ typedef enum { MOE_IDX_I32 = 0, MOE_IDX_I64 = 1 } moe_index_dtype;
  * block (the FP8 grouped GEMM page's block-wise scaling), or, in the _ROWS
  * forms, one per output row of each expert (the FP8 page's per-row scale of
  * its shared-expert weights, here for every expert).  A weight is the code's
- * e4m3fn value times its scale. */
+ * e4m3fn value times its scale.
+ * MXFP4 is the 4-bit expert format (the layer page's 4-bit grouped experts,
+ * in the OCP microscaling form gfx950 converts natively): E2M1 codes, two per
+ * byte, the lower nibble holding the lower k, so a row is K/2 bytes; one E8M0
+ * scale byte per 32 consecutive k of a row, [E, N, K/32] uint8.  A weight is
+ * the code's E2M1 value times 2^(scale byte - 127). */
 typedef enum {
   MOE_W_BF16 = 0,                /* bf16, row-major [E, N, K]                  */
   MOE_W_FP8_E4M3 = 1,            /* e4m3fn codes, row-major [E, N, K], scales
@@ -89,7 +94,10 @@ typedef enum {
   MOE_W_FP8_E4M3_TILED = 3,      /* e4m3fn codes, tiled; block scales as above */
   MOE_W_FP8_E4M3_ROWS = 4,       /* e4m3fn codes, row-major [E, N, K], scales
                                     [E, N] (16-byte aligned)                   */
-  MOE_W_FP8_E4M3_ROWS_TILED = 5  /* e4m3fn codes, tiled; row scales as above   */
+  MOE_W_FP8_E4M3_ROWS_TILED = 5, /* e4m3fn codes, tiled; row scales as above   */
+  MOE_W_MXFP4 = 6,               /* E2M1 codes, row-major [E, N, K/2] bytes;
+                                    E8M0 scales [E, N, K/32] (4-byte aligned)  */
+  MOE_W_MXFP4_TILED = 7          /* E2M1 codes, tiled; scales as above         */
 } moe_weight_dtype;
 
 /* Experts one align launch handles (fp8_moe_grouped.rs: the one-launch sort's
@@ -176,27 +184,33 @@ int moe_align_ws(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t t
  * bandwidth of reading 16 row-major rows side by side).  Scales are unchanged. */
 
 /* Bytes of the tiled copy of row-major weights of dtype `wdt` (MOE_W_BF16,
- * MOE_W_FP8_E4M3 or MOE_W_FP8_E4M3_ROWS: the codes tile the same way whatever
- * their scales) and shape [E, N, K]: E * N * roundup(K, 128) * element size.
+ * MOE_W_FP8_E4M3, MOE_W_FP8_E4M3_ROWS or MOE_W_MXFP4: the codes tile the same
+ * way whatever their scales) and shape [E, N, K]: E * N * roundup(K, 128) *
+ * element size (half a byte for MXFP4, whose 1 KB fragments hold two 512-byte
+ * halves, each the 64-deep half of the chunk with lane l's 8 bytes at 8*l).
  * Returns 0 for an invalid shape (the projection rules of the grouped calls). */
 size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K);
 
 /* Write the tiled copy of `src` (row-major, dtype `wdt`) into `dst` (device,
  * moe_tiled_weight_bytes bytes, must not overlap src) on `stream`.  The result
- * is used with MOE_W_BF16_TILED, MOE_W_FP8_E4M3_TILED or
- * MOE_W_FP8_E4M3_ROWS_TILED. */
+ * is used with MOE_W_BF16_TILED, MOE_W_FP8_E4M3_TILED,
+ * MOE_W_FP8_E4M3_ROWS_TILED or MOE_W_MXFP4_TILED. */
 int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K,
                      hipStream_t stream);
 
 /* ---------------------------------------------------- grouped expert FFN -- */
 
-/* One projection's weights: w is [E, N, K] (bf16 or e4m3fn codes), row-major
- * or tiled as the call's weight dtype says; scale is float32, [E, N/128, K/128]
- * for block-scaled FP8, [E, N] for row-scaled FP8, and ignored (may be NULL)
- * for BF16.  FP8 needs N and K in whole multiples of 128 either way. */
+/* One projection's weights: w is [E, N, K] (bf16 or e4m3fn codes; MXFP4:
+ * [E, N, K/2] bytes), row-major or tiled as the call's weight dtype says;
+ * scale is float32 [E, N/128, K/128] for block-scaled FP8, float32 [E, N] for
+ * row-scaled FP8, uint8 E8M0 [E, N, K/32] for MXFP4, and ignored (may be NULL)
+ * for BF16.  FP8 needs N and K in whole multiples of 128 either way; MXFP4
+ * needs K a multiple of 128 and N of 16.  MXFP4 scale bytes from 2 to 252
+ * give every weight exactly (its value is a bf16); outside that range (255 is
+ * E8M0's NaN) the results are not specified. */
 typedef struct {
   const void* w;
-  const float* scale;
+  const void* scale;
 } moe_weight;
 
 /* act[p, :] = silu(g) * u with g = W_gate[e] x[t], u = W_up[e] x[t] for every
@@ -206,8 +220,8 @@ typedef struct {
  * the same launch writes sh_act[t, :] (float32 [M, S]) for every token.
  * `t` are the tables moe_align wrote for the same topk_ids.
  * Shapes: FP8 needs H, I, S multiples of 128; BF16 needs H multiple of 32 and
- * I, S multiples of 16.  Errors as for moe_align, plus MOE_ERR_SHAPE for the
- * block rules above. */
+ * I, S multiples of 16; MXFP4 needs H a multiple of 128 and I, S of 16.
+ * Errors as for moe_align, plus MOE_ERR_SHAPE for the block rules above. */
 int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe_weight* gate,
                              const moe_weight* up, const moe_align_tables* t, float* act,
                              const moe_weight* sh_gate, const moe_weight* sh_up, float* sh_act,
@@ -236,7 +250,8 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
  * (float32 [M, H]).  The depth is summed in 64-deep halves of 128-deep chunks,
  * ascending, from 0: each half's float32 product (times its block or row scale, FP8)
  * is rounded and then added, with no fused multiply-add across halves.  Shapes: FP8 needs H,
- * I, S multiples of 128; BF16 needs I, S multiples of 32 and H a multiple of 16. */
+ * I, S multiples of 128; BF16 needs I, S multiples of 32 and H a multiple of 16;
+ * MXFP4 needs I, S multiples of 128 and H of 16. */
 int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down,
                      const moe_align_tables* t, float* expert_out, const moe_weight* sh_down,
                      const float* sh_act, float* sh_out, int64_t M, int32_t H, int32_t I,

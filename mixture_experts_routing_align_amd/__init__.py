@@ -14,10 +14,12 @@ Entry points (same names as the C ABI): ``moe_align``,
 
 Weights are passed as ``(w, scale)`` pairs: ``w`` is ``[E, N, K]``
 ``torch.uint8`` e4m3fn codes with ``scale`` float32 ``[E, N/128, K/128]`` (one
-per 128x128 block) or ``[E, N]`` (one per row), or ``torch.bfloat16`` with
+per 128x128 block) or ``[E, N]`` (one per row), or ``[E, N, K/2]``
+``torch.uint8`` MXFP4 codes (two E2M1 codes per byte, lower nibble first) with
+``scale`` ``torch.uint8`` E8M0 ``[E, N, K/32]``, or ``torch.bfloat16`` with
 ``scale`` None - or as the :class:`TiledWeight` that ``moe_tile_weights`` makes
 from such a pair.  A shared expert's ``[N, K]`` matrix takes ``[N/128, K/128]``
-or ``[N]`` scales.
+or ``[N]`` scales (MXFP4: ``[N, K/2]`` codes, ``[N, K/32]`` scales).
 """
 
 from __future__ import annotations
@@ -52,6 +54,8 @@ from ._ffi import (  # noqa: F401
     MOE_W_FP8_E4M3_ROWS,
     MOE_W_FP8_E4M3_ROWS_TILED,
     MOE_W_FP8_E4M3_TILED,
+    MOE_W_MXFP4,
+    MOE_W_MXFP4_TILED,
     TABLE_FIELDS,
     MoeAlignTables,
     MoeLayerDesc,
@@ -178,12 +182,15 @@ class TiledWeight:
 
 def weight_dtype(w) -> int:
     """The weight dtype of a pair, a tiled weight or a bare tensor; FP8 scales
-    with one dimension fewer than the codes are row scales."""
+    with one dimension fewer than the codes are row scales, and byte codes with
+    byte scales are MXFP4."""
     s = None
     if isinstance(w, TiledWeight):
         return w.wdt
     if isinstance(w, tuple):
         w, s = w
+    if w.dtype == torch.uint8 and s is not None and s.dtype == torch.uint8:
+        return MOE_W_MXFP4
     if w.dtype in (torch.uint8, torch.float8_e4m3fn):
         return MOE_W_FP8_E4M3_ROWS if s is not None and s.dim() == w.dim() - 1 else MOE_W_FP8_E4M3
     if w.dtype == torch.bfloat16:
@@ -197,6 +204,8 @@ def weight_shape(wt) -> Tuple[int, int, int]:
     if isinstance(wt, TiledWeight):
         return tuple(wt.shape)
     shape = tuple(wt[0].shape)
+    if weight_dtype(wt) == MOE_W_MXFP4:  # two codes per byte
+        shape = shape[:-1] + (2 * shape[-1],)
     return (1,) + shape if len(shape) == 2 else shape
 
 
@@ -207,7 +216,8 @@ def _weight(wt) -> Optional[MoeWeight]:
         return MoeWeight(wt.w.data_ptr(), _ptr(wt.scale))
     w, s = wt
     _need(w.is_contiguous() and (s is None or s.is_contiguous()), "weights must be contiguous")
-    if weight_dtype(w) == MOE_W_FP8_E4M3:
+    wdt = weight_dtype(wt)
+    if wdt in (MOE_W_FP8_E4M3, MOE_W_FP8_E4M3_ROWS):
         _need(s is not None and s.dtype == torch.float32, "FP8 weights need float32 scales")
     return MoeWeight(w.data_ptr(), _ptr(s))
 
@@ -228,7 +238,7 @@ def moe_tile_weights(wt: Weight, stream=None) -> TiledWeight:
     dst = torch.empty(moe_tiled_weight_bytes(wdt, E, N, K), dtype=torch.uint8, device=w.device)
     _check(lib().moe_tile_weights(w.data_ptr(), dst.data_ptr(), wdt, E, N, K, _stream(stream)))
     tiled = {MOE_W_FP8_E4M3: MOE_W_FP8_E4M3_TILED, MOE_W_FP8_E4M3_ROWS: MOE_W_FP8_E4M3_ROWS_TILED,
-             MOE_W_BF16: MOE_W_BF16_TILED}[wdt]
+             MOE_W_BF16: MOE_W_BF16_TILED, MOE_W_MXFP4: MOE_W_MXFP4_TILED}[wdt]
     return TiledWeight(dst, s, tiled, (E, N, K))
 
 

@@ -23,6 +23,8 @@ MOE_W_BF16_TILED = 2
 MOE_W_FP8_E4M3_TILED = 3
 MOE_W_FP8_E4M3_ROWS = 4
 MOE_W_FP8_E4M3_ROWS_TILED = 5
+MOE_W_MXFP4 = 6
+MOE_W_MXFP4_TILED = 7
 MOE_MAX_EXPERTS = 1024
 MOE_ROUTER_MAX_TOP_K = 64
 MOE_FUSED_ALIGN_MAX_SLOTS = 2048

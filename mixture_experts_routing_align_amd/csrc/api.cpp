@@ -89,9 +89,13 @@ int check_tables(const char* fn, const moe_align_tables* t, bool all) {
 
 bool is_rows(moe_weight_dtype wdt) { return wdt == MOE_W_FP8_E4M3_ROWS || wdt == MOE_W_FP8_E4M3_ROWS_TILED; }
 bool is_fp8(moe_weight_dtype wdt) { return wdt == MOE_W_FP8_E4M3 || wdt == MOE_W_FP8_E4M3_TILED || is_rows(wdt); }
+bool is_fp4(moe_weight_dtype wdt) { return wdt == MOE_W_MXFP4 || wdt == MOE_W_MXFP4_TILED; }
 bool is_tiled(moe_weight_dtype wdt) {
-  return wdt == MOE_W_BF16_TILED || wdt == MOE_W_FP8_E4M3_TILED || wdt == MOE_W_FP8_E4M3_ROWS_TILED;
+  return wdt == MOE_W_BF16_TILED || wdt == MOE_W_FP8_E4M3_TILED || wdt == MOE_W_FP8_E4M3_ROWS_TILED ||
+         wdt == MOE_W_MXFP4_TILED;
 }
+// the kernels' element format of a weight dtype
+int fmt_of(moe_weight_dtype wdt) { return is_fp4(wdt) ? moe::kFmtFP4 : (is_fp8(wdt) ? moe::kFmtFP8 : moe::kFmtBF16); }
 
 // The kernels move weights, x, act and the float32 intermediates 16 bytes per
 // lane and the bf16 output 8 bytes per lane: a pointer off that alignment is
@@ -110,21 +114,30 @@ int check_weight(const char* fn, const char* name, const moe_weight* w, moe_weig
   // per-row scales are read four rows at a time
   if (is_rows(wdt) && reinterpret_cast<uintptr_t>(w->scale) % 16)
     return fail(MOE_ERR_SHAPE, "%s: %s FP8 row scales are not 16-byte aligned", fn, name);
+  if (is_fp4(wdt) && w->scale == nullptr) return fail(MOE_ERR_NULL, "%s: %s MXFP4 scales are NULL", fn, name);
+  // a row's four scale bytes of one 128-deep chunk are read as one dword
+  if (is_fp4(wdt) && reinterpret_cast<uintptr_t>(w->scale) % 4)
+    return fail(MOE_ERR_SHAPE, "%s: %s MXFP4 scales are not 4-byte aligned", fn, name);
   return MOE_OK;
 }
 
 int check_wdt(const char* fn, moe_weight_dtype wdt) {
-  if (wdt < MOE_W_BF16 || wdt > MOE_W_FP8_E4M3_ROWS_TILED)
+  if (wdt < MOE_W_BF16 || wdt > MOE_W_MXFP4_TILED)
     return fail(MOE_ERR_SHAPE, "%s: unknown weight dtype %d", fn, (int)wdt);
   return MOE_OK;
 }
 
 // A projection with N output rows and depth K: FP8 needs whole 128x128 scale
 // blocks (with per-row scales too: the kernels walk K in the same 128-deep
-// chunks); BF16 needs K in whole 32-deep MFMA steps and N in whole 16-row tiles.
+// chunks); MXFP4 needs K in whole 128-deep chunks (four scale bytes each) and
+// N in whole 16-row tiles; BF16 needs K in whole 32-deep MFMA steps and N in
+// whole 16-row tiles.
 int check_projection(const char* fn, const char* name, moe_weight_dtype wdt, int32_t N, int32_t K) {
   if (N < 1 || K < 1) return fail(MOE_ERR_SHAPE, "%s: %s is %dx%d", fn, name, N, K);
-  if (is_fp8(wdt)) {
+  if (is_fp4(wdt)) {
+    if (N % 16 || K % 128)
+      return fail(MOE_ERR_SHAPE, "%s: MXFP4 %s is %dx%d; needs N %% 16 == 0 and K %% 128 == 0", fn, name, N, K);
+  } else if (is_fp8(wdt)) {
     if (N % moe::kFp8Block || K % moe::kFp8Block)
       return fail(MOE_ERR_SHAPE, "%s: FP8 %s is %dx%d, not whole 128x128 scale blocks", fn, name, N, K);
   } else if (N % 16 || K % 32) {
@@ -197,7 +210,7 @@ int forced_path() {
 // A forced single pass that does not fit is refused.
 int layer_path(const char* fn, const moe_layer_desc* d) {
   const bool fits = is_tiled(d->wdt) &&
-                    moe::fused_layer_fits(is_fp8(d->wdt), is_rows(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
+                    moe::fused_layer_fits(fmt_of(d->wdt), is_rows(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
   const int want = d->path != MOE_LAYER_PATH_AUTO ? (int)d->path : forced_path();
   if (want == MOE_LAYER_PATH_STEPS) return MOE_LAYER_PATH_STEPS;
   if (want == MOE_LAYER_PATH_SINGLE_PASS && !fits)
@@ -220,8 +233,8 @@ void log_path_once(const moe_layer_desc* d, int path) {
   const unsigned bit = 1u << path;
   if (logged.fetch_or(bit) & bit) return;
   static const char* names[] = {"auto", "steps", "single_pass"};
-  static const char* wnames[] = {"bf16", "fp8_e4m3", "bf16_tiled", "fp8_e4m3_tiled", "fp8_e4m3_rows",
-                                 "fp8_e4m3_rows_tiled"};
+  static const char* wnames[] = {"bf16",          "fp8_e4m3",            "bf16_tiled", "fp8_e4m3_tiled",
+                                 "fp8_e4m3_rows", "fp8_e4m3_rows_tiled", "mxfp4",      "mxfp4_tiled"};
   fprintf(stderr,
           "moe_mi355x: moe_layer_forward path %s (M=%lld H=%d I=%d S=%d E=%d top_k=%d BS=%d weights %s%s)\n",
           names[path], (long long)d->M, d->H, d->I, d->S, d->E, d->top_k, d->BS, wnames[d->wdt],
@@ -280,7 +293,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 9; }
+int32_t moe_abi_version(void) { return 10; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -368,7 +381,7 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
   moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
   a.scale_rows = is_rows(wdt);
   return hip_status(
-      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
+      moe::launch_grouped_gate_up(a, fmt_of(wdt), is_tiled(wdt), stream), fn);
 }
 
 int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void* x_bf16, moe_weight_dtype wdt,
@@ -412,7 +425,7 @@ int moe_align_gate_up_silu(const void* topk_ids, moe_index_dtype idt, const void
   a.tables = to_align_out(*t);
   a.scale_rows = is_rows(wdt);
   return hip_status(
-      moe::launch_grouped_gate_up(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
+      moe::launch_grouped_gate_up(a, fmt_of(wdt), is_tiled(wdt), stream), fn);
 }
 
 int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* down, const moe_align_tables* t,
@@ -459,7 +472,7 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
   a.cap = s.cap;
   a.scale_rows = is_rows(wdt);
   return hip_status(
-      moe::launch_grouped_down(a, is_fp8(wdt), is_tiled(wdt), stream), fn);
+      moe::launch_grouped_down(a, fmt_of(wdt), is_tiled(wdt), stream), fn);
 }
 
 int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights, const int32_t* token_to_perm,
@@ -484,7 +497,7 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
 
 size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K) {
   const char* fn = "moe_tiled_weight_bytes";
-  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3 && wdt != MOE_W_FP8_E4M3_ROWS) {
+  if (wdt != MOE_W_BF16 && wdt != MOE_W_FP8_E4M3 && wdt != MOE_W_FP8_E4M3_ROWS && wdt != MOE_W_MXFP4) {
     fail(MOE_ERR_SHAPE, "%s: source dtype %d is not a row-major dtype", fn, (int)wdt);
     return 0;
   }
@@ -492,7 +505,7 @@ size_t moe_tiled_weight_bytes(moe_weight_dtype wdt, int64_t E, int32_t N, int32_
     if (E < 1) fail(MOE_ERR_SHAPE, "%s: E=%lld", fn, (long long)E);
     return 0;
   }
-  return moe::tiled_weight_bytes(is_fp8(wdt), E, N, K);
+  return moe::tiled_weight_bytes(fmt_of(wdt), E, N, K);
 }
 
 int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E, int32_t N, int32_t K,
@@ -503,7 +516,7 @@ int moe_tile_weights(const void* src, void* dst, moe_weight_dtype wdt, int64_t E
   if (src == dst) return fail(MOE_ERR_SHAPE, "%s: src and dst must not alias", fn);
   int rc;
   if ((rc = check_aligned(fn, "src", src, 16)) || (rc = check_aligned(fn, "dst", dst, 16))) return rc;
-  return hip_status(moe::launch_tile_weights(src, dst, is_fp8(wdt), E, N, K, stream), fn);
+  return hip_status(moe::launch_tile_weights(src, dst, fmt_of(wdt), E, N, K, stream), fn);
 }
 
 int moe_layer_workspace_layout(const moe_layer_desc* d, size_t offsets[MOE_LAYER_WORKSPACE_REGIONS + 1]) {
@@ -619,7 +632,7 @@ int moe_layer_partials(const moe_layer_desc* d, const void* x_bf16, const void* 
   if ((rc = check_aligned(fn, "x", x_bf16, 16))) return rc;
   const moe::FusedLayerArgs a =
       single_pass_args(d, static_cast<char*>(workspace), off, x_bf16, topk_ids, nullptr, nullptr);
-  return hip_status(moe::launch_layer_partials(a, is_fp8(d->wdt), stream), fn);
+  return hip_status(moe::launch_layer_partials(a, fmt_of(d->wdt), stream), fn);
 }
 
 int moe_layer_blend_partials(const moe_layer_desc* d, const void* x_bf16, const void* topk_ids,
@@ -655,7 +668,7 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
   char* ws = static_cast<char*>(workspace);
   if (path == MOE_LAYER_PATH_SINGLE_PASS) {
     const moe::FusedLayerArgs a = single_pass_args(d, ws, off, x_bf16, topk_ids, topk_weights, out_bf16);
-    if ((rc = hip_status(moe::launch_layer_partials(a, is_fp8(d->wdt), stream), fn))) return rc;
+    if ((rc = hip_status(moe::launch_layer_partials(a, fmt_of(d->wdt), stream), fn))) return rc;
     return hip_status(moe::launch_blend_partials(a, stream), fn);
   }
   const bool shared = d->S > 0;

@@ -4,8 +4,8 @@
 namespace moe {
 
 hipError_t launch_down_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
-  return a.scale_rows ? grouped_detail::launch<true, true, false>(a, rowcap, tiled, s)
-                      : grouped_detail::launch<true, false, false>(a, rowcap, tiled, s);
+  return a.scale_rows ? grouped_detail::launch<kFmtFP8, true, false>(a, rowcap, tiled, s)
+                      : grouped_detail::launch<kFmtFP8, false, false>(a, rowcap, tiled, s);
 }
 
 }  // namespace moe

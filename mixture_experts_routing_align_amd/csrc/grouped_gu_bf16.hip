@@ -4,7 +4,7 @@
 namespace moe {
 
 hipError_t launch_gate_up_bf16(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
-  return grouped_detail::launch<false, false, true>(a, rowcap, tiled, s);
+  return grouped_detail::launch<kFmtBF16, false, true>(a, rowcap, tiled, s);
 }
 
 }  // namespace moe

@@ -4,8 +4,8 @@
 namespace moe {
 
 hipError_t launch_gate_up_fp8(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
-  return a.scale_rows ? grouped_detail::launch<true, true, true>(a, rowcap, tiled, s)
-                      : grouped_detail::launch<true, false, true>(a, rowcap, tiled, s);
+  return a.scale_rows ? grouped_detail::launch<kFmtFP8, true, true>(a, rowcap, tiled, s)
+                      : grouped_detail::launch<kFmtFP8, false, true>(a, rowcap, tiled, s);
 }
 
 }  // namespace moe

@@ -19,7 +19,10 @@
 //    convert exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, scale
 //    1); bf16 activations are exact, so the only rounding is the float32
 //    accumulation.  Each 128-deep FP8 scale block is accumulated alone and then
-//    multiplied by its scale.  The down projection's float32 input is split into
+//    multiplied by its scale.  MXFP4 codes convert to bf16 with their 32-deep
+//    block's E8M0 scale applied in the same instruction
+//    (v_cvt_scalef32_pk_bf16_fp4): a power-of-two multiple of an E2M1 value is
+//    exact in bf16, so these accumulate like bf16 weights.  The down projection's float32 input is split into
 //    bf16 hi + lo and both halves go through the matrix core, so it keeps ~16
 //    bits of the input's mantissa.
 //  * Memory: each lane streams 16-byte (dwordx4) loads of its weight row,
@@ -68,6 +71,7 @@ __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
   return ((size_t)kWaves * E + E + (E + 1) + E + 2 * kWaves + 2 + n) * sizeof(int);
 }
 
+// FMT: the weight format (kFmtBF16, kFmtFP8, kFmtFP4).
 // ROWS (FP8 only): one float32 scale per weight row, [E, N], instead of one per
 // 128x128 block; it multiplies the same places the block scale does (each
 // 128-deep gate/up chunk's sum, each 64-deep down half), per output column.
@@ -75,12 +79,15 @@ __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
 // time, one barrier per chunk), kResident (the whole depth at once, no barrier
 // in the weight stream), or kRoutedResident (routed items resident, the shared
 // expert's deeper rows staged; chosen when only the routed depth fits in LDS).
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
+template <int FMT, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
 __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int rowcap, int ctw, size_t xs_bytes) {
+  constexpr bool FP8 = FMT == kFmtFP8;
+  constexpr bool FP4 = FMT == kFmtFP4;
+  constexpr bool BMAP = FMT != kFmtBF16;  // byte-coded weights: whole 128-deep chunks, the FP8 k map
   constexpr int NS = GATE_UP ? 2 : 1;   // weight streams (gate, up) or (down)
   constexpr int NX = GATE_UP ? 1 : 2;   // B planes: bf16 x, or bf16 hi + lo of act
-  constexpr int WL = FP8 ? 2 : 4;       // 16-byte weight loads per lane per chunk
-  constexpr int ESZ = FP8 ? 1 : 2;      // weight element bytes
+  constexpr int WL = FP4 ? 1 : (FP8 ? 2 : 4);  // 16 bytes of weights per lane per chunk, in WL registers
+  constexpr int ESZ = FP8 ? 1 : 2;      // weight element bytes (MXFP4: half a byte, see wbytes)
   constexpr int NBUF = RES == kStaged ? 2 : 3;  // weight chunks in the register ring
   constexpr int EPP = GATE_UP ? 8 : 4;  // source elements per 16-byte staging piece
   constexpr int SL = kMaxScaleBlocks / 64;  // scale registers per stream (one scale per lane)
@@ -190,26 +197,36 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     rows = min(rowcap, p.M - row_base);
   }
 
+  // bytes of n weight elements
+  auto wbytes = [](size_t n) -> size_t { return FP4 ? n / 2 : n * ESZ; };
   const char *W0, *W1 = nullptr;
-  const float *S0 = nullptr, *S1 = nullptr;
+  const float *S0 = nullptr, *S1 = nullptr;      // FP8 scales
+  const uint8_t *B0 = nullptr, *B1 = nullptr;    // MXFP4 E8M0 scale bytes [N, K/32]
   const char* X;
   float* OUT;
   if (routed) {
-    const size_t wstride = (size_t)N * (TILED ? round_up(K, kKC) : K) * ESZ;
+    const size_t wstride = wbytes((size_t)N * (TILED ? round_up(K, kKC) : K));
     W0 = static_cast<const char*>(p.w0) + (size_t)e * wstride;
     if (GATE_UP) W1 = static_cast<const char*>(p.w1) + (size_t)e * wstride;
     if (FP8) {
       const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
-      S0 = p.s0 + (size_t)e * sstride;
-      if (GATE_UP) S1 = p.s1 + (size_t)e * sstride;
+      S0 = static_cast<const float*>(p.s0) + (size_t)e * sstride;
+      if (GATE_UP) S1 = static_cast<const float*>(p.s1) + (size_t)e * sstride;
+    }
+    if (FP4) {
+      const size_t sstride = (size_t)N * (K / kMxBlock);
+      B0 = static_cast<const uint8_t*>(p.s0) + (size_t)e * sstride;
+      if (GATE_UP) B1 = static_cast<const uint8_t*>(p.s1) + (size_t)e * sstride;
     }
     X = static_cast<const char*>(p.x);
     OUT = p.out;
   } else {
     W0 = static_cast<const char*>(p.sw0);
     W1 = static_cast<const char*>(p.sw1);
-    S0 = p.ss0;
-    S1 = p.ss1;
+    S0 = static_cast<const float*>(p.ss0);
+    S1 = static_cast<const float*>(p.ss1);
+    B0 = static_cast<const uint8_t*>(p.ss0);
+    B1 = static_cast<const uint8_t*>(p.ss1);
     X = static_cast<const char*>(p.sx);
     OUT = p.sout;
   }
@@ -227,8 +244,10 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   };
   // row-major: this lane's weight row (A operand row r16 of the wave's tile);
   // tiled: the wave's 16-row tile, one contiguous run of 128-deep fragments
+  // (MXFP4: each fragment two 512-byte halves, this lane's 8 bytes at 8 * lane)
   auto lane_offset = [&](int wcol) -> size_t {
-    return TILED ? (size_t)(wcol / kWaveCols) * kpad * kWaveCols * ESZ + lane * 16 : (size_t)(wcol + r16) * K * ESZ;
+    return TILED ? wbytes((size_t)(wcol / kWaveCols) * kpad * kWaveCols) + lane * (FP4 ? 8 : 16)
+                 : wbytes((size_t)(wcol + r16) * K);
   };
 
   // load cursor: tile `lt`, chunk `lc` of the next weight load, and this lane's
@@ -236,18 +255,41 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   int lt = t_begin, lc = 0;
   const char* lp0 = nullptr;
   const char* lp1 = nullptr;
+  const uint8_t* lb0 = nullptr;  // MXFP4: this lane's row of scale bytes
+  const uint8_t* lb1 = nullptr;
   auto set_load_tile = [&](int t) {
     bool on;
-    const size_t lo = lane_offset(wave_col(t, on));
+    const int wcol = wave_col(t, on);
+    const size_t lo = lane_offset(wcol);
     lp0 = W0 + lo;
     if (GATE_UP) lp1 = W1 + lo;
+    if (FP4) {
+      lb0 = B0 + (size_t)(wcol + r16) * (K / kMxBlock);
+      if (GATE_UP) lb1 = B1 + (size_t)(wcol + r16) * (K / kMxBlock);
+    }
   };
   // unconditional loads of the cursor's chunk, then advance the cursor (past the
   // last step it stays on the last chunk, which is then loaded again): the
-  // steady state has no branch around loads and no integer division
-  auto load_next = [&](uint4 (&wr)[NS][WL]) {
+  // steady state has no branch around loads and no integer division.  MXFP4:
+  // the lane's 16 bytes are half 0 then half 1 of the chunk (k = 64h + 16q ..
+  // +15 each), and `sr` gets the row's four scale bytes of the chunk.
+  auto load_next = [&](uint4 (&wr)[NS][WL], uint32_t (&sr)[NS]) {
+    if constexpr (FP4) {
+      const size_t off = TILED ? (size_t)lc * 1024 : (size_t)lc * (kKC / 2) + 8 * q;
+      const size_t hoff = TILED ? 512 : 32;
+      const uint2 a0 = *reinterpret_cast<const uint2*>(lp0 + off);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(lp0 + off + hoff);
+      wr[0][0] = uint4{a0.x, a0.y, a1.x, a1.y};
+      sr[0] = *reinterpret_cast<const uint32_t*>(lb0 + 4 * lc);
+      if (GATE_UP) {
+        const uint2 b0 = *reinterpret_cast<const uint2*>(lp1 + off);
+        const uint2 b1 = *reinterpret_cast<const uint2*>(lp1 + off + hoff);
+        wr[NS - 1][0] = uint4{b0.x, b0.y, b1.x, b1.y};
+        sr[NS - 1] = *reinterpret_cast<const uint32_t*>(lb1 + 4 * lc);
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < WL; ++j) {
+    for (int j = 0; j < (FP4 ? 0 : WL); ++j) {
       if (TILED) {
         const size_t off = (size_t)lc * kKC * kWaveCols * ESZ + j * 1024;
         wr[0][j] = *reinterpret_cast<const uint4*>(lp0 + off);
@@ -274,9 +316,10 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
 
   // the first weight chunks of the first pass go out before anything else
   uint4 wb[NBUF][NS][WL];
+  uint32_t sb[NBUF][NS];  // MXFP4 scale bytes of each ring chunk (unused otherwise)
   set_load_tile(lt);
 #pragma unroll
-  for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j]);
+  for (int j = 0; j < NBUF - 1; ++j) load_next(wb[j], sb[j]);
 
   // the FP8 scales of a tile's 16 columns of this wave: one 128-deep block per
   // lane, or (ROWS) the scales of this lane's 4 output columns
@@ -372,14 +415,20 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     zero_acc();
 
     // multiply chunk c: A from registers, B from LDS slot `slot` at element `kb`
-    auto compute = [&](const uint4 (&wc)[NS][WL], int slot, int kb, int c) {
+    auto compute = [&](const uint4 (&wc)[NS][WL], const uint32_t (&scb)[NS], int slot, int kb, int c) {
       const int k0 = c * kKC;
       bf16x8 a[NS][4];
 #pragma unroll
       for (int st = 0; st < NS; ++st)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          if (FP8) {
+          if constexpr (FP4) {
+            // step s lies in half s / 2, whose 16 k of this lane are 32-deep
+            // block 2 (s / 2) + q / 2 of the chunk
+            const uint4 v = wc[st][0];
+            const uint32_t d = s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
+            a[st][s] = fp4x8_to_bf16(d, e8m0_to_f32(scb[st] >> (16 * (s >> 1) + 8 * (q >> 1))));
+          } else if constexpr (FP8) {
             const uint4 v = wc[st][s >> 1];
             a[st][s] = (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
           } else {
@@ -411,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
 #pragma unroll
             for (int s = 0; s < 4; ++s)
               b[x][s] = as_bf16x8(
-                  *reinterpret_cast<const uint4*>(xb + x * plane + rowc * stride + k_of_step<FP8>(s, q)));
+                  *reinterpret_cast<const uint4*>(xb + x * plane + rowc * stride + k_of_step<BMAP>(s, q)));
 #pragma unroll
           for (int st = 0; st < NS; ++st) {
             if (GATE_UP && FP8) {
@@ -424,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
               // bf16 depth comes in whole 32-deep steps; steps past K are skipped
 #pragma unroll
               for (int s = 0; s < 4; ++s)
-                if (k0 + s * 32 < K) acc[st][rt] = mfma(a[st][s], b[0][s], acc[st][rt]);
+                if (BMAP || k0 + s * 32 < K) acc[st][rt] = mfma(a[st][s], b[0][s], acc[st][rt]);
             } else {
               // down: each 64-deep half of the chunk is multiplied from zero,
               // scaled (FP8), rounded and then added to the sum (no fused
@@ -433,11 +482,11 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
               // bf16 steps past K are skipped, a half wholly past K adds nothing
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
-                if (FP8 || k0 + 64 * h < K) {
+                if (BMAP || k0 + 64 * h < K) {
                   f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                   for (int s = 2 * h; s < 2 * h + 2; ++s)
-                    if (FP8 || k0 + s * 32 < K)
+                    if (BMAP || k0 + s * 32 < K)
 #pragma unroll
                       for (int x = 0; x < NX; ++x) t = mfma(a[st][s], b[x][s], t);
 #pragma unroll
@@ -480,8 +529,8 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     int ct = t_begin, cc = 0;
     bool con;
     int cwcol = wave_col(ct, con);
-    auto step = [&](const uint4 (&wc)[NS][WL], int slot, int kb) {
-      if (con) compute(wc, slot, kb, cc);
+    auto step = [&](const uint4 (&wc)[NS][WL], const uint32_t (&scb)[NS], int slot, int kb) {
+      if (con) compute(wc, scb, slot, kb, cc);
       if (cc + 1 < nch) {
         ++cc;
       } else {
@@ -517,8 +566,8 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       for (int v0 = 0; v0 < nv; v0 += NBUF) {
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) {
-          load_next(wb[(j + NBUF - 1) % NBUF]);
-          if (v0 + j < nv) step(wb[j], 0, cc * kKC);
+          load_next(wb[(j + NBUF - 1) % NBUF], sb[(j + NBUF - 1) % NBUF]);
+          if (v0 + j < nv) step(wb[j], sb[j], 0, cc * kKC);
         }
       }
     } else {
@@ -550,8 +599,8 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
           const int v = v0 + j;
           if (v < nv) {
             load_x(cc + 1 < nch ? cc + 1 : 0);  // issued before the weights: waiting on it leaves them in flight
-            load_next(wb[(j + NBUF - 1) % NBUF]);
-            step(wb[j], v & 1, 0);
+            load_next(wb[(j + NBUF - 1) % NBUF], sb[(j + NBUF - 1) % NBUF]);
+            step(wb[j], sb[j], v & 1, 0);
             if (v + 1 < nv) store_x((v + 1) & 1);
             __syncthreads();
           }
@@ -574,9 +623,9 @@ inline int device_cus() {
   return cus[dev];
 }
 
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
+template <int FMT, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
 hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
-  auto kern = grouped_kernel<FP8, ROWS, GATE_UP, RT, RES, TILED, FUSED, IdT>;
+  auto kern = grouped_kernel<FMT, ROWS, GATE_UP, RT, RES, TILED, FUSED, IdT>;
   const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
   static std::atomic<size_t> allowed[kMaxCachedDevices];
   hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, allowed);
@@ -603,17 +652,17 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
   return hipGetLastError();
 }
 
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED>
+template <int FMT, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED>
 hipError_t launch_fused_or_not(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   if (GATE_UP && a.ids != nullptr) {
     if (a.ids64)
-      return launch_one<FP8, ROWS, GATE_UP, RT, RES, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
-    return launch_one<FP8, ROWS, GATE_UP, RT, RES, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
+      return launch_one<FMT, ROWS, GATE_UP, RT, RES, TILED, GATE_UP, int64_t>(a, rowcap, xs_bytes, tiles, s);
+    return launch_one<FMT, ROWS, GATE_UP, RT, RES, TILED, GATE_UP, int32_t>(a, rowcap, xs_bytes, tiles, s);
   }
-  return launch_one<FP8, ROWS, GATE_UP, RT, RES, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
+  return launch_one<FMT, ROWS, GATE_UP, RT, RES, TILED, false, int32_t>(a, rowcap, xs_bytes, tiles, s);
 }
 
-template <bool FP8, bool ROWS, bool GATE_UP, int RT, bool TILED>
+template <int FMT, bool ROWS, bool GATE_UP, int RT, bool TILED>
 hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   constexpr int NX = GATE_UP ? 1 : 2;
   const int kmax = (a.sw0 != nullptr && a.sK > a.K) ? a.sK : a.K;
@@ -629,20 +678,20 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   const int64_t n = (int64_t)a.M * a.top_k;
   b.items = (int)((n + (int64_t)a.cap * (rowcap - 1)) / rowcap);
   if (resident <= kResidentLdsBudget)
-    return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, kResident, TILED>(b, rowcap, resident, tiles, s);
+    return launch_fused_or_not<FMT, ROWS, GATE_UP, RT, kResident, TILED>(b, rowcap, resident, tiles, s);
   // only the shared expert's depth is too deep: its items stage 128 deep at a
   // time while the routed items keep their rows resident
   if (routed_resident <= kResidentLdsBudget)
-    return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, kRoutedResident, TILED>(
+    return launch_fused_or_not<FMT, ROWS, GATE_UP, RT, kRoutedResident, TILED>(
         b, rowcap, std::max(routed_resident, chunked), tiles, s);
-  return launch_fused_or_not<FP8, ROWS, GATE_UP, RT, kStaged, TILED>(b, rowcap, chunked, tiles, s);
+  return launch_fused_or_not<FMT, ROWS, GATE_UP, RT, kStaged, TILED>(b, rowcap, chunked, tiles, s);
 }
 
 // one 16-row tile per pass: each pass of an expert is a workgroup of its own
-template <bool FP8, bool ROWS, bool GATE_UP>
+template <int FMT, bool ROWS, bool GATE_UP>
 hipError_t launch(const GroupedArgs& a, int rowcap, bool tiled, hipStream_t s) {
-  return tiled ? launch_rt<FP8, ROWS, GATE_UP, 1, true>(a, rowcap, s)
-               : launch_rt<FP8, ROWS, GATE_UP, 1, false>(a, rowcap, s);
+  return tiled ? launch_rt<FMT, ROWS, GATE_UP, 1, true>(a, rowcap, s)
+               : launch_rt<FMT, ROWS, GATE_UP, 1, false>(a, rowcap, s);
 }
 
 }  // namespace grouped_detail

@@ -66,23 +66,30 @@ __host__ __device__ constexpr size_t act_lds_bytes(int rowcap, bool split) {
 // tiles, two 128-deep chunks per step, and the up sums reach the gate waves
 // through LDS; each wave then streams half the bytes, which helps when the
 // whole layer is only a few hundred workgroups.  Same arithmetic either way.
+// FMT: the weight format (kFmtBF16, kFmtFP8, kFmtFP4).  MXFP4 codes become
+// bf16 with their E8M0 block scale in the conversion (exact), so they
+// accumulate as bf16 weights do; their scale bytes ride the register ring
+// with the codes (one dword per row and chunk).
 // ROWS (FP8 only): one float32 scale per weight row ([E, N]) instead of one
 // per 128x128 block; it multiplies where the block scale does, per output
 // column (gate/up: the lane's 4 intermediate columns; down: its 4 rows of H,
 // read from a copy of the expert's down row scales in LDS).
-template <bool FP8, bool ROWS, int RT, typename IdT, int W>
+template <int FMT, bool ROWS, int RT, typename IdT, int W>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 ? 3 : 2))) void layer_kernel(
     FusedLayerArgs p, int rowcap, size_t xs_bytes, size_t act_bytes) {
   constexpr int kWaves = W;
   constexpr int kThreads = W * 64;
   constexpr bool SPLIT = W == 2 * kColTiles;
   static_assert(W == kColTiles || SPLIT, "4 waves (gate + up per wave) or 8 (gate and up on separate waves)");
-  constexpr int WL = FP8 ? 2 : 4;             // 16-byte loads per lane per 16x128 fragment
-  constexpr int HL = WL / 2;                  // per 64-deep half fragment
-  constexpr int NL = 2 * WL;                  // loads per lane per step (both phases)
-  constexpr int ESZ = FP8 ? 1 : 2;
-  constexpr int FB = kWaveCols * kKC * ESZ;   // bytes of one fragment
-  constexpr int NBUF = FP8 ? 3 : 2;           // steps in the register ring
+  constexpr bool FP8 = FMT == kFmtFP8;
+  constexpr bool FP4 = FMT == kFmtFP4;
+  constexpr bool BMAP = FMT != kFmtBF16;      // byte-coded weights: whole chunks, the byte k map
+  constexpr int WL = FP4 ? 1 : (FP8 ? 2 : 4); // 16-byte registers per lane per 16x128 fragment
+  constexpr int HL = FP8 ? 1 : 2;             // per 64-deep half fragment (MXFP4: 8 bytes, half a register)
+  constexpr int NL = 2 * WL;                  // registers per lane per step (both phases)
+  constexpr int FB = kWaveCols * kKC * (FP4 ? 1 : (FP8 ? 2 : 4)) / 2;  // bytes of one fragment
+  constexpr int LB = FP4 ? 8 : 16;            // bytes of one lane in a (half) fragment
+  constexpr int NBUF = FP8 || FP4 ? 3 : 2;      // steps in the register ring
   constexpr int SL = kMaxScaleBlocks / 64;
 
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -135,10 +142,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   // ---- weight streams
   const int kpH = round_up(H, kKC), kpI = round_up(NI, kKC);
   const int nchH = kpH / kKC;                           // 128-deep chunks of H
-  const size_t tile_g = (size_t)kpH * kWaveCols * ESZ;  // bytes of one 16-row tile of Wg / Wu
-  const size_t tile_d = (size_t)kpI * kWaveCols * ESZ;  // of Wd
+  const size_t tile_g = (size_t)kpH / kKC * FB;  // bytes of one 16-row tile of Wg / Wu
+  const size_t tile_d = (size_t)kpI / kKC * FB;  // of Wd
   const char *G, *U, *D;
-  const float *SG = nullptr, *SU = nullptr, *SD = nullptr;
+  const float *SG = nullptr, *SU = nullptr, *SD = nullptr;        // FP8 scales
+  const uint8_t *BG = nullptr, *BU = nullptr, *BD = nullptr;      // MXFP4 E8M0 bytes [N, K/32]
   float* OUT;
   if (routed) {
     G = static_cast<const char*>(p.w[0]) + (size_t)e * NI * tile_g / kWaveCols;
@@ -146,18 +154,27 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     D = static_cast<const char*>(p.w[2]) + (size_t)e * H * tile_d / kWaveCols;
     if (FP8) {
       const size_t ss = (size_t)(NI / kFp8Block) * (H / kFp8Block);
-      SG = p.s[0] + e * (ROWS ? (size_t)NI : ss);
-      SU = p.s[1] + e * (ROWS ? (size_t)NI : ss);
-      SD = p.s[2] + e * (ROWS ? (size_t)H : ss);
+      SG = static_cast<const float*>(p.s[0]) + e * (ROWS ? (size_t)NI : ss);
+      SU = static_cast<const float*>(p.s[1]) + e * (ROWS ? (size_t)NI : ss);
+      SD = static_cast<const float*>(p.s[2]) + e * (ROWS ? (size_t)H : ss);
+    }
+    if (FP4) {
+      const size_t ss = (size_t)NI * (H / kMxBlock);  // the same count for [I, H/32] and [H, I/32]
+      BG = static_cast<const uint8_t*>(p.s[0]) + e * ss;
+      BU = static_cast<const uint8_t*>(p.s[1]) + e * ss;
+      BD = static_cast<const uint8_t*>(p.s[2]) + e * ss;
     }
     OUT = p.part + (size_t)slice * p.n * H;
   } else {
     G = static_cast<const char*>(p.sw[0]);
     U = static_cast<const char*>(p.sw[1]);
     D = static_cast<const char*>(p.sw[2]);
-    SG = p.ss[0];
-    SU = p.ss[1];
-    SD = p.ss[2];
+    SG = static_cast<const float*>(p.ss[0]);
+    SU = static_cast<const float*>(p.ss[1]);
+    SD = static_cast<const float*>(p.ss[2]);
+    BG = static_cast<const uint8_t*>(p.ss[0]);
+    BU = static_cast<const uint8_t*>(p.ss[1]);
+    BD = static_cast<const uint8_t*>(p.ss[2]);
     OUT = p.sh_part + (size_t)slice * p.M * H;
   }
   // gate+up: this wave's 16 intermediate columns (a wave past NI loads the
@@ -166,8 +183,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   const int ct = SPLIT ? wave % kColTiles : wave;
   const int tg = slice * kColTiles + ct;
   const bool gon = tg * kWaveCols < NI;
-  const char* gbase = (SPLIT && st ? U : G) + (size_t)(gon ? tg : slice * kColTiles) * tile_g + lane * 16;
-  const char* ubase = U + (size_t)(gon ? tg : slice * kColTiles) * tile_g + lane * 16;
+  const int tgl = gon ? tg : slice * kColTiles;  // the tile this wave loads
+  const char* gbase = (SPLIT && st ? U : G) + (size_t)tgl * tile_g + lane * LB;
+  const char* ubase = U + (size_t)tgl * tile_g + lane * LB;
+  // MXFP4: this lane's row of gate / up scale bytes (split: of its one stream)
+  const uint8_t* bgrow = (SPLIT && st ? BU : BG) + (size_t)(tgl * kWaveCols + r16) * (H / kMxBlock);
+  const uint8_t* burow = BU + (size_t)(tgl * kWaveCols + r16) * (H / kMxBlock);
   const int ngs = SPLIT ? (nchH + 1) / 2 : nchH;  // gate/up steps (split: two chunks of one stream each)
   // down: this wave's run of 16-row tiles of H, kDownTiles per step (tiles past
   // H load the last tile again and store nothing); the slice is half `hf` of
@@ -178,11 +199,47 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   const int nd = per / kDownTiles;
   const int nv = ngs + nd;
   const int hf = slice & 1;
-  const char* dbase = D + (size_t)(slice >> 1) * FB + hf * HL * 1024 + lane * 16;
+  const char* dbase = D + (size_t)(slice >> 1) * FB + hf * (FB / 2) + lane * LB;
+  // MXFP4: the down scale dword of chunk slice / 2 in this lane's row of tile 0
+  const uint8_t* bdbase = BD + (size_t)r16 * (NI / kMxBlock) + 4 * (slice >> 1);
 
-  auto load_step = [&](int v, uint4 (&wr)[NL]) {
+  // one step's weights into the ring; MXFP4 also its scale dwords (`sr`:
+  // gate+up: gate, up or, split, the two chunks of the stream; down: per tile)
+  auto load_step = [&](int v, uint4 (&wr)[NL], uint32_t (&sr)[kDownTiles]) {
     v = min(v, nv - 1);
-    if (v < ngs) {
+    if constexpr (FP4) {
+      // both branches fill every register of the slot (a slot written in part
+      // on one branch is kept in scratch memory by the compiler)
+      uint4 r0, r1;
+      uint32_t c[kDownTiles];
+      if (v < ngs) {
+        const int c0 = SPLIT ? 2 * v : v, c1 = SPLIT ? min(2 * v + 1, nchH - 1) : v;
+        const char* a0 = gbase + (size_t)c0 * FB;
+        const char* a1 = (SPLIT ? gbase : ubase) + (size_t)c1 * FB;
+        const uint2 g0 = *reinterpret_cast<const uint2*>(a0), g1 = *reinterpret_cast<const uint2*>(a0 + FB / 2);
+        const uint2 u0 = *reinterpret_cast<const uint2*>(a1), u1 = *reinterpret_cast<const uint2*>(a1 + FB / 2);
+        r0 = uint4{g0.x, g0.y, g1.x, g1.y};
+        r1 = uint4{u0.x, u0.y, u1.x, u1.y};
+        c[0] = *reinterpret_cast<const uint32_t*>(bgrow + 4 * c0);
+        c[1] = *reinterpret_cast<const uint32_t*>((SPLIT ? bgrow : burow) + 4 * c1);
+        c[2] = c[3] = 0u;
+      } else {
+        const int T0 = dfirst + kDownTiles * (v - ngs);
+        uint2 d[kDownTiles];
+#pragma unroll
+        for (int u = 0; u < kDownTiles; ++u) {
+          const int t = min(T0 + u, ntd - 1);
+          d[u] = *reinterpret_cast<const uint2*>(dbase + (size_t)t * tile_d);
+          c[u] = *reinterpret_cast<const uint32_t*>(bdbase + (size_t)t * kWaveCols * (NI / kMxBlock));
+        }
+        r0 = uint4{d[0].x, d[0].y, d[1].x, d[1].y};
+        r1 = uint4{d[2].x, d[2].y, d[3].x, d[3].y};
+      }
+      wr[0] = r0;
+      wr[1] = r1;
+#pragma unroll
+      for (int u = 0; u < kDownTiles; ++u) sr[u] = c[u];
+    } else if (v < ngs) {
       const char* a0 = gbase + (size_t)(SPLIT ? 2 * v : v) * FB;
       const char* a1 = SPLIT ? gbase + (size_t)min(2 * v + 1, nchH - 1) * FB : ubase + (size_t)v * FB;
 #pragma unroll
@@ -238,6 +295,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   }
 
   uint4 wb[NBUF][NL];
+  uint32_t sb[NBUF][kDownTiles];  // MXFP4 scale dwords of each ring step (unused otherwise)
   for (int r0 = 0; r0 < rows; r0 += rowcap) {
     const int nr = min(rowcap, rows - r0);
     const int nrt = (nr + 15) >> 4;
@@ -256,7 +314,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 #pragma unroll
     for (int u = 0; u < kXFirst; ++u) xv[u] = x_piece(min(u * kThreads + tid, total - 1));
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) load_step(j, wb[j]);
+    for (int j = 0; j < NBUF - 1; ++j) load_step(j, wb[j], sb[j]);
 #pragma unroll
     for (int u = 0; u < kXFirst; ++u) {
       const int idx = u * kThreads + tid;
@@ -279,26 +337,37 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     for (int rt = 0; rt < RT; ++rt) ag[rt] = au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // gate+up: operand s (8 consecutive k per lane) of stream st of a ring slot
-    auto gu_op = [&](const uint4 (&wc)[NL], int st, int s) -> bf16x8 {
-      if (FP8) {
+    // (MXFP4: step s lies in half s / 2, block 2 (s / 2) + q / 2 of the chunk)
+    auto gu_op = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int st, int s) -> bf16x8 {
+      if constexpr (FP4) {
+        const uint4 v = wc[st];
+        const uint32_t d = s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
+        return fp4x8_to_bf16(d, e8m0_to_f32(sr[st] >> (16 * (s >> 1) + 8 * (q >> 1))));
+      } else if constexpr (FP8) {
         const uint4 v = wc[st * WL + (s >> 1)];
         return (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
+      } else {
+        return as_bf16x8(wc[st * WL + s]);
       }
-      return as_bf16x8(wc[st * WL + s]);
     };
     // down: operand s (0 or 1, within the 64-deep half) of tile u of a ring slot
-    auto dn_op = [&](const uint4 (&wc)[NL], int u, int s) -> bf16x8 {
-      if (FP8) {
+    auto dn_op = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int u, int s) -> bf16x8 {
+      if constexpr (FP4) {
+        const uint4 v = wc[u >> 1];
+        const uint32_t d = (u & 1) ? (s ? v.w : v.z) : (s ? v.y : v.x);
+        return fp4x8_to_bf16(d, e8m0_to_f32(sr[u] >> (16 * hf + 8 * (q >> 1))));
+      } else if constexpr (FP8) {
         const uint4 v = wc[u * HL];
         return (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
+      } else {
+        return as_bf16x8(wc[u * HL + s]);
       }
-      return as_bf16x8(wc[u * HL + s]);
     };
 
     // gate+up step v: chunk v of this wave's 16 gate and 16 up columns, or
     // (split) chunks 2v and 2v + 1 of its one stream; each accumulator sees the
     // MFMA sequence of the separate gate+up kernel
-    auto gate_up = [&](const uint4 (&wc)[NL], int v) {
+    auto gate_up = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int v) {
       if constexpr (SPLIT) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
@@ -315,18 +384,18 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 #pragma unroll
                   for (int s = 0; s < 4; ++s) {
                     const bf16x8 b =
-                        as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
-                    t4 = mfma(gu_op(wc, c2, s), b, t4);
+                        as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
+                    t4 = mfma(gu_op(wc, sr, c2, s), b, t4);
                   }
 #pragma unroll
                   for (int i = 0; i < 4; ++i) ag[rt][i] = fmaf(ROWS ? rsg[i] : scg, t4[i], ag[rt][i]);
                 } else {
 #pragma unroll
                   for (int s = 0; s < 4; ++s) {
-                    if (c * kKC + s * 32 < H) {
+                    if (BMAP || c * kKC + s * 32 < H) {
                       const bf16x8 b =
-                          as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
-                      ag[rt] = mfma(gu_op(wc, c2, s), b, ag[rt]);
+                          as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
+                      ag[rt] = mfma(gu_op(wc, sr, c2, s), b, ag[rt]);
                     }
                   }
                 }
@@ -347,9 +416,9 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
               f32x4 tg4 = {0.f, 0.f, 0.f, 0.f}, tu4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
               for (int s = 0; s < 4; ++s) {
-                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
-                tg4 = mfma(gu_op(wc, 0, s), b, tg4);
-                tu4 = mfma(gu_op(wc, 1, s), b, tu4);
+                const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
+                tg4 = mfma(gu_op(wc, sr, 0, s), b, tg4);
+                tu4 = mfma(gu_op(wc, sr, 1, s), b, tu4);
               }
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
@@ -359,11 +428,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
             } else {
 #pragma unroll
               for (int s = 0; s < 4; ++s) {
-                if (c * kKC + s * 32 < H) {
+                if (BMAP || c * kKC + s * 32 < H) {
                   const bf16x8 b =
-                      as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<FP8>(s, q)));
-                  ag[rt] = mfma(gu_op(wc, 0, s), b, ag[rt]);
-                  au[rt] = mfma(gu_op(wc, 1, s), b, au[rt]);
+                      as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
+                  ag[rt] = mfma(gu_op(wc, sr, 0, s), b, ag[rt]);
+                  au[rt] = mfma(gu_op(wc, sr, 1, s), b, au[rt]);
                 }
               }
             }
@@ -416,7 +485,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 
     // down step i: tiles T0 .. T0 + 3 of this wave, depth = the slice; per tile
     // the MFMA sequence of one 64-deep half in the separate down kernel
-    auto down = [&](const uint4 (&wc)[NL], int i) {
+    auto down = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int i) {
       const int T0 = dfirst + kDownTiles * i;
       const float sc = FP8 && !ROWS ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sd), i)) : 1.f;
       const int k0 = slice * kSlice;
@@ -429,13 +498,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
           for (int u = 0; u < kDownTiles; ++u) t[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            if (FP8 || k0 + s * 32 < NI) {
-              const uint16_t* ab = as + rowc * astride + k_of_step<FP8>(s, q);
+            if (BMAP || k0 + s * 32 < NI) {
+              const uint16_t* ab = as + rowc * astride + k_of_step<BMAP>(s, q);
               const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(ab));
               const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(ab + aplane));
 #pragma unroll
               for (int u = 0; u < kDownTiles; ++u) {
-                const bf16x8 a = dn_op(wc, u, s);
+                const bf16x8 a = dn_op(wc, sr, u, s);
                 t[u] = mfma(a, bh, t[u]);
                 t[u] = mfma(a, bl, t[u]);
               }
@@ -460,15 +529,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
       }
     };
 
-    auto step = [&](const uint4 (&wc)[NL], int v) {
+    auto step = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int v) {
       if (v < ngs) {
-        if (gon) gate_up(wc, v);
+        if (gon) gate_up(wc, sr, v);
         if (v == ngs - 1) {
           if (SPLIT || gon) act_to_lds();
           __syncthreads();  // every wave's act columns are in LDS
         }
       } else {
-        down(wc, v - ngs);
+        down(wc, sr, v - ngs);
       }
     };
 
@@ -476,8 +545,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     for (int v0 = 0; v0 < nv; v0 += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
-        load_step(v0 + j + NBUF - 1, wb[(j + NBUF - 1) % NBUF]);
-        if (v0 + j < nv) step(wb[j], v0 + j);
+        load_step(v0 + j + NBUF - 1, wb[(j + NBUF - 1) % NBUF], sb[(j + NBUF - 1) % NBUF]);
+        if (v0 + j < nv) step(wb[j], sb[j], v0 + j);
       }
     }
     __syncthreads();  // the next pass restages LDS
@@ -596,9 +665,9 @@ __global__ __launch_bounds__(256) void blend_parts_kernel(uint16_t* __restrict__
 // even; the 256-wide layer of 8 experts 9% slower)
 inline int layer_waves(int n, int H) { return n <= kNarrowSlots && H >= kNarrowMinH ? 2 * kColTiles : kColTiles; }
 
-template <bool FP8, bool ROWS, int RT, typename IdT, int W>
+template <int FMT, bool ROWS, int RT, typename IdT, int W>
 hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
-  auto kern = layer_kernel<FP8, ROWS, RT, IdT, W>;
+  auto kern = layer_kernel<FMT, ROWS, RT, IdT, W>;
   const size_t xs = x_lds_bytes(rowcap, a.H);
   const size_t ab = act_lds_bytes(rowcap, W == 2 * kColTiles) + (ROWS ? (size_t)a.H * 4 : 0);
   const size_t lds = xs + ab + align_lds_bytes(a.E, a.n, W);
@@ -613,21 +682,22 @@ hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <bool FP8, bool ROWS, typename IdT>
+template <int FMT, bool ROWS, typename IdT>
 hipError_t launch_rt(const FusedLayerArgs& a, hipStream_t s) {
   const int rowcap = grouped_rows_per_pass(a.M);
-  if (layer_waves(a.n, a.H) == 2 * kColTiles) return launch_kernel<FP8, ROWS, 1, IdT, 2 * kColTiles>(a, rowcap, s);
+  if (layer_waves(a.n, a.H) == 2 * kColTiles) return launch_kernel<FMT, ROWS, 1, IdT, 2 * kColTiles>(a, rowcap, s);
   switch (rowcap <= 16 ? 1 : rowcap / 16) {
-    case 1: return launch_kernel<FP8, ROWS, 1, IdT, kColTiles>(a, rowcap, s);
-    case 2: return launch_kernel<FP8, ROWS, 2, IdT, kColTiles>(a, rowcap, s);
-    default: return launch_kernel<FP8, ROWS, 4, IdT, kColTiles>(a, rowcap, s);
+    case 1: return launch_kernel<FMT, ROWS, 1, IdT, kColTiles>(a, rowcap, s);
+    case 2: return launch_kernel<FMT, ROWS, 2, IdT, kColTiles>(a, rowcap, s);
+    default: return launch_kernel<FMT, ROWS, 4, IdT, kColTiles>(a, rowcap, s);
   }
 }
 
-template <bool FP8, typename IdT>
+template <int FMT, typename IdT>
 hipError_t launch_scales(const FusedLayerArgs& a, hipStream_t s) {
-  if (FP8 && a.scale_rows) return launch_rt<FP8, true, IdT>(a, s);
-  return launch_rt<FP8, false, IdT>(a, s);
+  if constexpr (FMT == kFmtFP8)
+    if (a.scale_rows) return launch_rt<FMT, true, IdT>(a, s);
+  return launch_rt<FMT, false, IdT>(a, s);
 }
 
 template <typename IdT>
@@ -643,8 +713,9 @@ hipError_t launch_blend(const FusedLayerArgs& a, hipStream_t s) {
 
 }  // namespace layer_detail
 
-bool fused_layer_fits(bool fp8, bool scale_rows, int64_t M, int H, int I, int S, int E, int top_k) {
+bool fused_layer_fits(int fmt, bool scale_rows, int64_t M, int H, int I, int S, int E, int top_k) {
   using namespace layer_detail;
+  const bool fp8 = fmt == kFmtFP8;
   const int64_t n = M * top_k;
   if (n < 1 || n > kFusedLayerMaxSlots) return false;
   if (fp8 && H > kMaxScaleBlocks * kFp8Block) return false;
@@ -658,10 +729,11 @@ bool fused_layer_fits(bool fp8, bool scale_rows, int64_t M, int H, int I, int S,
   return lds <= kLdsBudget;
 }
 
-hipError_t launch_layer_partials(const FusedLayerArgs& a, bool fp8, hipStream_t s) {
+hipError_t launch_layer_partials(const FusedLayerArgs& a, int fmt, hipStream_t s) {
   using namespace layer_detail;
-  if (fp8) return a.ids64 ? launch_scales<true, int64_t>(a, s) : launch_scales<true, int32_t>(a, s);
-  return a.ids64 ? launch_scales<false, int64_t>(a, s) : launch_scales<false, int32_t>(a, s);
+  if (fmt == kFmtFP8) return a.ids64 ? launch_scales<kFmtFP8, int64_t>(a, s) : launch_scales<kFmtFP8, int32_t>(a, s);
+  if (fmt == kFmtFP4) return a.ids64 ? launch_scales<kFmtFP4, int64_t>(a, s) : launch_scales<kFmtFP4, int32_t>(a, s);
+  return a.ids64 ? launch_scales<kFmtBF16, int64_t>(a, s) : launch_scales<kFmtBF16, int32_t>(a, s);
 }
 
 hipError_t launch_blend_partials(const FusedLayerArgs& a, hipStream_t s) {

@@ -4,7 +4,9 @@
 // Lane l feeds A row l%16 and B column l%16 with 8 consecutive k of quad l/16,
 // and receives the 4 results D[4*(l/16) + i][l%16], i = 0..3.  FP8 e4m3 weight
 // codes become bf16 exactly in registers (v_cvt_scalef32_pk_bf16_fp8 with
-// scale 1), so a weight's only rounding is the float32 accumulation.
+// scale 1), and so do MXFP4 codes with their power-of-two block scale
+// (v_cvt_scalef32_pk_bf16_fp4), so a weight's only rounding is the float32
+// accumulation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,6 +69,26 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// The value of an E8M0 scale byte, 2^(e - 127) (255: NaN), as a float32.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  e &= 0xffu;
+  if (e == 0xffu) return __uint_as_float(0x7fc00000u);
+  if (e == 0u) return __uint_as_float(0x00400000u);  // 2^-127, a float32 subnormal
+  return __uint_as_float(e << 23);
+}
+
+// 8 E2M1 codes (one dword, lowest nibble first) times `scale` -> 8 bf16
+// (v_cvt_scalef32_pk_bf16_fp4: each byte's two codes, scaled).  With a
+// power-of-two scale the products are exact in bf16 for every scale the
+// weights carry (their exponents stay far inside bf16's range).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t d, float scale) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+  const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -74,11 +96,14 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 // Element offset, inside a 128-deep chunk, of the 8 consecutive k a lane of
 // quad q feeds to MFMA step s.  The A and B operands use the same map, so the
 // k order inside one MFMA is a permutation the product does not see.
-//  FP8: one 16-byte load holds 16 codes = steps s and s+1 (s even).
+//  Byte-coded weights (FP8, MXFP4): steps 2h and 2h + 1 take the lane's 16
+//  consecutive k 64h + 16q .. +15 (16 FP8 codes = one 16-byte load; 16 E2M1
+//  codes = 8 bytes, all in one 32-deep E8M0 block), so each 64-deep half of
+//  the chunk is steps 2h and 2h + 1 alone.
 //  BF16: one 16-byte load holds 8 elements = one step.
-template <bool FP8>
+template <bool BYTES>
 __device__ __forceinline__ int k_of_step(int s, int q) {
-  return FP8 ? ((s >> 1) * 64 + q * 16 + (s & 1) * 8) : (s * 32 + q * 8);
+  return BYTES ? ((s >> 1) * 64 + q * 16 + (s & 1) * 8) : (s * 32 + q * 8);
 }
 
 // Gate of the shared expert for one token, sigmoid(x . g), for a 256-thread

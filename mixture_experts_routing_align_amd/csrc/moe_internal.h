@@ -63,6 +63,13 @@ inline hipError_t occupancy_per_cu(const void* kern, int threads, size_t lds,
 
 constexpr int kFp8Block = 128;   // FP8 scale block edge (both N and K)
 
+// Expert weight element formats of the kernels' templates.
+//  kFmtBF16: bf16; kFmtFP8: OCP e4m3fn codes with float32 block or row scales;
+//  kFmtFP4: OCP MXFP4, E2M1 codes two per byte (the lower nibble first) with one
+//  E8M0 scale byte per 32 consecutive depth elements of a row.
+constexpr int kFmtBF16 = 0, kFmtFP8 = 1, kFmtFP4 = 2;
+constexpr int kMxBlock = 32;  // depth elements per E8M0 scale byte
+
 // Record a failure for moe_last_error() and return `code` (api.cpp).
 int fail_status(int code, const char* fmt, ...);
 
@@ -94,17 +101,17 @@ struct GroupedArgs {
   // routed experts
   const void* x;        // gate+up: bf16 [M, K] token rows; down: float32 [max_total, K] by position
   const void* w0;       // gate (gate+up) or down weights [E, N, K]
-  const float* s0;      // its FP8 scales [E, N/128, K/128] (unused for bf16)
+  const void* s0;       // its FP8 scales (float32 [E, N/128, K/128] or [E, N]) or MXFP4 E8M0 bytes [E, N, K/32]
   const void* w1;       // up weights (gate+up only)
-  const float* s1;
+  const void* s1;
   float* out;           // gate+up: act [max_total, N]; down: expert_out [max_total, N]
   int N, K;
   // shared expert (sw0 == nullptr: none)
   const void* sx;       // gate+up: bf16 [M, sK] (the same x); down: float32 sh_act [M, sK]
   const void* sw0;
-  const float* ss0;
+  const void* ss0;
   const void* sw1;
-  const float* ss1;
+  const void* ss1;
   float* sout;          // [M, sN]
   int sN, sK;
   // alignment tables
@@ -139,12 +146,13 @@ int grouped_rows_per_pass(int64_t M);
 int grouped_step_rows(int64_t M);
 int grouped_passes(int64_t M);
 
-hipError_t launch_grouped_gate_up(const GroupedArgs& a, bool fp8, bool tiled, hipStream_t s);
-hipError_t launch_grouped_down(const GroupedArgs& a, bool fp8, bool tiled, hipStream_t s);
+// fmt: the weight element format, kFmtBF16 / kFmtFP8 / kFmtFP4
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, int fmt, bool tiled, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, int fmt, bool tiled, hipStream_t s);
 
 // The tiled (MFMA-fragment-ordered) copy of row-major [E, N, K] weights.
-size_t tiled_weight_bytes(bool fp8, int64_t E, int N, int K);
-hipError_t launch_tile_weights(const void* src, void* dst, bool fp8, int64_t E, int N, int K, hipStream_t s);
+size_t tiled_weight_bytes(int fmt, int64_t E, int N, int K);
+hipError_t launch_tile_weights(const void* src, void* dst, int fmt, int64_t E, int N, int K, hipStream_t s);
 
 // Single-pass decode layer: one launch aligns (in LDS), runs gate+up+SiLU for a
 // 128-wide slice of the intermediate and the matching 128-deep slice of down
@@ -155,9 +163,9 @@ struct FusedLayerArgs {
   int ids64;
   const void* x;          // bf16 [M, H]
   const void* w[3];       // routed gate, up [E, I, H] and down [E, H, I], tiled
-  const float* s[3];      // their FP8 scales (unused for bf16)
+  const void* s[3];       // their FP8 scales, or MXFP4 E8M0 bytes (unused for bf16)
   const void* sw[3];      // shared expert (sw[0] == nullptr: none), tiled
-  const float* ss[3];
+  const void* ss[3];
   const void* sh_gate;    // bf16 [H] gate vector of the shared expert, or nullptr (ungated)
   int scale_rows;         // FP8 scales are one per weight row, [E, N] (else per 128x128 block)
   const float* topk_weights;
@@ -173,9 +181,9 @@ constexpr int kFusedLayerMaxSlots = 256;
 
 // Whether the single-pass layer runs this shape (tiled weights assumed): slot
 // count, depth limits and the LDS it needs.
-bool fused_layer_fits(bool fp8, bool scale_rows, int64_t M, int H, int I, int S, int E, int top_k);
+bool fused_layer_fits(int fmt, bool scale_rows, int64_t M, int H, int I, int S, int E, int top_k);
 // the first launch (align, gate+up+SiLU, down partials) and the second (sum + blend)
-hipError_t launch_layer_partials(const FusedLayerArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_layer_partials(const FusedLayerArgs& a, int fmt, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int blocks, hipStream_t s);
 hipError_t launch_router(const void* x, const void* w, int M, int H, int E, int top_k, float* logits, void* ids,
                          bool ids64, float* wts, hipStream_t s);

@@ -99,3 +99,23 @@ def compare_tables(gpu_tables: dict, ref: dict) -> None:
                                  f"oracle {r[bad[:5]]}")
     assert int(gpu_tables["active_count"].item()) == int(ref["active_count"])
     assert int(gpu_tables["total"].item()) == int(ref["total"])
+
+
+def separate_steps(moe, layer, xt, it, wt):
+    """align, gate+up, down and blend called one by one through their entry points."""
+    M = xt.shape[0]
+    t = moe.moe_align(it, layer.E, layer.BS)
+    mt = t.sorted_token_ids.numel()
+    act = torch.empty(mt, layer.I, device="cuda")
+    eo = torch.empty(mt, layer.H, device="cuda")
+    sh_act = sh_out = None
+    if layer.S:
+        sh_act = torch.empty(M, layer.S, device="cuda")
+        sh_out = torch.empty(M, layer.H, device="cuda")
+    moe.moe_grouped_gate_up_silu(xt, layer.gate, layer.up, t, act, layer.top_k, layer.BS, layer.sh_gate, layer.sh_up,
+                                 sh_act)
+    moe.moe_grouped_down(act, layer.down, t, eo, M, layer.top_k, layer.BS, layer.sh_down, sh_act, sh_out)
+    out = torch.empty(M, layer.H, dtype=torch.bfloat16, device="cuda")
+    moe.moe_blend(out, eo, wt, t.token_to_perm, sh_out)
+    torch.cuda.synchronize()
+    return out, t

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 9
+    assert lib.moe_abi_version() == 10
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -118,7 +118,7 @@ def test_grouped_refusals(lib):
     assert gu(I=64) == _ffi.MOE_ERR_SHAPE
     assert gu(wdt=0, H=48) == _ffi.MOE_ERR_SHAPE    # BF16 needs K % 32
     assert gu(wdt=0, I=24) == _ffi.MOE_ERR_SHAPE    # and N % 16
-    assert gu(wdt=6) == _ffi.MOE_ERR_SHAPE          # no such weight dtype
+    assert gu(wdt=8) == _ffi.MOE_ERR_SHAPE          # no such weight dtype
     assert gu(wdt=-1) == _ffi.MOE_ERR_SHAPE
     # FP8 with row scales keeps the 128-multiple shapes, and reads its scales 16 bytes at a time
     assert gu(wdt=_ffi.MOE_W_FP8_E4M3_ROWS, H=200) == _ffi.MOE_ERR_SHAPE
@@ -441,3 +441,41 @@ def test_misaligned_pointers_refused(lib):
     refused(lib.moe_tile_weights(FAKE, odd, 1, 2, 256, 128, None), "dst")
     refused(lib.moe_router_topk(odd, FAKE, 8, 2048, 128, 8, FAKE, FAKE, 1, FAKE, None), "x")
     refused(lib.moe_router_topk(FAKE, odd, 8, 2048, 128, 8, FAKE, FAKE, 1, FAKE, None), "router weight")
+
+
+def test_mxfp4_dtypes(lib):
+    """MXFP4 (two E2M1 codes per byte, one E8M0 byte per 32 k): the shape rules
+    (K in whole 128-deep chunks, N in 16-row tiles), non-NULL 4-byte aligned
+    scales, half-byte tiled sizes, and the binding's detection by the scales'
+    byte type with K read as twice the last dimension."""
+    import torch
+
+    import mixture_experts_routing_align_amd as moe
+
+    t = _tables()
+    u = _w()
+
+    def gu(wdt=_ffi.MOE_W_MXFP4, H=256, I=128, g=None):
+        return lib.moe_grouped_gate_up_silu(FAKE, wdt, ctypes.byref(g or _w()), ctypes.byref(u), ctypes.byref(t),
+                                            FAKE, None, None, None, 4, H, I, 0, 8, 2, 16, None)
+
+    for wdt in (_ffi.MOE_W_MXFP4, _ffi.MOE_W_MXFP4_TILED):
+        assert gu(wdt, H=192) == _ffi.MOE_ERR_SHAPE      # K % 128
+        assert "MXFP4" in _err(lib)
+        assert gu(wdt, I=24) == _ffi.MOE_ERR_SHAPE       # N % 16
+        assert gu(wdt, g=_ffi.MoeWeight(FAKE, None)) == _ffi.MOE_ERR_NULL
+        assert gu(wdt, g=_ffi.MoeWeight(FAKE, FAKE + 2)) == _ffi.MOE_ERR_SHAPE
+        assert "4-byte" in _err(lib)
+        d = _ffi.MoeWeight(FAKE, FAKE)
+        assert lib.moe_grouped_down(FAKE, wdt, ctypes.byref(d), ctypes.byref(t), FAKE, None, None, None,
+                                    4, 256, 192, 0, 8, 2, 16, None) == _ffi.MOE_ERR_SHAPE  # I % 128
+    for E, N, K in ((1, 16, 128), (8, 768, 2048), (3, 48, 384)):
+        assert lib.moe_tiled_weight_bytes(_ffi.MOE_W_MXFP4, E, N, K) == E * N * K // 2
+    assert lib.moe_tiled_weight_bytes(_ffi.MOE_W_MXFP4, 1, 16, 96) == 0
+    assert lib.moe_tiled_weight_bytes(_ffi.MOE_W_MXFP4_TILED, 1, 16, 128) == 0  # not a source dtype
+    codes = torch.zeros(4, 256, 64, dtype=torch.uint8)
+    sc = torch.zeros(4, 256, 4, dtype=torch.uint8)
+    assert moe.weight_dtype((codes, sc)) == _ffi.MOE_W_MXFP4
+    assert moe.weight_shape((codes, sc)) == (4, 256, 128)
+    assert moe.weight_shape((codes[0], sc[0])) == (1, 256, 128)
+    assert moe.weight_dtype((codes, torch.ones(4, 2, 1))) == _ffi.MOE_W_FP8_E4M3

@@ -9,7 +9,7 @@ import torch
 import oracle
 import workloads
 from moe_testlib import (DeviceModel, bf16_to_np, compare_tables, device_inputs, log, oracle_layer,
-                         tolerance_ok)
+                         separate_steps, tolerance_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -455,26 +455,6 @@ def test_tiled_odd_shapes_bit_identical(moe, cfg):
 
 # ------------------------------------------ fused layer vs the four steps --
 
-def _separate_steps(moe, layer, xt, it, wt):
-    """align, gate+up, down and blend called one by one through their entry points."""
-    M = xt.shape[0]
-    t = moe.moe_align(it, layer.E, layer.BS)
-    mt = t.sorted_token_ids.numel()
-    act = torch.empty(mt, layer.I, device="cuda")
-    eo = torch.empty(mt, layer.H, device="cuda")
-    sh_act = sh_out = None
-    if layer.S:
-        sh_act = torch.empty(M, layer.S, device="cuda")
-        sh_out = torch.empty(M, layer.H, device="cuda")
-    moe.moe_grouped_gate_up_silu(xt, layer.gate, layer.up, t, act, layer.top_k, layer.BS, layer.sh_gate, layer.sh_up,
-                                 sh_act)
-    moe.moe_grouped_down(act, layer.down, t, eo, M, layer.top_k, layer.BS, layer.sh_down, sh_act, sh_out)
-    out = torch.empty(M, layer.H, dtype=torch.bfloat16, device="cuda")
-    moe.moe_blend(out, eo, wt, t.token_to_perm, sh_out)
-    torch.cuda.synchronize()
-    return out, t
-
-
 @pytest.mark.parametrize("name,ids_dtype", [("tiny", torch.int64), ("decode", torch.int64), ("decode", torch.int32),
                                             ("verify", torch.int64)])
 def test_fused_layer_equals_separate_steps(moe, name, ids_dtype):
@@ -488,7 +468,7 @@ def test_fused_layer_equals_separate_steps(moe, name, ids_dtype):
         fused = layer.forward(xt, it, wt, workspace=ws)
         torch.cuda.synchronize()
         views = layer.workspace_views(ws, xt.shape[0], moe.MOE_IDX_I64 if ids_dtype == torch.int64 else moe.MOE_IDX_I32)
-        sep, t = _separate_steps(moe, layer, xt, it, wt)
+        sep, t = separate_steps(moe, layer, xt, it, wt)
         assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
         for k in moe.TABLE_FIELDS:
             assert torch.equal(views[k], getattr(t, k)), k
@@ -500,7 +480,7 @@ def test_fused_odd_shapes_equal_separate_steps(moe, cfg):
     _, (xt, it, wt) = device_inputs(cfg)
     layer = model.layer()
     fused = layer.forward(xt, it, wt)
-    sep, _ = _separate_steps(moe, layer, xt, it, wt)
+    sep, _ = separate_steps(moe, layer, xt, it, wt)
     assert torch.equal(fused.view(torch.int16), sep.view(torch.int16))
 
 
@@ -518,7 +498,7 @@ def test_fused_layer_with_dropped_and_repeated_ids(moe):
     compare_tables(views, ref["tables"])
     ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
     assert ok, (err, bound)
-    sep, _ = _separate_steps(moe, model.layer(), xt, it, wt)
+    sep, _ = separate_steps(moe, model.layer(), xt, it, wt)
     assert torch.equal(out.view(torch.int16), sep.view(torch.int16))
 
 
