@@ -55,12 +55,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-reps", type=int, default=25)
     ap.add_argument("--other-configs", default="verify",
-                    help="comma-separated workloads (tiny, verify, large, or decode_mN: the decode layer at "
-                         "N tokens; a _rows suffix: the same with per-row FP8 scales) also timed whole-layer and "
-                         "reported "
-                         "under other_configs (context for the headline, not the headline)")
+                    help="comma-separated workloads (tiny, decode, verify, large, or decode_mN: the decode "
+                         "layer at N tokens; a _rows suffix: the same with per-row FP8 scales, _mxfp4: with "
+                         "MXFP4 experts) also timed whole-layer and reported under other_configs (context for "
+                         "the headline, not the headline)")
     ap.add_argument("--only-config", default="",
-                    help="time one other workload (tiny, verify or large) alone and print its line; for profiling")
+                    help="time one other workload (names as for --other-configs) alone and print its line; for profiling")
     ap.add_argument("--path", default="auto", choices=["auto", "steps", "single_pass"],
                     help="layer path the descriptors ask for (auto: the library's choice)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -142,13 +142,19 @@ def measure_config(name, dev, steps=50):
     import workloads
     from workloads.device import DeviceWeights
 
-    base, rows = (name[:-len("_rows")], True) if name.endswith("_rows") else (name, False)
+    # a suffix names another weight format of the same layer: _rows (FP8 scaled
+    # per row instead of per 128x128 block) or _mxfp4 (4-bit MXFP4 experts)
+    wdt = None
+    base = name
+    for suffix, fmt in (("_rows", "fp8_rows"), ("_mxfp4", "mxfp4")):
+        if name.endswith(suffix):
+            base, wdt = name[:-len(suffix)], fmt
     if base.startswith("decode_m"):  # the decode layer at a narrower width: decode_m1, decode_m2, ...
         cfg = workloads.CONFIGS["decode"].replace(M=int(base[len("decode_m"):]), name=name)
     else:
         cfg = workloads.CONFIGS[base]
-    if rows:  # the same layer with FP8 weights scaled per row instead of per 128x128 block
-        cfg = cfg.replace(wdt="fp8_rows", name=name)
+    if wdt is not None:
+        cfg = cfg.replace(wdt=wdt, name=name)
     G = 2 if cfg.E * cfg.I * cfg.H > (1 << 31) else 4  # the large workload: 2 copies of its 11 GB
     log(f"other config {name}: generating weights, {G} copies")
     w0 = DeviceWeights(cfg, device=dev, threads=16)
@@ -168,12 +174,14 @@ def measure_config(name, dev, steps=50):
     wss = [layers[i].alloc_workspace(cfg.M) for i in range(G)]
     sh_bytes = 0
     if cfg.S:
-        esz = 1 if cfg.wdt in ("fp8", "fp8_rows") else 2
-        sh_bytes = 3 * cfg.S * cfg.H * esz
+        esz = {"fp8": 1.0, "fp8_rows": 1.0, "mxfp4": 0.5}.get(cfg.wdt, 2.0)
+        sh_bytes = int(3 * cfg.S * cfg.H * esz)
         if cfg.wdt == "fp8":
             sh_bytes += 3 * (cfg.S // 128) * (cfg.H // 128) * 4
         elif cfg.wdt == "fp8_rows":
             sh_bytes += (2 * cfg.S + cfg.H) * 4
+        elif cfg.wdt == "mxfp4":
+            sh_bytes += 3 * cfg.S * cfg.H // 32
     per = [w0.algorithmic_bytes(ids)["total"] for ids, _ in routings]
     stream = torch.cuda.Stream(device=dev)
     multi = graph_of(lambda: [layers[i].forward(xt, ids_d[i], w_d[i], out=outs[i], workspace=wss[i])

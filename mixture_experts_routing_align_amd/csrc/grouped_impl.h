@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
             // block 2 (s / 2) + q / 2 of the chunk
             const uint4 v = wc[st][0];
             const uint32_t d = s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
-            a[st][s] = fp4x8_to_bf16(d, e8m0_to_f32(scb[st] >> (16 * (s >> 1) + 8 * (q >> 1))));
+            a[st][s] = fp4x8_to_bf16(d, e8m0_at(scb[st], 16 * (s >> 1) + 8 * (q >> 1)));
           } else if constexpr (FP8) {
             const uint4 v = wc[st][s >> 1];
             a[st][s] = (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);

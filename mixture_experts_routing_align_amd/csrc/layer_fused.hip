@@ -56,6 +56,10 @@ __host__ __device__ constexpr size_t align_lds_bytes(int E, int n, int waves) {
   return ((size_t)waves * E + E + (E + 1) + E + 2 * waves + 2 + n) * sizeof(int);
 }
 __host__ __device__ constexpr size_t x_lds_bytes(int rowcap, int H) { return (size_t)rowcap * (H + kPad) * 2; }
+// MXFP4 scale bytes: gate and up rows of the slice ([kSlice][H/32 + 4] each, the
+// 4 pad bytes against bank conflicts), then one 16-bit pair per down row [H]
+__host__ __device__ constexpr int mx_row_bytes(int H) { return H / kMxBlock + 4; }
+__host__ __device__ constexpr size_t mx_scale_lds_bytes(int H) { return (size_t)2 * kSlice * mx_row_bytes(H) + (size_t)H * 2; }
 // act as bf16 hi + lo, plus (8-wave kernel) the up sums handed to the gate waves
 __host__ __device__ constexpr size_t act_lds_bytes(int rowcap, bool split) {
   return (size_t)2 * rowcap * (kSlice + kPad) * 2 + (split ? (size_t)rowcap * kSlice * 4 : 0);
@@ -68,8 +72,10 @@ __host__ __device__ constexpr size_t act_lds_bytes(int rowcap, bool split) {
 // whole layer is only a few hundred workgroups.  Same arithmetic either way.
 // FMT: the weight format (kFmtBF16, kFmtFP8, kFmtFP4).  MXFP4 codes become
 // bf16 with their E8M0 block scale in the conversion (exact), so they
-// accumulate as bf16 weights do; their scale bytes ride the register ring
-// with the codes (one dword per row and chunk).
+// accumulate as bf16 weights do.  A workgroup stages the scale bytes it uses
+// in LDS once, before its first pass: the 64 gate and 64 up rows of its slice
+// (every 32-deep block of H) and, for each of the H down rows, the two bytes
+// of its 64-deep half-chunk; each step then reads them from LDS, not HBM.
 // ROWS (FP8 only): one float32 scale per weight row ([E, N]) instead of one
 // per 128x128 block; it multiplies where the block scale does, per output
 // column (gate/up: the lane's 4 intermediate columns; down: its 4 rows of H,
@@ -186,9 +192,6 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   const int tgl = gon ? tg : slice * kColTiles;  // the tile this wave loads
   const char* gbase = (SPLIT && st ? U : G) + (size_t)tgl * tile_g + lane * LB;
   const char* ubase = U + (size_t)tgl * tile_g + lane * LB;
-  // MXFP4: this lane's row of gate / up scale bytes (split: of its one stream)
-  const uint8_t* bgrow = (SPLIT && st ? BU : BG) + (size_t)(tgl * kWaveCols + r16) * (H / kMxBlock);
-  const uint8_t* burow = BU + (size_t)(tgl * kWaveCols + r16) * (H / kMxBlock);
   const int ngs = SPLIT ? (nchH + 1) / 2 : nchH;  // gate/up steps (split: two chunks of one stream each)
   // down: this wave's run of 16-row tiles of H, kDownTiles per step (tiles past
   // H load the last tile again and store nothing); the slice is half `hf` of
@@ -200,18 +203,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
   const int nv = ngs + nd;
   const int hf = slice & 1;
   const char* dbase = D + (size_t)(slice >> 1) * FB + hf * (FB / 2) + lane * LB;
-  // MXFP4: the down scale dword of chunk slice / 2 in this lane's row of tile 0
-  const uint8_t* bdbase = BD + (size_t)r16 * (NI / kMxBlock) + 4 * (slice >> 1);
 
-  // one step's weights into the ring; MXFP4 also its scale dwords (`sr`:
-  // gate+up: gate, up or, split, the two chunks of the stream; down: per tile)
-  auto load_step = [&](int v, uint4 (&wr)[NL], uint32_t (&sr)[kDownTiles]) {
+  // one step's weights into the ring
+  auto load_step = [&](int v, uint4 (&wr)[NL]) {
     v = min(v, nv - 1);
     if constexpr (FP4) {
       // both branches fill every register of the slot (a slot written in part
       // on one branch is kept in scratch memory by the compiler)
       uint4 r0, r1;
-      uint32_t c[kDownTiles];
       if (v < ngs) {
         const int c0 = SPLIT ? 2 * v : v, c1 = SPLIT ? min(2 * v + 1, nchH - 1) : v;
         const char* a0 = gbase + (size_t)c0 * FB;
@@ -220,25 +219,17 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
         const uint2 u0 = *reinterpret_cast<const uint2*>(a1), u1 = *reinterpret_cast<const uint2*>(a1 + FB / 2);
         r0 = uint4{g0.x, g0.y, g1.x, g1.y};
         r1 = uint4{u0.x, u0.y, u1.x, u1.y};
-        c[0] = *reinterpret_cast<const uint32_t*>(bgrow + 4 * c0);
-        c[1] = *reinterpret_cast<const uint32_t*>((SPLIT ? bgrow : burow) + 4 * c1);
-        c[2] = c[3] = 0u;
       } else {
         const int T0 = dfirst + kDownTiles * (v - ngs);
         uint2 d[kDownTiles];
 #pragma unroll
-        for (int u = 0; u < kDownTiles; ++u) {
-          const int t = min(T0 + u, ntd - 1);
-          d[u] = *reinterpret_cast<const uint2*>(dbase + (size_t)t * tile_d);
-          c[u] = *reinterpret_cast<const uint32_t*>(bdbase + (size_t)t * kWaveCols * (NI / kMxBlock));
-        }
+        for (int u = 0; u < kDownTiles; ++u)
+          d[u] = *reinterpret_cast<const uint2*>(dbase + (size_t)min(T0 + u, ntd - 1) * tile_d);
         r0 = uint4{d[0].x, d[0].y, d[1].x, d[1].y};
         r1 = uint4{d[2].x, d[2].y, d[3].x, d[3].y};
       }
       wr[0] = r0;
       wr[1] = r1;
-#pragma unroll
-      for (int u = 0; u < kDownTiles; ++u) sr[u] = c[u];
     } else if (v < ngs) {
       const char* a0 = gbase + (size_t)(SPLIT ? 2 * v : v) * FB;
       const char* a1 = SPLIT ? gbase + (size_t)min(2 * v + 1, nchH - 1) * FB : ubase + (size_t)v * FB;
@@ -293,9 +284,29 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     for (int i = tid; i < H / 4; i += kThreads)
       *reinterpret_cast<f32x4*>(rsd + 4 * i) = *reinterpret_cast<const f32x4*>(SD + 4 * i);
   }
+  // MXFP4: the scale bytes of this workgroup (same place; ordered before any
+  // read by the same barrier).  Gate / up: rows slice*64 .. +63 (rows past NI
+  // repeat the last row; waves past NI multiply nothing), a contiguous run of
+  // 64 * H/32 bytes copied a dword at a time; down: row h's bytes 2*hf and
+  // 2*hf + 1 of its dword for chunk slice / 2.
+  const int mxrow = mx_row_bytes(H);
+  uint8_t* msg = reinterpret_cast<uint8_t*>(rsd);  // [kSlice][mxrow] gate, then up
+  uint8_t* msu = msg + kSlice * mxrow;
+  uint16_t* msd = reinterpret_cast<uint16_t*>(msu + kSlice * mxrow);  // [H]
+  if constexpr (FP4) {
+    const int rdw = H / 128;  // dwords per row
+    for (int i = tid; i < kSlice * rdw; i += kThreads) {
+      const int r = i / rdw, c = i % rdw;
+      const size_t row = (size_t)min(slice * kSlice + r, NI - 1);
+      const size_t off = row * (H / kMxBlock) + 4 * c;
+      *reinterpret_cast<uint32_t*>(msg + r * mxrow + 4 * c) = *reinterpret_cast<const uint32_t*>(BG + off);
+      *reinterpret_cast<uint32_t*>(msu + r * mxrow + 4 * c) = *reinterpret_cast<const uint32_t*>(BU + off);
+    }
+    for (int h = tid; h < H; h += kThreads)
+      msd[h] = *reinterpret_cast<const uint16_t*>(BD + (size_t)h * (NI / kMxBlock) + 4 * (slice >> 1) + 2 * hf);
+  }
 
   uint4 wb[NBUF][NL];
-  uint32_t sb[NBUF][kDownTiles];  // MXFP4 scale dwords of each ring step (unused otherwise)
   for (int r0 = 0; r0 < rows; r0 += rowcap) {
     const int nr = min(rowcap, rows - r0);
     const int nrt = (nr + 15) >> 4;
@@ -314,7 +325,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 #pragma unroll
     for (int u = 0; u < kXFirst; ++u) xv[u] = x_piece(min(u * kThreads + tid, total - 1));
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) load_step(j, wb[j], sb[j]);
+    for (int j = 0; j < NBUF - 1; ++j) load_step(j, wb[j]);
 #pragma unroll
     for (int u = 0; u < kXFirst; ++u) {
       const int idx = u * kThreads + tid;
@@ -336,13 +347,21 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) ag[rt] = au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // MXFP4 scales of the lane's gate/up rows for chunk c (st: 0 gate, 1 up):
+    // halves h = 0, 1 of the chunk hold this lane's k in 32-deep block
+    // 2h + q/2, whose byte is at bit 8 (2h + q/2) of the row's chunk dword
+    auto gu_scales = [&](int st, int c, float (&f)[2]) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>((st ? msu : msg) + (ct * kWaveCols + r16) * mxrow + 4 * c);
+      f[0] = e8m0_at(w, 8 * (q >> 1));
+      f[1] = e8m0_at(w, 16 + 8 * (q >> 1));
+    };
     // gate+up: operand s (8 consecutive k per lane) of stream st of a ring slot
-    // (MXFP4: step s lies in half s / 2, block 2 (s / 2) + q / 2 of the chunk)
-    auto gu_op = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int st, int s) -> bf16x8 {
+    // (MXFP4: step s lies in half s / 2, scaled by f[s / 2])
+    auto gu_op = [&](const uint4 (&wc)[NL], const float (&f)[2], int st, int s) -> bf16x8 {
       if constexpr (FP4) {
         const uint4 v = wc[st];
         const uint32_t d = s == 0 ? v.x : (s == 1 ? v.y : (s == 2 ? v.z : v.w));
-        return fp4x8_to_bf16(d, e8m0_to_f32(sr[st] >> (16 * (s >> 1) + 8 * (q >> 1))));
+        return fp4x8_to_bf16(d, f[s >> 1]);
       } else if constexpr (FP8) {
         const uint4 v = wc[st * WL + (s >> 1)];
         return (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
@@ -351,11 +370,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
       }
     };
     // down: operand s (0 or 1, within the 64-deep half) of tile u of a ring slot
-    auto dn_op = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int u, int s) -> bf16x8 {
+    auto dn_op = [&](const uint4 (&wc)[NL], float f, int u, int s) -> bf16x8 {
       if constexpr (FP4) {
         const uint4 v = wc[u >> 1];
         const uint32_t d = (u & 1) ? (s ? v.w : v.z) : (s ? v.y : v.x);
-        return fp4x8_to_bf16(d, e8m0_to_f32(sr[u] >> (16 * hf + 8 * (q >> 1))));
+        return fp4x8_to_bf16(d, f);
       } else if constexpr (FP8) {
         const uint4 v = wc[u * HL];
         return (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
@@ -367,12 +386,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     // gate+up step v: chunk v of this wave's 16 gate and 16 up columns, or
     // (split) chunks 2v and 2v + 1 of its one stream; each accumulator sees the
     // MFMA sequence of the separate gate+up kernel
-    auto gate_up = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int v) {
+    auto gate_up = [&](const uint4 (&wc)[NL], int v) {
       if constexpr (SPLIT) {
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const int c = 2 * v + c2;
           if (c < nchH) {
+            float f[2] = {1.f, 1.f};
+            if constexpr (FP4) gu_scales(st, c, f);
             const float scg = FP8 && !ROWS ? lane_scale(sg, c) : 1.f;
             const uint16_t* xb = xs + c * kKC;
 #pragma unroll
@@ -385,7 +406,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
                   for (int s = 0; s < 4; ++s) {
                     const bf16x8 b =
                         as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
-                    t4 = mfma(gu_op(wc, sr, c2, s), b, t4);
+                    t4 = mfma(gu_op(wc, f, c2, s), b, t4);
                   }
 #pragma unroll
                   for (int i = 0; i < 4; ++i) ag[rt][i] = fmaf(ROWS ? rsg[i] : scg, t4[i], ag[rt][i]);
@@ -395,7 +416,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
                     if (BMAP || c * kKC + s * 32 < H) {
                       const bf16x8 b =
                           as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
-                      ag[rt] = mfma(gu_op(wc, sr, c2, s), b, ag[rt]);
+                      ag[rt] = mfma(gu_op(wc, f, c2, s), b, ag[rt]);
                     }
                   }
                 }
@@ -407,6 +428,11 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
         const int c = v;
         const float scg = FP8 && !ROWS ? lane_scale(sg, c) : 1.f;
         const float scu = FP8 && !ROWS ? lane_scale(su, c) : 1.f;
+        float fg[2] = {1.f, 1.f}, fu[2] = {1.f, 1.f};
+        if constexpr (FP4) {
+          gu_scales(0, c, fg);
+          gu_scales(1, c, fu);
+        }
         const uint16_t* xb = xs + c * kKC;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -417,8 +443,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 #pragma unroll
               for (int s = 0; s < 4; ++s) {
                 const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
-                tg4 = mfma(gu_op(wc, sr, 0, s), b, tg4);
-                tu4 = mfma(gu_op(wc, sr, 1, s), b, tu4);
+                tg4 = mfma(gu_op(wc, fg, 0, s), b, tg4);
+                tu4 = mfma(gu_op(wc, fu, 1, s), b, tu4);
               }
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
@@ -431,8 +457,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
                 if (BMAP || c * kKC + s * 32 < H) {
                   const bf16x8 b =
                       as_bf16x8(*reinterpret_cast<const uint4*>(xb + rowc * xstride + k_of_step<BMAP>(s, q)));
-                  ag[rt] = mfma(gu_op(wc, sr, 0, s), b, ag[rt]);
-                  au[rt] = mfma(gu_op(wc, sr, 1, s), b, au[rt]);
+                  ag[rt] = mfma(gu_op(wc, fg, 0, s), b, ag[rt]);
+                  au[rt] = mfma(gu_op(wc, fu, 1, s), b, au[rt]);
                 }
               }
             }
@@ -485,8 +511,14 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
 
     // down step i: tiles T0 .. T0 + 3 of this wave, depth = the slice; per tile
     // the MFMA sequence of one 64-deep half in the separate down kernel
-    auto down = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int i) {
+    auto down = [&](const uint4 (&wc)[NL], int i) {
       const int T0 = dfirst + kDownTiles * i;
+      // MXFP4: the scale of this lane's row of each tile for the slice's half
+      // (its 16 k in 32-deep block 2 hf + q/2: byte q/2 of the row's pair)
+      float fd[kDownTiles];
+#pragma unroll
+      for (int u = 0; u < kDownTiles; ++u)
+        fd[u] = FP4 ? e8m0_at(msd[min(T0 + u, ntd - 1) * kWaveCols + r16], 8 * (q >> 1)) : 1.f;
       const float sc = FP8 && !ROWS ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sd), i)) : 1.f;
       const int k0 = slice * kSlice;
 #pragma unroll
@@ -504,7 +536,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
               const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(ab + aplane));
 #pragma unroll
               for (int u = 0; u < kDownTiles; ++u) {
-                const bf16x8 a = dn_op(wc, sr, u, s);
+                const bf16x8 a = dn_op(wc, fd[u], u, s);
                 t[u] = mfma(a, bh, t[u]);
                 t[u] = mfma(a, bl, t[u]);
               }
@@ -529,15 +561,15 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
       }
     };
 
-    auto step = [&](const uint4 (&wc)[NL], const uint32_t (&sr)[kDownTiles], int v) {
+    auto step = [&](const uint4 (&wc)[NL], int v) {
       if (v < ngs) {
-        if (gon) gate_up(wc, sr, v);
+        if (gon) gate_up(wc, v);
         if (v == ngs - 1) {
           if (SPLIT || gon) act_to_lds();
           __syncthreads();  // every wave's act columns are in LDS
         }
       } else {
-        down(wc, sr, v - ngs);
+        down(wc, v - ngs);
       }
     };
 
@@ -545,8 +577,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 
     for (int v0 = 0; v0 < nv; v0 += NBUF) {
 #pragma unroll
       for (int j = 0; j < NBUF; ++j) {
-        load_step(v0 + j + NBUF - 1, wb[(j + NBUF - 1) % NBUF], sb[(j + NBUF - 1) % NBUF]);
-        if (v0 + j < nv) step(wb[j], sb[j], v0 + j);
+        load_step(v0 + j + NBUF - 1, wb[(j + NBUF - 1) % NBUF]);
+        if (v0 + j < nv) step(wb[j], v0 + j);
       }
     }
     __syncthreads();  // the next pass restages LDS
@@ -669,7 +701,8 @@ template <int FMT, bool ROWS, int RT, typename IdT, int W>
 hipError_t launch_kernel(const FusedLayerArgs& a, int rowcap, hipStream_t s) {
   auto kern = layer_kernel<FMT, ROWS, RT, IdT, W>;
   const size_t xs = x_lds_bytes(rowcap, a.H);
-  const size_t ab = act_lds_bytes(rowcap, W == 2 * kColTiles) + (ROWS ? (size_t)a.H * 4 : 0);
+  const size_t ab = act_lds_bytes(rowcap, W == 2 * kColTiles) + (ROWS ? (size_t)a.H * 4 : 0) +
+                    (FMT == kFmtFP4 ? mx_scale_lds_bytes(a.H) : 0);
   const size_t lds = xs + ab + align_lds_bytes(a.E, a.n, W);
   static std::atomic<size_t> allowed[kMaxCachedDevices];
   const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, allowed);
@@ -725,7 +758,8 @@ bool fused_layer_fits(int fmt, bool scale_rows, int64_t M, int H, int I, int S, 
   if (rowcap > kMaxRowCap) return false;
   const int waves = layer_waves((int)n, H);
   const size_t lds = x_lds_bytes(rowcap, H) + act_lds_bytes(rowcap, waves == 2 * kColTiles) +
-                     (fp8 && scale_rows ? (size_t)H * 4 : 0) + align_lds_bytes(E, (int)n, waves);
+                     (fp8 && scale_rows ? (size_t)H * 4 : 0) + (fmt == kFmtFP4 ? mx_scale_lds_bytes(H) : 0) +
+                     align_lds_bytes(E, (int)n, waves);
   return lds <= kLdsBudget;
 }
 

@@ -69,12 +69,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t d0, uint32_t d1) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// The value of an E8M0 scale byte, 2^(e - 127) (255: NaN), as a float32.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  e &= 0xffu;
-  if (e == 0xffu) return __uint_as_float(0x7fc00000u);
-  if (e == 0u) return __uint_as_float(0x00400000u);  // 2^-127, a float32 subnormal
-  return __uint_as_float(e << 23);
+// The E8M0 scale byte at bit `pos` of `w` as a float32 scale: the bits
+// e << 23, which are 2^(e - 127) exactly for bytes 1..254 (byte 0 gives 0 and
+// byte 255, E8M0's NaN, gives infinity; the library specifies bytes 2..252).
+// Two instructions: a bit-field extract and a shift.
+__device__ __forceinline__ float e8m0_at(uint32_t w, int pos) {
+  return __uint_as_float(__builtin_amdgcn_ubfe(w, pos, 8) << 23);
 }
 
 // 8 E2M1 codes (one dword, lowest nibble first) times `scale` -> 8 bf16
