@@ -61,7 +61,7 @@ def parse():
                          "the headline, not the headline)")
     ap.add_argument("--only-config", default="",
                     help="time one other workload (names as for --other-configs) alone and print its line; for profiling")
-    ap.add_argument("--path", default="auto", choices=["auto", "steps", "single_pass"],
+    ap.add_argument("--path", default="auto", choices=["auto", "steps", "single_pass", "narrow"],
                     help="layer path the descriptors ask for (auto: the library's choice)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device copy 8 times (counter calibration) and exit")
@@ -132,9 +132,13 @@ def traffic_from_profile(digest):
         return None
 
 
-def measure_config(name, dev, steps=50):
+PATH_NAMES = {1: "steps", 2: "single_pass", 3: "narrow"}  # MOE_LAYER_PATH_* values
+
+
+def measure_config(name, dev, steps=50, path=0):
     """Whole-layer time of one workload, with the headline's method: a graph of
-    one step per (weight copy, routing) pair, replayed; weights tiled."""
+    one step per (weight copy, routing) pair, replayed; weights tiled; `path`
+    a MOE_LAYER_PATH_* value (0: the library's choice)."""
     import numpy as np
     import torch
 
@@ -163,7 +167,7 @@ def measure_config(name, dev, steps=50):
     for c in copies:
         sh = c.sh or {}
         layers.append(moe.MoeLayer(c.weight("gate"), c.weight("up"), c.weight("down"), cfg.top_k, cfg.BS,
-                                   sh.get("gate"), sh.get("up"), sh.get("down")).tiled())
+                                   sh.get("gate"), sh.get("up"), sh.get("down")).tiled().with_path(path))
         c.w = c.s = None
         torch.cuda.empty_cache()
     routings = [workloads.routing(cfg.replace(seed=cfg.seed + r)) for r in range(G)]
@@ -193,7 +197,7 @@ def measure_config(name, dev, steps=50):
     res = {
         "layer_us": us, "rows_per_s": cfg.M / (us * 1e-6), "weight_bytes_per_call": nbytes,
         "weight_gbps": nbytes / (us * 1e-6) / 1e9, "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-        "path": "single_pass" if layers[0].path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS else "steps",
+        "path": PATH_NAMES[layers[0].path(cfg.M)],
         "weight_copies": G, "shared_expert_bytes": sh_bytes,
         "workload": f"M={cfg.M} H={cfg.H} E={cfg.E} top_k={cfg.top_k} I={cfg.I} S={cfg.S} BS={cfg.BS} {cfg.wdt}",
     }
@@ -262,7 +266,8 @@ def main():
         return
 
     if args.only_config:
-        res = measure_config(args.only_config, dev, steps=args.steps)
+        forced = {"auto": 0, "steps": 1, "single_pass": 2, "narrow": 3}[args.path]
+        res = measure_config(args.only_config, dev, steps=args.steps, path=forced)
         print(json.dumps({"only_config": args.only_config, **res}))
         return
 
@@ -278,7 +283,7 @@ def main():
     w_d = [torch.from_numpy(w).to(dev) for _, w in routings]
     # the expert weights in the tiled layout (a one-time load-time reordering)
     want = {"auto": moe.MOE_LAYER_PATH_AUTO, "steps": moe.MOE_LAYER_PATH_STEPS,
-            "single_pass": moe.MOE_LAYER_PATH_SINGLE_PASS}[args.path]
+            "single_pass": moe.MOE_LAYER_PATH_SINGLE_PASS, "narrow": moe.MOE_LAYER_PATH_NARROW}[args.path]
     layers = [moe.MoeLayer(c.weight("gate"), c.weight("up"), c.weight("down"), cfg.top_k, cfg.BS).tiled()
               .with_path(want) for c in copies]
     del copies

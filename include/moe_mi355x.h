@@ -273,10 +273,11 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
 
 /* ------------------------------------------------------------ whole layer -- */
 
-/* The two ways moe_layer_forward runs.  A descriptor asks for one with its
+/* The three ways moe_layer_forward runs.  A descriptor asks for one with its
  * `path` field; MOE_LAYER_PATH_AUTO (0) lets the library choose from the
  * descriptor's shapes (never from the routing, so a captured graph stays valid
- * for any routing): the single pass where it fits, else the steps.  (The FP8
+ * for any routing): the narrow path for at most MOE_NARROW_AUTO_SLOTS slots
+ * where it fits, else the single pass where it fits, else the steps.  (The FP8
  * page picks its decode kernel pair the same way, from the shape and a kill
  * switch read once: metrale forward_nvfp4_grouped_decode.rs,
  * nvfp4_grouped_tc_enabled.)
@@ -297,16 +298,31 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
  *    per expert is metrale forward_nvfp4_grouped_decode.rs's; the per-slice
  *    split is this library's.)  Forcing it on a descriptor it does not fit
  *    (row-major weights, more slots, LDS) is refused with MOE_ERR_SHAPE.
+ *  - MOE_LAYER_PATH_NARROW: tiled FP8 weights and at most
+ *    MOE_NARROW_LAYER_MAX_SLOTS slots (a few tokens), within its LDS budget.
+ *    Launch 1 aligns (one workgroup writes the tables) and runs gate+up+SiLU
+ *    per (expert, 16-column tile) with the depth split over 8 waves: each
+ *    wave leaves the MFMA sums of its 128-deep chunks in LDS and one thread
+ *    per output runs the chunk chain in ascending order, writing act (float32
+ *    [n, I] by slot; shared expert [M, S] by token) to the workspace.  Launch 2
+ *    runs down and the blend per 16 rows of H, the 64-deep halves' scaled sums
+ *    added in ascending order.  The same bits as the other two paths.  Forcing
+ *    it on a descriptor it does not fit is refused with MOE_ERR_SHAPE.
  * Environment, read once per process:
- *  - MOE_FORCE_PATH=steps | single_pass replaces MOE_LAYER_PATH_AUTO in every
+ *  - MOE_FORCE_PATH=steps | single_pass | narrow replaces MOE_LAYER_PATH_AUTO in every
  *    descriptor (an explicit `path` wins); any other value is ignored;
  *  - MOE_LOG=1 prints one line to stderr the first time moe_layer_forward runs
  *    each path in the process, naming the path and the layer's shapes. */
 typedef enum {
   MOE_LAYER_PATH_AUTO = 0,
   MOE_LAYER_PATH_STEPS = 1,
-  MOE_LAYER_PATH_SINGLE_PASS = 2
+  MOE_LAYER_PATH_SINGLE_PASS = 2,
+  MOE_LAYER_PATH_NARROW = 3
 } moe_layer_path_kind;
+
+/* Slot counts (M*top_k) the narrow path takes, and up to which AUTO picks it. */
+#define MOE_NARROW_LAYER_MAX_SLOTS 32
+#define MOE_NARROW_AUTO_SLOTS 24
 typedef struct {
   int64_t M;          /* tokens                                       */
   int32_t H;          /* hidden size                                  */
@@ -333,7 +349,8 @@ typedef struct {
  * active_experts, active_count, total (the tables, int32), then float32:
  * act [max_total, I], expert_out [max_total, H], sh_act [M, S], sh_out [M, H]
  * (the steps path), part [ceil(I/64), M*top_k, H] and sh_part [ceil(S/64), M, H]
- * (the single-pass path).  A region the chosen path (or a layer without a shared
+ * (the single-pass path).  The narrow path uses act as [M*top_k, I] by slot
+ * and sh_act [M, S].  A region the chosen path (or a layer without a shared
  * expert) does not use has size 0. */
 #define MOE_LAYER_WORKSPACE_REGIONS 14
 

@@ -42,10 +42,13 @@ from ._ffi import (  # noqa: F401
     MOE_FUSED_ALIGN_MAX_SLOTS,
     MOE_FUSED_LAYER_MAX_SLOTS,
     MOE_LAYER_PATH_AUTO,
+    MOE_LAYER_PATH_NARROW,
     MOE_LAYER_PATH_SINGLE_PASS,
     MOE_LAYER_PATH_STEPS,
     MOE_LAYER_WORKSPACE_REGIONS,
     MOE_MAX_EXPERTS,
+    MOE_NARROW_AUTO_SLOTS,
+    MOE_NARROW_LAYER_MAX_SLOTS,
     MOE_OK,
     MOE_ROUTER_MAX_TOP_K,
     MOE_W_BF16,
@@ -388,7 +391,7 @@ class MoeLayer:
         return list(off)
 
     def path(self, M: int, idt: int = MOE_IDX_I64) -> int:
-        """MOE_LAYER_PATH_STEPS or MOE_LAYER_PATH_SINGLE_PASS for M tokens."""
+        """MOE_LAYER_PATH_STEPS, MOE_LAYER_PATH_SINGLE_PASS or MOE_LAYER_PATH_NARROW for M tokens."""
         d = self.desc(M, idt)
         rc = lib().moe_layer_path(ctypes.byref(d))
         if rc < 0:
@@ -404,15 +407,19 @@ class MoeLayer:
         off = self.workspace_layout(M, idt)
         n = M * self.top_k
         mt = moe_align_max_total(n, self.E, self.BS)
-        single = self.path(M, idt) == MOE_LAYER_PATH_SINGLE_PASS
+        path = self.path(M, idt)
+        narrow = path == MOE_LAYER_PATH_NARROW
         sizes = {
             "sorted_token_ids": (mt,), "block_expert_ids": (mt // self.BS,), "expert_offsets": (self.E + 1,),
             "expert_counts": (self.E,), "token_to_perm": (n,), "active_experts": (moe_active_cap(n, self.E),),
             "active_count": (1,), "total": (1,),
-            "act": (mt, self.I), "expert_out": (mt, self.H), "sh_act": (M, self.S), "sh_out": (M, self.H),
+            "act": (n if narrow else mt, self.I), "expert_out": (mt, self.H), "sh_act": (M, self.S),
+            "sh_out": (M, self.H),
             "part": (-(-self.I // 64), n, self.H), "sh_part": (-(-self.S // 64), M, self.H),
         }
-        used = set(TABLE_FIELDS) | ({"part", "sh_part"} if single else {"act", "expert_out", "sh_act", "sh_out"})
+        used = set(TABLE_FIELDS) | {MOE_LAYER_PATH_SINGLE_PASS: {"part", "sh_part"},
+                                    MOE_LAYER_PATH_NARROW: {"act", "sh_act"}}.get(
+            path, {"act", "expert_out", "sh_act", "sh_out"})
         views = {}
         for i, name in enumerate(WORKSPACE_REGIONS):
             if name not in used or (name.startswith("sh_") and self.S == 0):

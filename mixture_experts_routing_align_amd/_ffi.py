@@ -32,6 +32,9 @@ MOE_FUSED_LAYER_MAX_SLOTS = 256
 MOE_LAYER_PATH_AUTO = 0
 MOE_LAYER_PATH_STEPS = 1
 MOE_LAYER_PATH_SINGLE_PASS = 2
+MOE_LAYER_PATH_NARROW = 3
+MOE_NARROW_LAYER_MAX_SLOTS = 32
+MOE_NARROW_AUTO_SLOTS = 24
 MOE_LAYER_WORKSPACE_REGIONS = 14
 MOE_NOALLOC_WORKSPACE_BYTES = 64 << 20
 

@@ -192,13 +192,14 @@ moe::GroupedArgs gate_up_args(const void* x_bf16, const moe_weight* gate, const 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // MOE_FORCE_PATH, read once per process: the path that replaces
-// MOE_LAYER_PATH_AUTO ("steps" or "single_pass"; anything else: none).
+// MOE_LAYER_PATH_AUTO ("steps", "single_pass" or "narrow"; anything else: none).
 int forced_path() {
   static const int forced = [] {
     const char* v = getenv("MOE_FORCE_PATH");
     if (v == nullptr) return (int)MOE_LAYER_PATH_AUTO;
     if (!strcmp(v, "steps")) return (int)MOE_LAYER_PATH_STEPS;
     if (!strcmp(v, "single_pass")) return (int)MOE_LAYER_PATH_SINGLE_PASS;
+    if (!strcmp(v, "narrow")) return (int)MOE_LAYER_PATH_NARROW;
     return (int)MOE_LAYER_PATH_AUTO;
   }();
   return forced;
@@ -206,18 +207,29 @@ int forced_path() {
 
 // The path moe_layer_forward takes for a checked descriptor (shape only, never
 // the routing): the one the descriptor (else MOE_FORCE_PATH) asks for, or by
-// default the single-pass layer where it fits (tiled weights at decode width).
-// A forced single pass that does not fit is refused.
+// default the narrow path for a few tokens, else the single-pass layer where
+// it fits (tiled weights at decode width), else the steps.  A forced path that
+// does not fit is refused.
 int layer_path(const char* fn, const moe_layer_desc* d) {
+  static_assert(MOE_NARROW_LAYER_MAX_SLOTS == moe::kNarrowLayerMaxSlots, "narrow slot limit");
+  const int64_t n = d->M * d->top_k;
   const bool fits = is_tiled(d->wdt) &&
                     moe::fused_layer_fits(fmt_of(d->wdt), is_rows(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
+  const bool narrow_fits =
+      is_tiled(d->wdt) && moe::narrow_layer_fits(fmt_of(d->wdt), d->M, d->H, d->I, d->S, d->E, d->top_k);
   const int want = d->path != MOE_LAYER_PATH_AUTO ? (int)d->path : forced_path();
   if (want == MOE_LAYER_PATH_STEPS) return MOE_LAYER_PATH_STEPS;
   if (want == MOE_LAYER_PATH_SINGLE_PASS && !fits)
     return fail(MOE_ERR_SHAPE,
                 "%s: the single-pass path needs tiled weights, at most %d slots (M*top_k = %lld) and its LDS "
                 "budget",
-                fn, MOE_FUSED_LAYER_MAX_SLOTS, (long long)(d->M * d->top_k));
+                fn, MOE_FUSED_LAYER_MAX_SLOTS, (long long)n);
+  if (want == MOE_LAYER_PATH_NARROW && !narrow_fits)
+    return fail(MOE_ERR_SHAPE,
+                "%s: the narrow path needs tiled FP8 weights, at most %d slots (M*top_k = %lld) and its LDS budget",
+                fn, MOE_NARROW_LAYER_MAX_SLOTS, (long long)n);
+  if (want != MOE_LAYER_PATH_AUTO) return want;
+  if (narrow_fits && n <= MOE_NARROW_AUTO_SLOTS) return MOE_LAYER_PATH_NARROW;
   return fits ? MOE_LAYER_PATH_SINGLE_PASS : MOE_LAYER_PATH_STEPS;
 }
 
@@ -232,7 +244,7 @@ void log_path_once(const moe_layer_desc* d, int path) {
   static std::atomic<unsigned> logged{0};
   const unsigned bit = 1u << path;
   if (logged.fetch_or(bit) & bit) return;
-  static const char* names[] = {"auto", "steps", "single_pass"};
+  static const char* names[] = {"auto", "steps", "single_pass", "narrow"};
   static const char* wnames[] = {"bf16",          "fp8_e4m3",            "bf16_tiled", "fp8_e4m3_tiled",
                                  "fp8_e4m3_rows", "fp8_e4m3_rows_tiled", "mxfp4",      "mxfp4_tiled"};
   fprintf(stderr,
@@ -252,7 +264,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
   if (d->idt != MOE_IDX_I32 && d->idt != MOE_IDX_I64)
     return fail(MOE_ERR_SHAPE, "%s: unknown index dtype %d", fn, (int)d->idt);
   if (d->S < 0) return fail(MOE_ERR_SHAPE, "%s: S=%d is negative", fn, d->S);
-  if (d->path < MOE_LAYER_PATH_AUTO || d->path > MOE_LAYER_PATH_SINGLE_PASS)
+  if (d->path < MOE_LAYER_PATH_AUTO || d->path > MOE_LAYER_PATH_NARROW)
     return fail(MOE_ERR_SHAPE, "%s: unknown path %d", fn, (int)d->path);
   if ((rc = check_projection(fn, "gate/up", d->wdt, d->I, d->H))) return rc;
   if ((rc = check_projection(fn, "down", d->wdt, d->H, d->I))) return rc;
@@ -263,7 +275,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
   const int lp = layer_path(fn, d);
   if (lp < 0) return lp;
   if (path) *path = lp;
-  const bool single = lp == MOE_LAYER_PATH_SINGLE_PASS;
+  const bool single = lp == MOE_LAYER_PATH_SINGLE_PASS, narrow = lp == MOE_LAYER_PATH_NARROW;
   const size_t mt = (size_t)s.max_total, n = (size_t)s.n, M = (size_t)d->M, H = (size_t)d->H;
   const size_t S = (size_t)d->S, I = (size_t)d->I;
   size_t cur = 0;
@@ -279,10 +291,10 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
   take(5, (size_t)s.cap * 4);                             // active_experts
   take(6, 4);                                             // active_count
   take(7, 4);                                             // total
-  take(8, single ? 0 : mt * I * 4);                       // act
-  take(9, single ? 0 : mt * H * 4);                       // expert_out
+  take(8, single ? 0 : (narrow ? n : mt) * I * 4);        // act (narrow: by slot)
+  take(9, single || narrow ? 0 : mt * H * 4);             // expert_out
   take(10, single ? 0 : M * S * 4);                       // sh_act
-  take(11, single ? 0 : M * H * 4);                       // sh_out
+  take(11, single || narrow ? 0 : M * H * 4);             // sh_out
   take(12, single ? ((I + 63) / 64) * n * H * 4 : 0);     // part: per 64-wide slice of I, per slot
   take(13, single ? ((S + 63) / 64) * M * H * 4 : 0);     // sh_part: per 64-wide slice of S, per token
   off[14] = cur;
@@ -293,7 +305,7 @@ int layout(const moe_layer_desc* d, size_t off[MOE_LAYER_WORKSPACE_REGIONS + 1],
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 10; }
+int32_t moe_abi_version(void) { return 11; }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
@@ -670,6 +682,12 @@ int moe_layer_forward(const moe_layer_desc* d, const void* x_bf16, const void* t
     const moe::FusedLayerArgs a = single_pass_args(d, ws, off, x_bf16, topk_ids, topk_weights, out_bf16);
     if ((rc = hip_status(moe::launch_layer_partials(a, fmt_of(d->wdt), stream), fn))) return rc;
     return hip_status(moe::launch_blend_partials(a, stream), fn);
+  }
+  if (path == MOE_LAYER_PATH_NARROW) {
+    moe::FusedLayerArgs a = single_pass_args(d, ws, off, x_bf16, topk_ids, topk_weights, out_bf16);
+    a.act = reinterpret_cast<float*>(ws + off[8]);
+    a.sh_act = d->S > 0 ? reinterpret_cast<float*>(ws + off[10]) : nullptr;
+    return hip_status(moe::launch_narrow_layer(a, stream), fn);
   }
   const bool shared = d->S > 0;
   const int64_t n = d->M * d->top_k;

@@ -106,18 +106,20 @@ __device__ __forceinline__ int k_of_step(int s, int q) {
   return BYTES ? ((s >> 1) * 64 + q * 16 + (s & 1) * 8) : (s * 32 + q * 8);
 }
 
-// Gate of the shared expert for one token, sigmoid(x . g), for a 256-thread
-// workgroup (every thread gets it): thread j sums h = j, j + 256, ... with
-// float32 fused multiply-adds in ascending h, and the 256 partial sums meet in
-// a fixed tree through `red` (256 floats of LDS).  Both blend kernels call it,
-// so a token's gate has the same bits on either path.  Contains barriers:
-// every thread of the workgroup calls it.
+// Gate of the shared expert for one token, sigmoid(x . g), computed by the
+// first 256 threads of the workgroup (every thread gets it): thread j sums
+// h = j, j + 256, ... with float32 fused multiply-adds in ascending h, and the
+// 256 partial sums meet in a fixed tree through `red` (256 floats of LDS).
+// Every blend kernel calls it, so a token's gate has the same bits on every
+// path.  Contains barriers: every thread of the workgroup (at least 256) calls it.
 __device__ inline float shared_gate256(const uint16_t* __restrict__ x, const uint16_t* __restrict__ g, int H,
                                        float* red) {
   const int j = threadIdx.x;
-  float s = 0.f;
-  for (int h = j; h < H; h += 256) s = fmaf(bf16_bits_to_f32(x[h]), bf16_bits_to_f32(g[h]), s);
-  red[j] = s;
+  if (j < 256) {
+    float s = 0.f;
+    for (int h = j; h < H; h += 256) s = fmaf(bf16_bits_to_f32(x[h]), bf16_bits_to_f32(g[h]), s);
+    red[j] = s;
+  }
   __syncthreads();
   for (int d = 128; d > 0; d >>= 1) {
     if (j < d) red[j] = add_rn(red[j], red[j + d]);

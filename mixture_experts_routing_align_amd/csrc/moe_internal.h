@@ -172,6 +172,8 @@ struct FusedLayerArgs {
   uint16_t* out;          // bf16 [M, H]
   float* part;            // [ceil(I/64)][n][H] routed partials by slot
   float* sh_part;         // [ceil(S/64)][M][H] shared partials by token
+  float* act;             // narrow path: float32 [n][I] act by slot
+  float* sh_act;          // narrow path: float32 [M][S] shared act by token
   int M, H, I, S, E, top_k, BS, n, cap, max_total;
   AlignOut tables;
 };
@@ -188,6 +190,13 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
 hipError_t launch_router(const void* x, const void* w, int M, int H, int E, int top_k, float* logits, void* ids,
                          bool ids64, float* wts, hipStream_t s);
 hipError_t launch_blend_partials(const FusedLayerArgs& a, hipStream_t s);
+
+// Narrow-width layer (narrow.hip): gate+up with the depth split over 8 waves
+// per (expert, 16-column tile), then down + blend per 16 rows of H.  FP8 tiled
+// weights, at most kNarrowLayerMaxSlots slots; the same bits as the other paths.
+constexpr int kNarrowLayerMaxSlots = 32;
+bool narrow_layer_fits(int fmt, int64_t M, int H, int I, int S, int E, int top_k);
+hipError_t launch_narrow_layer(const FusedLayerArgs& a, hipStream_t s);
 
 hipError_t launch_blend(uint16_t* out, const float* expert_out, const float* w, const int32_t* perm,
                         const float* sh_out, const void* x, const void* sh_gate, int M, int H, int top_k,

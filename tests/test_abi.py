@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.moe_abi_version() == 10
+    assert lib.moe_abi_version() == 11
 
 
 @pytest.mark.parametrize("seed", range(5))
@@ -292,6 +292,41 @@ def test_path_control(lib):
     assert "path" in _err(lib)
 
 
+def test_narrow_path_control(lib):
+    """AUTO takes the narrow path for tiled FP8 weights and at most
+    MOE_NARROW_AUTO_SLOTS slots; forcing it elsewhere (BF16, row-major, more
+    than MOE_NARROW_LAYER_MAX_SLOTS slots) is refused; its workspace holds act
+    by slot and no expert_out, sh_out or partials."""
+    P = _ffi
+    for M, want in ((1, P.MOE_LAYER_PATH_NARROW), (2, P.MOE_LAYER_PATH_NARROW), (3, P.MOE_LAYER_PATH_NARROW),
+                    (4, P.MOE_LAYER_PATH_SINGLE_PASS), (8, P.MOE_LAYER_PATH_SINGLE_PASS)):
+        assert lib.moe_layer_path(ctypes.byref(_tiled(_desc(M=M)))) == want, M
+    four = _tiled(_desc(M=4))                           # 32 slots of 768-wide act: past the LDS budget
+    four.path = P.MOE_LAYER_PATH_NARROW
+    assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_ERR_SHAPE
+    four = _tiled(_desc(M=4, H=1024, I=256))            # 32 slots of a smaller layer: narrow when asked for
+    assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_LAYER_PATH_SINGLE_PASS
+    four.path = P.MOE_LAYER_PATH_NARROW
+    assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_LAYER_PATH_NARROW
+    five = _tiled(_desc(M=5, H=1024, I=256))
+    five.path = P.MOE_LAYER_PATH_NARROW
+    assert lib.moe_layer_path(ctypes.byref(five)) == P.MOE_ERR_SHAPE
+    assert "narrow" in _err(lib)
+    for d in (_desc(M=1), _tiled(_desc(M=1, wdt=0))):   # row-major FP8; tiled BF16
+        d.path = P.MOE_LAYER_PATH_NARROW
+        assert lib.moe_layer_path(ctypes.byref(d)) == P.MOE_ERR_SHAPE
+    b = _tiled(_desc(M=1, wdt=0))
+    assert lib.moe_layer_path(ctypes.byref(b)) == P.MOE_LAYER_PATH_SINGLE_PASS
+    s = _tiled(_desc(M=2, S=2048))
+    assert lib.moe_layer_path(ctypes.byref(s)) == P.MOE_LAYER_PATH_NARROW
+    off = (ctypes.c_size_t * (P.MOE_LAYER_WORKSPACE_REGIONS + 1))()
+    assert lib.moe_layer_workspace_layout(ctypes.byref(s), off) == P.MOE_OK
+    size = [off[i + 1] - off[i] for i in range(P.MOE_LAYER_WORKSPACE_REGIONS)]
+    assert size[8] >= 16 * 768 * 4 and size[8] < 16 * 768 * 4 + 256     # act [n, I] by slot
+    assert size[9] == 0 and size[11] == 0 and size[12] == 0 and size[13] == 0
+    assert size[10] >= 2 * 2048 * 4                                     # sh_act [M, S]
+
+
 FORCE_SCRIPT = """
 import ctypes, sys
 sys.path.insert(0, {root!r})
@@ -307,7 +342,8 @@ print(auto, explicit, lib.moe_layer_path(ctypes.byref(r)))
 """
 
 
-@pytest.mark.parametrize("env,want", [("steps", (1, 2, 1)), ("single_pass", (2, 2, -2)), ("bogus", (2, 2, 1))])
+@pytest.mark.parametrize("env,want", [("steps", (1, 2, 1)), ("single_pass", (2, 2, -2)), ("bogus", (2, 2, 1)),
+                                      ("narrow", (-2, 2, -2))])
 def test_force_path_environment(env, want):
     """MOE_FORCE_PATH replaces AUTO in every descriptor (an explicit path wins;
     a forced single pass that does not fit is refused); read once, so each case
@@ -365,6 +401,7 @@ def test_shared_gate_needs_a_shared_expert(lib):
     assert lib.moe_layer_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
     assert "shared gate" in _err(lib)
     t = _tiled(_desc(M=4, H=256, E=8, top_k=2, I=128, S=128))   # single pass, gated: blend needs x
+    t.path = _ffi.MOE_LAYER_PATH_SINGLE_PASS
     t.sh_expert_gate = FAKE
     need = lib.moe_layer_workspace_bytes(ctypes.byref(t))
     assert lib.moe_layer_blend_partials(ctypes.byref(t), None, FAKE, FAKE, FAKE, 0x100000, need,

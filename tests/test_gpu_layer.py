@@ -32,8 +32,10 @@ def model_for(name, **kw):
     return _MODELS[name]
 
 
-def _run_layer(moe, model, xt, it, wt, tiled=False):
+def _run_layer(moe, model, xt, it, wt, tiled=False, path=None):
     layer = model.tiled_layer() if tiled else model.layer()
+    if path is not None:
+        layer = layer.with_path(path)
     ws = layer.alloc_workspace(xt.shape[0], moe.MOE_IDX_I64 if it.dtype == torch.int64 else moe.MOE_IDX_I32)
     out = layer.forward(xt, it, wt, workspace=ws)
     torch.cuda.synchronize()
@@ -539,7 +541,7 @@ def test_narrow_width_kernel(moe, m):
     (x, ids, w), (xt, it, wt) = device_inputs(model.cfg)
     x, ids, w = x[:m], ids[:m], w[:m]
     xt, it, wt = xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous()
-    tiled = model.tiled_layer()
+    tiled = model.tiled_layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS)  # AUTO takes the narrow path here
     assert tiled.path(m) == moe.MOE_LAYER_PATH_SINGLE_PASS
     a = tiled.forward(xt, it, wt)
     b = model.layer().forward(xt, it, wt)
@@ -560,10 +562,11 @@ def test_row_scales_single_pass(moe, name):
     cfg = next(c for c in ODD if c.name == name)
     model = DeviceModel(cfg, threads=4)
     (x, ids, w), (xt, it, wt) = device_inputs(cfg)
-    assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    single = moe.MOE_LAYER_PATH_SINGLE_PASS  # the one-token case would take the narrow path under AUTO
+    assert model.tiled_layer().with_path(single).path(cfg.M) == single
     assert model.tiled_layer().wdt == moe.MOE_W_FP8_E4M3_ROWS_TILED
     log(f"row-scale single pass: {cfg}")
-    out, views = _run_layer(moe, model, xt, it, wt, tiled=True)
+    out, views = _run_layer(moe, model, xt, it, wt, tiled=True, path=single)
     ref = oracle_layer(model, x, ids, w)
     compare_tables(views, ref["tables"])
     ok, err, bound = tolerance_ok(bf16_to_np(out), ref["out"])
