@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=4, help="weight copies / routings cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-reps", type=int, default=25)
-    ap.add_argument("--other-configs", default="verify",
+    ap.add_argument("--other-configs", default="verify,decode_m1,decode_mxfp4",
                     help="comma-separated workloads (tiny, decode, verify, large, or decode_mN: the decode "
                          "layer at N tokens; a _rows suffix: the same with per-row FP8 scales, _mxfp4: with "
                          "MXFP4 experts) also timed whole-layer and reported under other_configs (context for "
