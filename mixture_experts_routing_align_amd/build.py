@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
 SOURCES = ["align.hip", "grouped.hip", "grouped_gu_fp8.hip", "grouped_gu_bf16.hip", "grouped_gu_fp4.hip",
-           "grouped_down_fp8.hip", "grouped_down_bf16.hip", "grouped_down_fp4.hip", "layer_fused.hip", "narrow.hip", "blend.hip", "probe.hip", "router.hip", "noalloc.hip", "api.cpp"]
+           "grouped_down_fp8.hip", "grouped_down_bf16.hip", "grouped_down_fp4.hip", "layer_fused.hip", "narrow.hip", "wide.hip", "blend.hip", "probe.hip", "router.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # packed-fp32-ops stay off: the compiler emits no v_pk_{add,mul,fma}_f32.

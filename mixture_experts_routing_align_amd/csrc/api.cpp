@@ -392,6 +392,7 @@ int moe_grouped_gate_up_silu(const void* x_bf16, moe_weight_dtype wdt, const moe
   }
   moe::GroupedArgs a = gate_up_args(x_bf16, gate, up, t, act, sh_gate, sh_up, sh_act, M, H, I, S, top_k, s.cap);
   a.scale_rows = is_rows(wdt);
+  a.E = E;
   return hip_status(
       moe::launch_grouped_gate_up(a, fmt_of(wdt), is_tiled(wdt), stream), fn);
 }
@@ -482,6 +483,7 @@ int moe_grouped_down(const float* act, moe_weight_dtype wdt, const moe_weight* d
   a.M = (int)M;
   a.top_k = top_k;
   a.cap = s.cap;
+  a.E = E;
   a.scale_rows = is_rows(wdt);
   return hip_status(
       moe::launch_grouped_down(a, fmt_of(wdt), is_tiled(wdt), stream), fn);

@@ -1,0 +1,608 @@
+// Wide-pass grouped projections for gfx950: every row an expert holds, up to
+// 64 at a time, in one workgroup per (expert, column group), so an expert's
+// weights are streamed once per column group instead of once per 16-row pass.
+// For layers whose experts hold many rows (verify and prefill widths); FP8
+// weights (block or row scales), tiled or row-major.
+//
+// What is computed is the grouped projection of the pass kernels
+// (grouped_impl.h; metrale fp8_moe_grouped.rs: the gate+up and down launchers;
+// nbxtensor moe_decode_vec.py: the SwiGLU epilogue), with the same arithmetic
+// for every output element:
+//   gate+up: per 128-deep chunk c (one FP8 scale block), t = the chunk's 4 MFMA
+//            steps from zero, acc = fma(scale_c, t, acc), c ascending;
+//            act = silu(g) * u
+//   down:    per 64-deep half h, t = its 2 MFMA steps over bf16 hi then lo of
+//            act, from zero; acc = acc + scale * t, both rounded, h ascending
+// so a row has the same bits whichever kernel (or layer path) runs it.
+//
+// gfx950 design.  4 waves.  Each wave streams its own weight rows (16 gate and
+// 16 up columns; or 4 x 16 rows of the down output) straight from HBM into a
+// 3-step register ring, 16-byte loads, no LDS.  The expert's activation rows
+// (bf16 x, or act split into bf16 hi + lo) are shared by the 4 waves through
+// two LDS slots: each thread requests its 4 pieces of the rows two steps ahead
+// into registers and writes them to LDS one step ahead, with one barrier per
+// step, so neither the weights nor the rows wait a round trip per step.
+// Rows past the expert's count repeat its last row (valid addresses) and only
+// reach outputs that are never stored.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+
+#include "align_device.h"
+#include "mma_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace wide_detail {
+
+using namespace mma;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRows = 32;                                // rows per routed pass
+constexpr int kShRows = 32;                              // rows (tokens) per shared-expert pass
+constexpr int kRT = kRows / 16;                          // 16-row tiles per pass
+constexpr int kGuCols = kWaves * kWaveCols;              // gate+up columns per workgroup
+constexpr int kDnTiles = 4;                              // down: 16-row output tiles per wave
+constexpr int kDnCols = kWaves * kDnTiles * kWaveCols;   // down output rows (of H) per routed workgroup
+constexpr int kDnShCols = kWaves * kWaveCols;            // per shared-expert workgroup (one tile per wave)
+constexpr int kNbuf = 4;                                 // weight steps in the register ring (3 ahead)
+constexpr int kMaxScaleBlocks = 128;                     // FP8 depth limit: 128 scale blocks
+constexpr int kSL = kMaxScaleBlocks / 64;
+constexpr int kXStride = kKC + kPad;                     // staged x row, bf16 elements (one chunk)
+constexpr size_t kGuLds = (size_t)2 * kRows * kXStride * 2;      // two slots
+constexpr int kPieces = kRows * 16 / kThreads;           // 16-byte row pieces per thread per step
+static_assert(kPieces * kThreads == kRows * 16, "each thread stages kPieces pieces: rows u*16 + tid/16");
+// 16 bytes as a native vector: a register copy, where the uint4 struct would
+// be copied through private memory
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Staged rows and the down weights are read with buffer loads: a load whose
+// offset lies past the resource's size returns zeros and fetches nothing, so
+// rows past an expert's count (and a wave's tiles past the output) cost no
+// memory traffic and need no branch around their loads.
+constexpr uint32_t kNoFetch = 0x80000000u;  // past every resource this file builds (each < 2^31 bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// Which pass routed item j is: the active experts in ascending order, each
+// contributing ceil(count / kRows) passes.  Every thread takes a run of active
+// indices, a block scan of their pass counts places the runs, and the thread
+// whose run holds pass j publishes (expert, first row, count, offset).
+// e = -1: the routing has fewer passes.  Contains barriers.
+struct Pass {
+  int e, r0, count, offset;
+};
+__device__ __forceinline__ Pass locate_pass(const GroupedArgs& p, int j, int* s_item) {
+  constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  const int per = (p.cap + kThreads - 1) / kThreads;
+  const int a0 = min(p.cap, tid * per);
+  int ex[kPer], cn[kPer], np = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) ex[i] = (i < per && a0 + i < p.cap) ? p.active_experts[a0 + i] : -1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cn[i] = ex[i] >= 0 ? p.expert_counts[ex[i]] : 0;
+    np += (cn[i] + kRows - 1) / kRows;
+  }
+  if (tid == 0) s_item[0] = -1;
+  int base, unused_ex, total, unused_tot;
+  align_dev::block_scan2<kWaves>(np, 0, s_item + 4, s_item + 4 + kWaves, base, unused_ex, total, unused_tot);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int npi = (cn[i] + kRows - 1) / kRows;
+    if (j >= base && j < base + npi) {
+      s_item[0] = ex[i];
+      s_item[1] = (j - base) * kRows;
+      s_item[2] = cn[i];
+      s_item[3] = p.expert_offsets[ex[i]];
+    }
+    base += npi;
+  }
+  __syncthreads();
+  return Pass{s_item[0], s_item[1], s_item[2], s_item[3]};
+}
+
+// the FP8 block scale of chunk c from the lane-indexed registers
+__device__ __forceinline__ float block_scale(const float (&sr)[kSL], int c) {
+  const float v = (kSL == 1 || c < 64) ? sr[0] : sr[kSL - 1];
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), c & 63));
+}
+
+// ------------------------------------------------------------------ gate+up --
+
+// one 128-deep chunk: gate and up from the ring, x rows from LDS slot xb
+template <bool ROWS>
+__device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t* __restrict__ xb, int nrt, int q,
+                                         int r16, float sg, float su, const f32x4 (&rs)[2], f32x4 (&acc)[2][kRT]) {
+  bf16x8 a[2][4];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 v = w[st][s >> 1];
+      a[st][s] = (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
+    }
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt < nrt) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(xb + (rt * 16 + r16) * kXStride + k_of_step<true>(s, q)));
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) t = mfma(a[st][s], b[s], t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[st][rt][i] = fmaf(ROWS ? rs[st][i] : (st == 0 ? sg : su), t[i], acc[st][rt][i]);
+      }
+    }
+  }
+}
+
+// Grid (1-D): the shared expert's (64-token pass, 64-column group) units, then
+// the routed (pass item, 64-column group) units with the column group fastest,
+// so the routing's real passes come first and the items past them (the grid
+// covers the most passes any routing of n slots can need) come last and exit.
+template <bool ROWS, bool TILED>
+__global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [2][kRows][kXStride]
+  __shared__ int s_src[kRows];
+  __shared__ int s_item[4 + 2 * kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int sng = p.sw0 != nullptr ? p.sN / kGuCols : 0;
+  const int nshared = p.sgroups * sng;
+  const bool routed = (int)blockIdx.x >= nshared;
+  int g, e = 0, r0 = 0, nr, row_base;
+  if (routed) {
+    const int r = (int)blockIdx.x - nshared;
+    const int ng = p.N / kGuCols;
+    const Pass ps = locate_pass(p, r / ng, s_item);
+    if (ps.e < 0) return;
+    g = r % ng;
+    e = ps.e;
+    r0 = ps.r0;
+    nr = min(kRows, ps.count - r0);
+    row_base = ps.offset;
+  } else {
+    g = (int)blockIdx.x % sng;
+    row_base = (int)blockIdx.x / sng * kShRows;
+    nr = min(kShRows, p.M - row_base);
+  }
+  const int N = routed ? p.N : p.sN, K = routed ? p.K : p.sK;
+  const int nch = K / kKC;
+  const int wcol = g * kGuCols + wave * kWaveCols;
+
+  const size_t wstride = (size_t)N * K;
+  const char* W0 = routed ? static_cast<const char*>(p.w0) + (size_t)e * wstride : static_cast<const char*>(p.sw0);
+  const char* W1 = routed ? static_cast<const char*>(p.w1) + (size_t)e * wstride : static_cast<const char*>(p.sw1);
+  const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
+  const float* S0 = routed ? static_cast<const float*>(p.s0) + (size_t)e * sstride : static_cast<const float*>(p.ss0);
+  const float* S1 = routed ? static_cast<const float*>(p.s1) + (size_t)e * sstride : static_cast<const float*>(p.ss1);
+  // tiled: the wave's 16-column tile is one run of 2 KB chunk fragments, this
+  // lane's 16 bytes at 16 * lane of each 1 KB half; row-major: the lane's row
+  const size_t lo = TILED ? (size_t)(wcol / kWaveCols) * K * kWaveCols + lane * 16 : (size_t)(wcol + r16) * K + q * 16;
+  const char* lp0 = W0 + lo;
+  const char* lp1 = W1 + lo;
+
+  // the row sources: the token of each row
+  if (tid < nr) s_src[tid] = routed ? p.sorted_token_ids[row_base + r0 + tid] / p.top_k : row_base + tid;
+
+  // scales: per lane one 128x128 block of the wave's columns, or (ROWS) the
+  // row scales of the lane's 4 output columns
+  float sreg[2][kSL];
+  f32x4 rs[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const float* sp = st == 0 ? S0 : S1;
+    if constexpr (ROWS) {
+      rs[st] = *reinterpret_cast<const f32x4*>(sp + wcol + 4 * q);
+#pragma unroll
+      for (int i = 0; i < kSL; ++i) sreg[st][i] = 0.f;
+    } else {
+      const int kb = K / kFp8Block;
+      const float* sw = sp + (size_t)(wcol / kFp8Block) * kb;
+#pragma unroll
+      for (int i = 0; i < kSL; ++i) sreg[st][i] = lane + 64 * i < kb ? sw[lane + 64 * i] : 0.f;
+      rs[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __syncthreads();  // s_src
+
+  // x [M, K] bf16 as a buffer; this thread's rows u*16 + prow, 16-byte piece
+  // ppc of each chunk (rows past the count: no fetch, zeros)
+  const __amdgpu_buffer_rsrc_t xrs =
+      rsrc(routed ? p.x : p.sx, (uint32_t)((size_t)p.M * K * 2));
+  const int prow = tid >> 4, ppc = tid & 15;
+  uint32_t xo[kPieces];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u)
+    xo[u] = u * 16 + prow < nr ? (uint32_t)(((size_t)s_src[u * 16 + prow] * K + ppc * 8) * 2) : kNoFetch;
+  uint16_t* xdst = xs + prow * kXStride + ppc * 8;
+
+  uint4 wb[kNbuf][2][2];
+  u32x4 xr[2][kPieces];
+  f32x4 acc[2][kRT];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) acc[st][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nrt = (nr + 15) >> 4;
+
+#define WIDE_LOAD_W(c, W)                                                                             \
+  {                                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                  \
+      const size_t off = TILED ? (size_t)(c) * (kKC * kWaveCols) + j * 1024 : (size_t)(c) * kKC + j * 64; \
+      (W)[0][j] = *reinterpret_cast<const uint4*>(lp0 + off);                                        \
+      (W)[1][j] = *reinterpret_cast<const uint4*>(lp1 + off);                                        \
+    }                                                                                                 \
+  }
+#define WIDE_LOAD_X(c, R)                                                                                         \
+  {                                                                                                               \
+    _Pragma("unroll") for (int u = 0; u < kPieces; ++u)(R)[u] = bload(xrs, xo[u] + (uint32_t)(c) * (kKC * 2));  \
+  }
+#define WIDE_STORE_X(slot, R)                                                                                     \
+  {                                                                                                               \
+    _Pragma("unroll") for (int u = 0; u < kPieces; ++u) *reinterpret_cast<u32x4*>(                              \
+        xdst + (slot) * (kRows * kXStride) + u * 16 * kXStride) = (R)[u];                                        \
+  }
+
+  // prologue: x of chunks 0, 1 and weights of chunks 0, 1, 2 requested, x(0) staged
+  WIDE_LOAD_X(0, xr[0]);
+  WIDE_LOAD_W(0, wb[0]);
+  WIDE_LOAD_X(1, xr[1]);
+  WIDE_LOAD_W(1, wb[1]);
+  WIDE_LOAD_W(2, wb[2]);
+  WIDE_STORE_X(0, xr[0]);
+  __syncthreads();
+  // step c: request x(c + 2) and the weights of c + 3 (wrapped past the end:
+  // valid memory, never used), multiply chunk c (ring slot c % 4, LDS slot
+  // c % 2), stage x(c + 1), barrier.  Four steps written out, so every ring
+  // index is a constant and no step is conditional (a load under a branch
+  // costs a full wait for every load in flight); nch is a multiple of 4.
+#define WIDE_GU_STEP(JJ)                                                                                   \
+  {                                                                                                        \
+    const int c = c0 + (JJ);                                                                               \
+    WIDE_LOAD_X((c + 2) % nch, xr[(JJ) % 2]);                                                              \
+    WIDE_LOAD_W((c + 3) % nch, wb[((JJ) + 3) % 4]);                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+    gu_chunk<ROWS>(wb[(JJ) % 4], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, block_scale(sreg[0], c), \
+                   block_scale(sreg[1], c), rs, acc);                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+    WIDE_STORE_X(((JJ) + 1) % 2, xr[((JJ) + 1) % 2]);                                                      \
+    __syncthreads();                                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+  }
+  for (int c0 = 0; c0 < nch; c0 += 4) {
+    WIDE_GU_STEP(0)
+    WIDE_GU_STEP(1)
+    WIDE_GU_STEP(2)
+    WIDE_GU_STEP(3)
+  }
+#undef WIDE_GU_STEP
+#undef WIDE_LOAD_W
+#undef WIDE_LOAD_X
+#undef WIDE_STORE_X
+
+  float* OUT = routed ? p.out : p.sout;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int r = rt * 16 + r16;
+    if (rt < nrt && r < nr) {
+      float4 v;
+      v.x = silu_mul(acc[0][rt][0], acc[1][rt][0]);
+      v.y = silu_mul(acc[0][rt][1], acc[1][rt][1]);
+      v.z = silu_mul(acc[0][rt][2], acc[1][rt][2]);
+      v.w = silu_mul(acc[0][rt][3], acc[1][rt][3]);
+      *reinterpret_cast<float4*>(OUT + (size_t)(row_base + r0 + r) * N + wcol + 4 * q) = v;
+    }
+  }
+}
+
+// --------------------------------------------------------------------- down --
+
+constexpr int kAStride = 64 + kPad;                          // staged act row, bf16 elements (one half)
+constexpr size_t kDnLds = (size_t)2 * 2 * kRows * kAStride * 2;  // two slots of (hi, lo)
+constexpr int kDnRing = 3;                                   // weight halves in the register ring (2 ahead)
+constexpr int kDnSets = 3;                                   // act register sets (requested 3 halves ahead)
+
+// one 64-deep half: the wave's output tiles from the ring, act rows (hi, lo)
+// from LDS slot ab
+template <bool ROWS>
+__device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16_t* __restrict__ ab, int nrt, int q,
+                                        int r16, int ntl, float sc, const f32x4 (&rs)[kDnTiles],
+                                        f32x4 (&acc)[kDnTiles][kRT]) {
+  bf16x8 a[kDnTiles][2];
+#pragma unroll
+  for (int tt = 0; tt < kDnTiles; ++tt) {
+    a[tt][0] = fp8x8_to_bf16(w[tt].x, w[tt].y);
+    a[tt][1] = fp8x8_to_bf16(w[tt].z, w[tt].w);
+  }
+  constexpr int plane = kRows * kAStride;
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    if (rt < nrt) {
+      bf16x8 b[2][2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          b[x][s] = as_bf16x8(
+              *reinterpret_cast<const uint4*>(ab + x * plane + (rt * 16 + r16) * kAStride + q * 16 + s * 8));
+#pragma unroll
+      for (int tt = 0; tt < kDnTiles; ++tt) {
+        if (tt < ntl) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) t = mfma(a[tt][s], b[x][s], t);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][rt][i] = add_rn(acc[tt][rt][i], mul_rn(ROWS ? rs[tt][i] : sc, t[i]));
+        }
+      }
+    }
+  }
+}
+
+// Grid (1-D): the shared expert's (32-token pass, 64-row group of H) units,
+// then the routed (pass item, 256-row group) units, the group fastest.  A
+// routed wave owns output tiles 4 (4g + w) .. +3, a shared wave tile 4g + w
+// (tiles past N: none of its work).  The halves run in rounds of 3 (the ring
+// lengths); a round past the depth multiplies zeros (its loads lie past their
+// buffers and fetch nothing; scale 0), which leaves every sum as it is.
+template <bool ROWS, bool TILED>
+__global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t as[];  // [2 slots][hi, lo][kRows][kAStride]
+  __shared__ int s_item[4 + 2 * kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int sng = p.sw0 != nullptr ? (p.sN + kDnShCols - 1) / kDnShCols : 0;
+  const int nshared = p.sgroups * sng;
+  const bool routed = (int)blockIdx.x >= nshared;
+  int g, e = 0, r0 = 0, nr, row_base;
+  if (routed) {
+    const int r = (int)blockIdx.x - nshared;
+    const int ng = (p.N + kDnCols - 1) / kDnCols;
+    const Pass ps = locate_pass(p, r / ng, s_item);
+    if (ps.e < 0) return;
+    g = r % ng;
+    e = ps.e;
+    r0 = ps.r0;
+    nr = min(kRows, ps.count - r0);
+    row_base = ps.offset;
+  } else {
+    g = (int)blockIdx.x % sng;
+    row_base = (int)blockIdx.x / sng * kShRows;
+    nr = min(kShRows, p.M - row_base);
+  }
+  const int N = routed ? p.N : p.sN, K = routed ? p.K : p.sK;
+  const int nh = K / 64;
+  // routed: 4 output tiles per wave; shared: 1 (its units are deeper, so narrower)
+  const int tpw = routed ? kDnTiles : 1;
+  const int tile0 = (g * kWaves + wave) * tpw;                     // first output tile of this wave
+  const int ntl = min(tpw, max(0, N / kWaveCols - tile0));         // its tiles inside N
+
+  const size_t wstride = (size_t)N * K;
+  const char* W = routed ? static_cast<const char*>(p.w0) + (size_t)e * wstride : static_cast<const char*>(p.sw0);
+  const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
+  const float* S = routed ? static_cast<const float*>(p.s0) + (size_t)e * sstride : static_cast<const float*>(p.ss0);
+  // the expert's [N, K] FP8 matrix as a buffer; per tile: tiled, one run of
+  // 2 KB chunk fragments (1 KB per half, this lane's 16 bytes at 16 * lane);
+  // row-major, the lane's row.  A tile past the wave's count fetches nothing.
+  const __amdgpu_buffer_rsrc_t wrs = rsrc(W, (uint32_t)wstride);
+  uint32_t wo[kDnTiles];
+#pragma unroll
+  for (int tt = 0; tt < kDnTiles; ++tt) {
+    const int t = tile0 + tt;
+    wo[tt] = tt < ntl ? (uint32_t)(TILED ? (size_t)t * K * kWaveCols + lane * 16 : (size_t)(t * kWaveCols + r16) * K + q * 16)
+                      : kNoFetch;
+  }
+  float sreg[kSL];
+  f32x4 rs[kDnTiles];
+  if constexpr (ROWS) {
+#pragma unroll
+    for (int tt = 0; tt < kDnTiles; ++tt) {
+      const int t = tt < ntl ? tile0 + tt : 0;
+      rs[tt] = *reinterpret_cast<const f32x4*>(S + t * kWaveCols + 4 * q);
+    }
+#pragma unroll
+    for (int i = 0; i < kSL; ++i) sreg[i] = 0.f;
+  } else {
+    // the wave's rows lie in one 128-row block; past the depth the scale is 0
+    const int kb = K / kFp8Block;
+    const float* sw = S + (size_t)(min(tile0, N / kWaveCols - 1) * kWaveCols / kFp8Block) * kb;
+#pragma unroll
+    for (int i = 0; i < kSL; ++i) sreg[i] = lane + 64 * i < kb ? sw[lane + 64 * i] : 0.f;
+#pragma unroll
+    for (int tt = 0; tt < kDnTiles; ++tt) rs[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // the pass's act rows (consecutive: sorted positions, or tokens) as a buffer
+  // of exactly nr rows; rows u*16 + prow, 4 floats at 4 * ppc of each half
+  // (rows past nr lie past the buffer: no fetch, zeros)
+  const char* A = routed ? static_cast<const char*>(p.x) : static_cast<const char*>(p.sx);
+  const __amdgpu_buffer_rsrc_t ars = rsrc(A + (size_t)(row_base + r0) * K * 4, (uint32_t)((size_t)nr * K * 4));
+  const int prow = tid >> 4, ppc = tid & 15;
+  uint32_t ao[kPieces];
+#pragma unroll
+  for (int u = 0; u < kPieces; ++u)
+    ao[u] = u * 16 + prow < nr ? (uint32_t)(((u * 16 + prow) * K + ppc * 4) * 4) : kNoFetch;
+  uint16_t* adst = as + prow * kAStride + ppc * 4;
+  constexpr int plane = kRows * kAStride;
+
+  u32x4 wb[kDnRing][kDnTiles];
+  u32x4 xr[kDnSets][kPieces];
+  f32x4 acc[kDnTiles][kRT];
+#pragma unroll
+  for (int tt = 0; tt < kDnTiles; ++tt)
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nrt = (nr + 15) >> 4;
+  const int nsteps = (nh + 2) / 3 * 3;  // whole rounds of 3
+
+  // halves past the depth: offsets past the buffers (zeros, nothing fetched)
+#define WIDE_LOAD_W(h, W)                                                                                   \
+  {                                                                                                         \
+    const uint32_t off = (h) < nh ? (TILED ? ((h) >> 1) * (kKC * kWaveCols) + ((h) & 1) * 1024 : (h) * 64)   \
+                                  : kNoFetch;                                                               \
+    _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt)(W)[tt] = bload(wrs, wo[tt] + off);           \
+  }
+#define WIDE_LOAD_A(h, R)                                                                                   \
+  {                                                                                                         \
+    const uint32_t ho = (h) < nh ? (uint32_t)(h) * 256 : kNoFetch;                                          \
+    _Pragma("unroll") for (int u = 0; u < kPieces; ++u)(R)[u] = bload(ars, ao[u] + ho);                    \
+  }
+  // act as bf16 hi + lo (the hi rounded to nearest even, the lo of the rest)
+#define WIDE_STORE_A(slot, R)                                                                               \
+  {                                                                                                         \
+    _Pragma("unroll") for (int u = 0; u < kPieces; ++u) {                                                  \
+      const u32x4 v = (R)[u];                                                                               \
+      uint16_t hi[4], lw[4];                                                                                \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                                      \
+        const float f = __uint_as_float(v[i]);                                                              \
+        hi[i] = bf16_rne_bits(f);                                                                           \
+        lw[i] = bf16_rne_bits(f - bf16_bits_to_f32(hi[i]));                                                \
+      }                                                                                                     \
+      uint16_t* d = adst + (slot) * (2 * plane) + u * 16 * kAStride;                                       \
+      *reinterpret_cast<uint2*>(d) = uint2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)}; \
+      *reinterpret_cast<uint2*>(d + plane) =                                                                \
+          uint2{lw[0] | ((uint32_t)lw[1] << 16), lw[2] | ((uint32_t)lw[3] << 16)};                          \
+    }                                                                                                       \
+  }
+
+  // prologue: act of halves 0, 1, 2 and weights of 0, 1 requested, act(0) staged
+  WIDE_LOAD_A(0, xr[0]);
+  WIDE_LOAD_W(0, wb[0]);
+  WIDE_LOAD_A(1, xr[1]);
+  WIDE_LOAD_W(1, wb[1]);
+  WIDE_LOAD_A(2, xr[2]);
+  WIDE_STORE_A(0, xr[0]);
+  __syncthreads();
+  // step h: request the weights of h + 2 and the act of h + 3 (set h % 3 held
+  // act(h), staged a step ago), multiply half h (ring slot h % 3, LDS slot
+  // h % 2), stage act(h + 1) (requested two steps ago), barrier.  Three steps
+  // written out, so every ring index is a constant and no step is conditional.
+#define WIDE_DN_STEP(JJ)                                                                                    \
+  {                                                                                                         \
+    const int h = h0 + (JJ);                                                                                \
+    WIDE_LOAD_W(h + 2, wb[((JJ) + 2) % 3]);                                                                 \
+    WIDE_LOAD_A(h + 3, xr[(JJ) % 3]);                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    dn_half<ROWS>(wb[(JJ) % 3], as + ((JJ) % 2 == (h0 & 1) ? 0 : 2 * plane), nrt, q, r16, ntl,               \
+                  block_scale(sreg, h >> 1), rs, acc);                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+    WIDE_STORE_A(((JJ) % 2 == (h0 & 1)) ? 1 : 0, xr[((JJ) + 1) % 3]);                                      \
+    __syncthreads();                                                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                                      \
+  }
+  for (int h0 = 0; h0 < nsteps; h0 += 3) {
+    WIDE_DN_STEP(0)
+    WIDE_DN_STEP(1)
+    WIDE_DN_STEP(2)
+  }
+#undef WIDE_DN_STEP
+#undef WIDE_LOAD_W
+#undef WIDE_LOAD_A
+#undef WIDE_STORE_A
+
+  float* OUT = routed ? p.out : p.sout;
+#pragma unroll
+  for (int tt = 0; tt < kDnTiles; ++tt) {
+    if (tt < ntl) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        const int r = rt * 16 + r16;
+        if (rt < nrt && r < nr) {
+          const f32x4 v = acc[tt][rt];
+          *reinterpret_cast<float4*>(OUT + (size_t)(row_base + r0 + r) * N + (tile0 + tt) * kWaveCols + 4 * q) =
+              float4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+  }
+}
+
+// the most kRows-row passes n slots can need: sum over experts of
+// ceil(count / kRows) <= (n + active * (kRows - 1)) / kRows
+inline int64_t max_items(const GroupedArgs& a) {
+  const int64_t n = (int64_t)a.M * a.top_k;
+  return (n + (int64_t)a.cap * (kRows - 1)) / kRows;
+}
+
+template <bool ROWS, bool TILED>
+hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
+  GroupedArgs b = a;
+  const int64_t items = max_items(a);
+  b.sgroups = a.sw0 != nullptr ? (a.M + kShRows - 1) / kShRows : 0;
+  const long long blocks =
+      (long long)b.sgroups * (a.sw0 != nullptr ? a.sN / kGuCols : 0) + (long long)items * (a.N / kGuCols);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
+  b.items = (int)items;
+  hipLaunchKernelGGL((wide_gate_up_kernel<ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kGuLds, s, b);
+  return hipGetLastError();
+}
+
+template <bool ROWS, bool TILED>
+hipError_t launch_dn(const GroupedArgs& a, hipStream_t s) {
+  GroupedArgs b = a;
+  const int64_t items = max_items(a);
+  b.sgroups = a.sw0 != nullptr ? (a.M + kShRows - 1) / kShRows : 0;
+  const long long blocks = (long long)b.sgroups * (a.sw0 != nullptr ? (a.sN + kDnShCols - 1) / kDnShCols : 0) +
+                           (long long)items * ((a.N + kDnCols - 1) / kDnCols);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
+  b.items = (int)items;
+  hipLaunchKernelGGL((wide_down_kernel<ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kDnLds, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace wide_detail
+
+bool grouped_wide(int fmt, const GroupedArgs& a, bool gate_up) {
+  // FP8 only, tables from the align launch (not the fused align), experts that
+  // can hold more rows than one 16-row pass (M > 16) and hold 4 or more on
+  // average (n >= 4E: a sparser routing leaves most passes a few rows, which
+  // the 16-row kernels stream as fast), depth within the scale registers and
+  // a whole number of gate+up rounds (4 steps: 512 deep; down pads its depth
+  // to rounds of 3 halves itself)
+  // (and every buffer the kernels address under 2^31 bytes)
+  const int round = gate_up ? 4 * mma::kKC : mma::kKC;
+  constexpr int64_t kLim = (int64_t)1 << 31;
+  auto ok = [&](int N, int K) {
+    return K % round == 0 && K / kFp8Block <= wide_detail::kMaxScaleBlocks && (int64_t)N * K < kLim &&
+           (!gate_up || (int64_t)a.M * K * 2 < kLim);
+  };
+  return fmt == kFmtFP8 && a.ids == nullptr && a.M > 16 && (int64_t)a.M * a.top_k >= 4 * (int64_t)a.E &&
+         ok(a.N, a.K) && (a.sw0 == nullptr || ok(a.sN, a.sK));
+}
+
+hipError_t launch_wide_gate_up(const GroupedArgs& a, bool tiled, hipStream_t s) {
+  using namespace wide_detail;
+  if (a.scale_rows) return tiled ? launch_gu<true, true>(a, s) : launch_gu<true, false>(a, s);
+  return tiled ? launch_gu<false, true>(a, s) : launch_gu<false, false>(a, s);
+}
+
+hipError_t launch_wide_down(const GroupedArgs& a, bool tiled, hipStream_t s) {
+  using namespace wide_detail;
+  if (a.scale_rows) return tiled ? launch_dn<true, true>(a, s) : launch_dn<true, false>(a, s);
+  return tiled ? launch_dn<false, true>(a, s) : launch_dn<false, false>(a, s);
+}
+
+}  // namespace moe
