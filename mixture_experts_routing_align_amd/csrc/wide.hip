@@ -1,8 +1,8 @@
-// Wide-pass grouped projections for gfx950: every row an expert holds, up to
-// 64 at a time, in one workgroup per (expert, column group), so an expert's
-// weights are streamed once per column group instead of once per 16-row pass.
-// For layers whose experts hold many rows (verify and prefill widths); FP8
-// weights (block or row scales), tiled or row-major.
+// Wide-pass grouped projections for gfx950: every row an expert holds, 32 at
+// a time, in one workgroup per (expert pass, column group), so an expert's
+// weights are streamed once per column group per 32 rows instead of once per
+// 16-row pass.  For layers whose experts hold many rows (verify and prefill
+// widths); FP8 weights (block or row scales), tiled or row-major.
 //
 // What is computed is the grouped projection of the pass kernels
 // (grouped_impl.h; metrale fp8_moe_grouped.rs: the gate+up and down launchers;
@@ -15,15 +15,17 @@
 //            act, from zero; acc = acc + scale * t, both rounded, h ascending
 // so a row has the same bits whichever kernel (or layer path) runs it.
 //
-// gfx950 design.  4 waves.  Each wave streams its own weight rows (16 gate and
-// 16 up columns; or 4 x 16 rows of the down output) straight from HBM into a
-// 3-step register ring, 16-byte loads, no LDS.  The expert's activation rows
-// (bf16 x, or act split into bf16 hi + lo) are shared by the 4 waves through
-// two LDS slots: each thread requests its 4 pieces of the rows two steps ahead
-// into registers and writes them to LDS one step ahead, with one barrier per
-// step, so neither the weights nor the rows wait a round trip per step.
-// Rows past the expert's count repeat its last row (valid addresses) and only
-// reach outputs that are never stored.
+// gfx950 design.  4 waves, 3 workgroups per compute unit (at most 168
+// registers a lane, none spilled).  Each wave streams its own weight rows (16
+// gate and 16 up columns; or 4 x 16 rows of the down output) from HBM into a
+// 4-step register ring, 16-byte loads, no LDS.  The rows' activations (bf16
+// x, or act split into bf16 hi + lo) are shared by the 4 waves through two
+// LDS slots: each thread requests its pieces of the rows two steps ahead into
+// registers and writes them to LDS one step ahead, with one barrier per step.
+// Rows and tiles past an expert's count or the output fetch nothing (buffer
+// loads past the buffer's end) and only reach outputs that are never stored.
+// The shared expert's units are narrower than the routed ones (its depth S
+// makes them longer), so that no unit holds the launch up.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -315,14 +317,15 @@ __global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p
 
 constexpr int kAStride = 64 + kPad;                          // staged act row, bf16 elements (one half)
 constexpr size_t kDnLds = (size_t)2 * 2 * kRows * kAStride * 2;  // two slots of (hi, lo)
-constexpr int kDnRing = 3;                                   // weight halves in the register ring (2 ahead)
-constexpr int kDnSets = 3;                                   // act register sets (requested 3 halves ahead)
+constexpr int kDnRing = 4;                                   // weight halves in the register ring (3 ahead)
+constexpr int kDnSets = 2;                                   // act register sets (requested 2 halves ahead)
 
 // one 64-deep half: the wave's output tiles from the ring, act rows (hi, lo)
-// from LDS slot ab
+// from LDS slot ab; ROWS: the row scales of the wave's tiles from LDS (rsl,
+// 16 per tile: held in registers they would not fit)
 template <bool ROWS>
 __device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16_t* __restrict__ ab, int nrt, int q,
-                                        int r16, int ntl, float sc, const f32x4 (&rs)[kDnTiles],
+                                        int r16, int ntl, float sc, const float* __restrict__ rsl,
                                         f32x4 (&acc)[kDnTiles][kRT]) {
   bf16x8 a[kDnTiles][2];
 #pragma unroll
@@ -349,8 +352,10 @@ __device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16
           for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int x = 0; x < 2; ++x) t = mfma(a[tt][s], b[x][s], t);
+          f32x4 rsc = {sc, sc, sc, sc};
+          if constexpr (ROWS) rsc = *reinterpret_cast<const f32x4*>(rsl + tt * 16 + 4 * q);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tt][rt][i] = add_rn(acc[tt][rt][i], mul_rn(ROWS ? rs[tt][i] : sc, t[i]));
+          for (int i = 0; i < 4; ++i) acc[tt][rt][i] = add_rn(acc[tt][rt][i], mul_rn(rsc[i], t[i]));
         }
       }
     }
@@ -360,8 +365,8 @@ __device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16
 // Grid (1-D): the shared expert's (32-token pass, 64-row group of H) units,
 // then the routed (pass item, 256-row group) units, the group fastest.  A
 // routed wave owns output tiles 4 (4g + w) .. +3, a shared wave tile 4g + w
-// (tiles past N: none of its work).  The halves run in rounds of 3 (the ring
-// lengths); a round past the depth multiplies zeros (its loads lie past their
+// (tiles past N: none of its work).  The halves run in rounds of 4 (the ring
+// length); a half past the depth multiplies zeros (its loads lie past their
 // buffers and fetch nothing; scale 0), which leaves every sum as it is.
 template <bool ROWS, bool TILED>
 __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
@@ -414,13 +419,12 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
                       : kNoFetch;
   }
   float sreg[kSL];
-  f32x4 rs[kDnTiles];
+  // ROWS: lane l of each wave puts the scale of row l % 16 of its tile l / 16 in LDS
+  __shared__ float s_rs[ROWS ? kWaves * kDnTiles * kWaveCols : 1];
+  float* const rsl = s_rs + (ROWS ? wave * kDnTiles * kWaveCols : 0);
   if constexpr (ROWS) {
-#pragma unroll
-    for (int tt = 0; tt < kDnTiles; ++tt) {
-      const int t = tt < ntl ? tile0 + tt : 0;
-      rs[tt] = *reinterpret_cast<const f32x4*>(S + t * kWaveCols + 4 * q);
-    }
+    const int tt = lane >> 4;
+    rsl[lane] = tt < ntl ? S[(tile0 + tt) * kWaveCols + (lane & 15)] : 0.f;
 #pragma unroll
     for (int i = 0; i < kSL; ++i) sreg[i] = 0.f;
   } else {
@@ -429,8 +433,6 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
     const float* sw = S + (size_t)(min(tile0, N / kWaveCols - 1) * kWaveCols / kFp8Block) * kb;
 #pragma unroll
     for (int i = 0; i < kSL; ++i) sreg[i] = lane + 64 * i < kb ? sw[lane + 64 * i] : 0.f;
-#pragma unroll
-    for (int tt = 0; tt < kDnTiles; ++tt) rs[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // the pass's act rows (consecutive: sorted positions, or tokens) as a buffer
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nrt = (nr + 15) >> 4;
-  const int nsteps = (nh + 2) / 3 * 3;  // whole rounds of 3
+  const int nsteps = (nh + 3) / 4 * 4;  // whole rounds of 4
 
   // halves past the depth: offsets past the buffers (zeros, nothing fetched)
 #define WIDE_LOAD_W(h, W)                                                                                   \
@@ -486,35 +488,36 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
     }                                                                                                       \
   }
 
-  // prologue: act of halves 0, 1, 2 and weights of 0, 1 requested, act(0) staged
+  // prologue: act of halves 0, 1 and weights of 0, 1, 2 requested, act(0) staged
   WIDE_LOAD_A(0, xr[0]);
   WIDE_LOAD_W(0, wb[0]);
   WIDE_LOAD_A(1, xr[1]);
   WIDE_LOAD_W(1, wb[1]);
-  WIDE_LOAD_A(2, xr[2]);
+  WIDE_LOAD_W(2, wb[2]);
   WIDE_STORE_A(0, xr[0]);
   __syncthreads();
-  // step h: request the weights of h + 2 and the act of h + 3 (set h % 3 held
-  // act(h), staged a step ago), multiply half h (ring slot h % 3, LDS slot
-  // h % 2), stage act(h + 1) (requested two steps ago), barrier.  Three steps
+  // step h: request the weights of h + 3 and the act of h + 2 (set h % 2 held
+  // act(h), staged a step ago), multiply half h (ring slot h % 4, LDS slot
+  // h % 2), stage act(h + 1) (requested a step ago), barrier.  Four steps
   // written out, so every ring index is a constant and no step is conditional.
 #define WIDE_DN_STEP(JJ)                                                                                    \
   {                                                                                                         \
     const int h = h0 + (JJ);                                                                                \
-    WIDE_LOAD_W(h + 2, wb[((JJ) + 2) % 3]);                                                                 \
-    WIDE_LOAD_A(h + 3, xr[(JJ) % 3]);                                                                       \
+    WIDE_LOAD_W(h + 3, wb[((JJ) + 3) % 4]);                                                                 \
+    WIDE_LOAD_A(h + 2, xr[(JJ) % 2]);                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
-    dn_half<ROWS>(wb[(JJ) % 3], as + ((JJ) % 2 == (h0 & 1) ? 0 : 2 * plane), nrt, q, r16, ntl,               \
-                  block_scale(sreg, h >> 1), rs, acc);                                                      \
+    dn_half<ROWS>(wb[(JJ) % 4], as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, block_scale(sreg, h >> 1), rsl, \
+                  acc);                                                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
-    WIDE_STORE_A(((JJ) % 2 == (h0 & 1)) ? 1 : 0, xr[((JJ) + 1) % 3]);                                      \
+    WIDE_STORE_A(((JJ) + 1) % 2, xr[((JJ) + 1) % 2]);                                                       \
     __syncthreads();                                                                                        \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
   }
-  for (int h0 = 0; h0 < nsteps; h0 += 3) {
+  for (int h0 = 0; h0 < nsteps; h0 += 4) {
     WIDE_DN_STEP(0)
     WIDE_DN_STEP(1)
     WIDE_DN_STEP(2)
+    WIDE_DN_STEP(3)
   }
 #undef WIDE_DN_STEP
 #undef WIDE_LOAD_W
