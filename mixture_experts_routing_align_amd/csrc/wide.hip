@@ -15,17 +15,19 @@
 //            act, from zero; acc = acc + scale * t, both rounded, h ascending
 // so a row has the same bits whichever kernel (or layer path) runs it.
 //
-// gfx950 design.  4 waves, 3 workgroups per compute unit (at most 168
-// registers a lane, none spilled).  Each wave streams its own weight rows (16
-// gate and 16 up columns; or 4 x 16 rows of the down output) from HBM into a
-// 4-step register ring, 16-byte loads, no LDS.  The rows' activations (bf16
-// x, or act split into bf16 hi + lo) are shared by the 4 waves through two
-// LDS slots: each thread requests its pieces of the rows two steps ahead into
-// registers and writes them to LDS one step ahead, with one barrier per step.
-// Rows and tiles past an expert's count or the output fetch nothing (buffer
-// loads past the buffer's end) and only reach outputs that are never stored.
-// The shared expert's units are narrower than the routed ones (its depth S
-// makes them longer), so that no unit holds the launch up.
+// gfx950 design.  4 waves.  Each wave streams its own weight rows (16 gate
+// and 16 up columns; or 4 x 16 rows of the down output) from HBM into a
+// register ring (gate+up: 3 steps, 4 workgroups per compute unit at 128
+// registers a lane; down: 4 steps, 3 workgroups per compute unit), 16-byte
+// buffer loads, no LDS.  The rows' activations (bf16 x, or act split into
+// bf16 hi + lo) are shared by the 4 waves through two LDS slots: each thread
+// requests its pieces of the rows two steps ahead into registers and writes
+// them to LDS one step ahead, with one barrier per step.  Rows and tiles past
+// an expert's count or the output, and the steps that pad the depth to whole
+// loop rounds, fetch nothing (buffer loads past the buffer's end return zeros)
+// and change no stored output.  The shared expert's units are narrower than
+// the routed ones (its depth S makes them longer), so that no unit holds the
+// launch up.  No register spills.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -48,7 +50,7 @@ constexpr int kGuCols = kWaves * kWaveCols;              // gate+up columns per 
 constexpr int kDnTiles = 4;                              // down: 16-row output tiles per wave
 constexpr int kDnCols = kWaves * kDnTiles * kWaveCols;   // down output rows (of H) per routed workgroup
 constexpr int kDnShCols = kWaves * kWaveCols;            // per shared-expert workgroup (one tile per wave)
-constexpr int kNbuf = 4;                                 // weight steps in the register ring (3 ahead)
+constexpr int kGuRing = 3;                               // gate+up: weight steps in the register ring (2 ahead)
 constexpr int kMaxScaleBlocks = 128;                     // FP8 depth limit: 128 scale blocks
 constexpr int kSL = kMaxScaleBlocks / 64;
 constexpr int kXStride = kKC + kPad;                     // staged x row, bf16 elements (one chunk)
@@ -118,34 +120,32 @@ __device__ __forceinline__ float block_scale(const float (&sr)[kSL], int c) {
 
 // ------------------------------------------------------------------ gate+up --
 
-// one 128-deep chunk: gate and up from the ring, x rows from LDS slot xb
+// one 128-deep chunk: gate and up from the ring, x rows from LDS slot xb.
+// Each MFMA step reads its x fragment once for both matrices and converts the
+// codes where they are used (registers for 4 workgroups per compute unit);
+// every sum still runs its 4 steps in order.
 template <bool ROWS>
 __device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t* __restrict__ xb, int nrt, int q,
                                          int r16, float sg, float su, const f32x4 (&rs)[2], f32x4 (&acc)[2][kRT]) {
-  bf16x8 a[2][4];
-#pragma unroll
-  for (int st = 0; st < 2; ++st)
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const uint4 v = w[st][s >> 1];
-      a[st][s] = (s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y);
-    }
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     if (rt < nrt) {
-      bf16x8 b[4];
+      f32x4 t[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        b[s] = as_bf16x8(*reinterpret_cast<const uint4*>(xb + (rt * 16 + r16) * kXStride + k_of_step<true>(s, q)));
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 b =
+            as_bf16x8(*reinterpret_cast<const uint4*>(xb + (rt * 16 + r16) * kXStride + k_of_step<true>(s, q)));
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 2; ++st) {
+          const uint4 v = w[st][s >> 1];
+          t[st] = mfma((s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y), b, t[st]);
+        }
+      }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) t = mfma(a[st][s], b[s], t);
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          acc[st][rt][i] = fmaf(ROWS ? rs[st][i] : (st == 0 ? sg : su), t[i], acc[st][rt][i]);
-      }
+          acc[st][rt][i] = fmaf(ROWS ? rs[st][i] : (st == 0 ? sg : su), t[st][i], acc[st][rt][i]);
     }
   }
 }
@@ -155,7 +155,7 @@ __device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t*
 // so the routing's real passes come first and the items past them (the grid
 // covers the most passes any routing of n slots can need) come last and exit.
 template <bool ROWS, bool TILED>
-__global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p) {
+__global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [2][kRows][kXStride]
   __shared__ int s_src[kRows];
   __shared__ int s_item[4 + 2 * kWaves];
@@ -193,11 +193,12 @@ __global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p
   const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
   const float* S0 = routed ? static_cast<const float*>(p.s0) + (size_t)e * sstride : static_cast<const float*>(p.ss0);
   const float* S1 = routed ? static_cast<const float*>(p.s1) + (size_t)e * sstride : static_cast<const float*>(p.ss1);
-  // tiled: the wave's 16-column tile is one run of 2 KB chunk fragments, this
-  // lane's 16 bytes at 16 * lane of each 1 KB half; row-major: the lane's row
-  const size_t lo = TILED ? (size_t)(wcol / kWaveCols) * K * kWaveCols + lane * 16 : (size_t)(wcol + r16) * K + q * 16;
-  const char* lp0 = W0 + lo;
-  const char* lp1 = W1 + lo;
+  // the expert's gate and up [N, K] FP8 matrices as buffers; tiled: the
+  // wave's 16-column tile is one run of 2 KB chunk fragments, this lane's 16
+  // bytes at 16 * lane of each 1 KB half; row-major: the lane's row
+  const __amdgpu_buffer_rsrc_t wrs0 = rsrc(W0, (uint32_t)wstride), wrs1 = rsrc(W1, (uint32_t)wstride);
+  const uint32_t lo = (uint32_t)(TILED ? (size_t)(wcol / kWaveCols) * K * kWaveCols + lane * 16
+                                       : (size_t)(wcol + r16) * K + q * 16);
 
   // the row sources: the token of each row
   if (tid < nr) s_src[tid] = routed ? p.sorted_token_ids[row_base + r0 + tid] / p.top_k : row_base + tid;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p
     xo[u] = u * 16 + prow < nr ? (uint32_t)(((size_t)s_src[u * 16 + prow] * K + ppc * 8) * 2) : kNoFetch;
   uint16_t* xdst = xs + prow * kXStride + ppc * 8;
 
-  uint4 wb[kNbuf][2][2];
+  uint4 wb[kGuRing][2][2];
   u32x4 xr[2][kPieces];
   f32x4 acc[2][kRT];
 #pragma unroll
@@ -243,17 +244,20 @@ __global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p
     for (int rt = 0; rt < kRT; ++rt) acc[st][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nrt = (nr + 15) >> 4;
 
+  // chunks past the depth (the last round's padding) fetch nothing: zeros
 #define WIDE_LOAD_W(c, W)                                                                             \
   {                                                                                                   \
     _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                  \
-      const size_t off = TILED ? (size_t)(c) * (kKC * kWaveCols) + j * 1024 : (size_t)(c) * kKC + j * 64; \
-      (W)[0][j] = *reinterpret_cast<const uint4*>(lp0 + off);                                        \
-      (W)[1][j] = *reinterpret_cast<const uint4*>(lp1 + off);                                        \
+      const uint32_t off =                                                                            \
+          (c) < nch ? lo + (TILED ? (c) * (kKC * kWaveCols) + j * 1024 : (c) * kKC + j * 64) : kNoFetch; \
+      (W)[0][j] = __builtin_bit_cast(uint4, bload(wrs0, off));                                       \
+      (W)[1][j] = __builtin_bit_cast(uint4, bload(wrs1, off));                                       \
     }                                                                                                 \
   }
 #define WIDE_LOAD_X(c, R)                                                                                         \
   {                                                                                                               \
-    _Pragma("unroll") for (int u = 0; u < kPieces; ++u)(R)[u] = bload(xrs, xo[u] + (uint32_t)(c) * (kKC * 2));  \
+    const uint32_t co = (c) < nch ? (uint32_t)(c) * (kKC * 2) : kNoFetch;                                        \
+    _Pragma("unroll") for (int u = 0; u < kPieces; ++u)(R)[u] = bload(xrs, xo[u] + co);                          \
   }
 #define WIDE_STORE_X(slot, R)                                                                                     \
   {                                                                                                               \
@@ -261,37 +265,40 @@ __global__ __launch_bounds__(kThreads, 3) void wide_gate_up_kernel(GroupedArgs p
         xdst + (slot) * (kRows * kXStride) + u * 16 * kXStride) = (R)[u];                                        \
   }
 
-  // prologue: x of chunks 0, 1 and weights of chunks 0, 1, 2 requested, x(0) staged
+  // prologue: x and weights of chunks 0 and 1 requested, x(0) staged
   WIDE_LOAD_X(0, xr[0]);
   WIDE_LOAD_W(0, wb[0]);
   WIDE_LOAD_X(1, xr[1]);
   WIDE_LOAD_W(1, wb[1]);
-  WIDE_LOAD_W(2, wb[2]);
   WIDE_STORE_X(0, xr[0]);
   __syncthreads();
-  // step c: request x(c + 2) and the weights of c + 3 (wrapped past the end:
-  // valid memory, never used), multiply chunk c (ring slot c % 4, LDS slot
-  // c % 2), stage x(c + 1), barrier.  Four steps written out, so every ring
-  // index is a constant and no step is conditional (a load under a branch
-  // costs a full wait for every load in flight); nch is a multiple of 4.
+  // step c: request x and weights of chunk c + 2, multiply chunk c (ring slot
+  // c % 3, LDS slot c % 2), stage x(c + 1), barrier.  Six steps written out,
+  // so every ring index is a constant and no step is conditional (a load under
+  // a branch costs a full wait for every load in flight); the depth is padded
+  // to whole rounds of 6 with chunks that fetch nothing (zeros, block scale
+  // 0), which leave every sum as it is.
+  const int nsteps = (nch + 5) / 6 * 6;
 #define WIDE_GU_STEP(JJ)                                                                                   \
   {                                                                                                        \
     const int c = c0 + (JJ);                                                                               \
-    WIDE_LOAD_X((c + 2) % nch, xr[(JJ) % 2]);                                                              \
-    WIDE_LOAD_W((c + 3) % nch, wb[((JJ) + 3) % 4]);                                                        \
+    WIDE_LOAD_X(c + 2, xr[(JJ) % 2]);                                                                      \
+    WIDE_LOAD_W(c + 2, wb[((JJ) + 2) % 3]);                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
-    gu_chunk<ROWS>(wb[(JJ) % 4], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, block_scale(sreg[0], c), \
+    gu_chunk<ROWS>(wb[(JJ) % 3], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, block_scale(sreg[0], c), \
                    block_scale(sreg[1], c), rs, acc);                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
     WIDE_STORE_X(((JJ) + 1) % 2, xr[((JJ) + 1) % 2]);                                                      \
     __syncthreads();                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
   }
-  for (int c0 = 0; c0 < nch; c0 += 4) {
+  for (int c0 = 0; c0 < nsteps; c0 += 6) {
     WIDE_GU_STEP(0)
     WIDE_GU_STEP(1)
     WIDE_GU_STEP(2)
     WIDE_GU_STEP(3)
+    WIDE_GU_STEP(4)
+    WIDE_GU_STEP(5)
   }
 #undef WIDE_GU_STEP
 #undef WIDE_LOAD_W
@@ -583,13 +590,11 @@ bool grouped_wide(int fmt, const GroupedArgs& a, bool gate_up) {
   // can hold more rows than one 16-row pass (M > 16) and hold 4 or more on
   // average (n >= 4E: a sparser routing leaves most passes a few rows, which
   // the 16-row kernels stream as fast), depth within the scale registers and
-  // a whole number of gate+up rounds (4 steps: 512 deep; down pads its depth
-  // to rounds of 3 halves itself)
+  // (both kernels pad the depth to whole rounds themselves)
   // (and every buffer the kernels address under 2^31 bytes)
-  const int round = gate_up ? 4 * mma::kKC : mma::kKC;
   constexpr int64_t kLim = (int64_t)1 << 31;
   auto ok = [&](int N, int K) {
-    return K % round == 0 && K / kFp8Block <= wide_detail::kMaxScaleBlocks && (int64_t)N * K < kLim &&
+    return K % mma::kKC == 0 && K / kFp8Block <= wide_detail::kMaxScaleBlocks && (int64_t)N * K < kLim &&
            (!gate_up || (int64_t)a.M * K * 2 < kLim);
   };
   return fmt == kFmtFP8 && a.ids == nullptr && a.M > 16 && (int64_t)a.M * a.top_k >= 4 * (int64_t)a.E &&

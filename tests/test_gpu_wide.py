@@ -5,7 +5,7 @@ wide run's), on shapes that exercise the cases of the wide kernels: experts
 with several 32-row passes, every slot on a few experts, out-of-range ids, a
 shared expert whose tokens end mid-pass and whose depth ends mid-round,
 per-row scales, an output width that ends inside a 256-row group, and a
-gate+up that stays on the pass kernel while down runs wide."""
+depth of 3 chunks that the gate+up pads to a round of 6."""
 
 import numpy as np
 import pytest
@@ -33,8 +33,8 @@ CONFIGS = {
     # shared depth 384 (6 halves: down pads to rounds of 4)
     "shared_rows": workloads.MoeConfig("wide_shared_rows", 40, 512, 8, 2, 128, 384, 16, "fp8_rows", "softmax",
                                        seed=62),
-    # hidden 384: gate+up (depth 384) stays on the pass kernel, down runs wide
-    # with its second 256-row group half full
+    # hidden 384: gate+up depth of 3 chunks (padded to a round of 6), down's
+    # second 256-row group half full
     "mixed": workloads.MoeConfig("wide_mixed", 48, 384, 4, 2, 256, 0, 16, "fp8", "softmax", seed=63),
 }
 
