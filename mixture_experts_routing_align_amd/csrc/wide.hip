@@ -43,9 +43,10 @@ using namespace mma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 32;                                // rows per routed pass
-constexpr int kShRows = 32;                              // rows (tokens) per shared-expert pass
-constexpr int kRT = kRows / 16;                          // 16-row tiles per pass
+// rows per pass: routed passes of an expert, shared-expert passes of tokens
+constexpr int kGuRows = 32, kGuShRows = 32;              // gate+up
+constexpr int kDnRows = 32, kDnShRows = 32;              // down
+static_assert(kGuShRows <= kGuRows && kDnShRows <= kDnRows, "a shared pass fits the routed pass registers");
 constexpr int kGuCols = kWaves * kWaveCols;              // gate+up columns per workgroup
 constexpr int kDnTiles = 4;                              // down: 16-row output tiles per wave
 constexpr int kDnCols = kWaves * kDnTiles * kWaveCols;   // down output rows (of H) per routed workgroup
@@ -54,9 +55,13 @@ constexpr int kGuRing = 3;                               // gate+up: weight step
 constexpr int kMaxScaleBlocks = 128;                     // FP8 depth limit: 128 scale blocks
 constexpr int kSL = kMaxScaleBlocks / 64;
 constexpr int kXStride = kKC + kPad;                     // staged x row, bf16 elements (one chunk)
-constexpr size_t kGuLds = (size_t)2 * kRows * kXStride * 2;      // two slots
-constexpr int kPieces = kRows * 16 / kThreads;           // 16-byte row pieces per thread per step
-static_assert(kPieces * kThreads == kRows * 16, "each thread stages kPieces pieces: rows u*16 + tid/16");
+constexpr size_t kGuLds = (size_t)2 * kGuRows * kXStride * 2;    // two slots
+// 16-byte row pieces each thread stages per step (rows u*16 + tid/16)
+template <int RP>
+constexpr int pieces_of() {
+  static_assert(RP * 16 % kThreads == 0, "whole pieces per thread");
+  return RP * 16 / kThreads;
+}
 // 16 bytes as a native vector: a register copy, where the uint4 struct would
 // be copied through private memory
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -74,13 +79,14 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 
 // Which pass routed item j is: the active experts in ascending order, each
-// contributing ceil(count / kRows) passes.  Every thread takes a run of active
+// contributing ceil(count / RP) passes.  Every thread takes a run of active
 // indices, a block scan of their pass counts places the runs, and the thread
 // whose run holds pass j publishes (expert, first row, count, offset).
 // e = -1: the routing has fewer passes.  Contains barriers.
 struct Pass {
   int e, r0, count, offset;
 };
+template <int RP>
 __device__ __forceinline__ Pass locate_pass(const GroupedArgs& p, int j, int* s_item) {
   constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
   const int tid = threadIdx.x;
@@ -92,17 +98,17 @@ __device__ __forceinline__ Pass locate_pass(const GroupedArgs& p, int j, int* s_
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     cn[i] = ex[i] >= 0 ? p.expert_counts[ex[i]] : 0;
-    np += (cn[i] + kRows - 1) / kRows;
+    np += (cn[i] + RP - 1) / RP;
   }
   if (tid == 0) s_item[0] = -1;
   int base, unused_ex, total, unused_tot;
   align_dev::block_scan2<kWaves>(np, 0, s_item + 4, s_item + 4 + kWaves, base, unused_ex, total, unused_tot);
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int npi = (cn[i] + kRows - 1) / kRows;
+    const int npi = (cn[i] + RP - 1) / RP;
     if (j >= base && j < base + npi) {
       s_item[0] = ex[i];
-      s_item[1] = (j - base) * kRows;
+      s_item[1] = (j - base) * RP;
       s_item[2] = cn[i];
       s_item[3] = p.expert_offsets[ex[i]];
     }
@@ -126,9 +132,10 @@ __device__ __forceinline__ float block_scale(const float (&sr)[kSL], int c) {
 // every sum still runs its 4 steps in order.
 template <bool ROWS>
 __device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t* __restrict__ xb, int nrt, int q,
-                                         int r16, float sg, float su, const f32x4 (&rs)[2], f32x4 (&acc)[2][kRT]) {
+                                         int r16, float sg, float su, const f32x4 (&rs)[2],
+                                         f32x4 (&acc)[2][kGuRows / 16]) {
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
+  for (int rt = 0; rt < kGuRows / 16; ++rt) {
     if (rt < nrt) {
       f32x4 t[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -156,6 +163,7 @@ __device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t*
 // covers the most passes any routing of n slots can need) come last and exit.
 template <bool ROWS, bool TILED>
 __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p) {
+  constexpr int kRows = kGuRows, kShRows = kGuShRows, kRT = kRows / 16, kPieces = pieces_of<kRows>();
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [2][kRows][kXStride]
   __shared__ int s_src[kRows];
   __shared__ int s_item[4 + 2 * kWaves];
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   if (routed) {
     const int r = (int)blockIdx.x - nshared;
     const int ng = p.N / kGuCols;
-    const Pass ps = locate_pass(p, r / ng, s_item);
+    const Pass ps = locate_pass<kRows>(p, r / ng, s_item);
     if (ps.e < 0) return;
     g = r % ng;
     e = ps.e;
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
 // --------------------------------------------------------------------- down --
 
 constexpr int kAStride = 64 + kPad;                          // staged act row, bf16 elements (one half)
-constexpr size_t kDnLds = (size_t)2 * 2 * kRows * kAStride * 2;  // two slots of (hi, lo)
+constexpr size_t kDnLds = (size_t)2 * 2 * kDnRows * kAStride * 2;  // two slots of (hi, lo)
 constexpr int kDnRing = 4;                                   // weight halves in the register ring (3 ahead)
 constexpr int kDnSets = 2;                                   // act register sets (requested 2 halves ahead)
 
@@ -333,16 +341,16 @@ constexpr int kDnSets = 2;                                   // act register set
 template <bool ROWS>
 __device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16_t* __restrict__ ab, int nrt, int q,
                                         int r16, int ntl, float sc, const float* __restrict__ rsl,
-                                        f32x4 (&acc)[kDnTiles][kRT]) {
+                                        f32x4 (&acc)[kDnTiles][kDnRows / 16]) {
   bf16x8 a[kDnTiles][2];
 #pragma unroll
   for (int tt = 0; tt < kDnTiles; ++tt) {
     a[tt][0] = fp8x8_to_bf16(w[tt].x, w[tt].y);
     a[tt][1] = fp8x8_to_bf16(w[tt].z, w[tt].w);
   }
-  constexpr int plane = kRows * kAStride;
+  constexpr int plane = kDnRows * kAStride;
 #pragma unroll
-  for (int rt = 0; rt < kRT; ++rt) {
+  for (int rt = 0; rt < kDnRows / 16; ++rt) {
     if (rt < nrt) {
       bf16x8 b[2][2];
 #pragma unroll
@@ -377,6 +385,7 @@ __device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16
 // buffers and fetch nothing; scale 0), which leaves every sum as it is.
 template <bool ROWS, bool TILED>
 __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
+  constexpr int kRows = kDnRows, kShRows = kDnShRows, kRT = kRows / 16, kPieces = pieces_of<kRows>();
   extern __shared__ __attribute__((aligned(16))) uint16_t as[];  // [2 slots][hi, lo][kRows][kAStride]
   __shared__ int s_item[4 + 2 * kWaves];
 
@@ -391,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   if (routed) {
     const int r = (int)blockIdx.x - nshared;
     const int ng = (p.N + kDnCols - 1) / kDnCols;
-    const Pass ps = locate_pass(p, r / ng, s_item);
+    const Pass ps = locate_pass<kRows>(p, r / ng, s_item);
     if (ps.e < 0) return;
     g = r % ng;
     e = ps.e;
@@ -548,18 +557,18 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   }
 }
 
-// the most kRows-row passes n slots can need: sum over experts of
-// ceil(count / kRows) <= (n + active * (kRows - 1)) / kRows
-inline int64_t max_items(const GroupedArgs& a) {
+// the most RP-row passes n slots can need: sum over experts of
+// ceil(count / RP) <= (n + active * (RP - 1)) / RP
+inline int64_t max_items(const GroupedArgs& a, int RP) {
   const int64_t n = (int64_t)a.M * a.top_k;
-  return (n + (int64_t)a.cap * (kRows - 1)) / kRows;
+  return (n + (int64_t)a.cap * (RP - 1)) / RP;
 }
 
 template <bool ROWS, bool TILED>
 hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
   GroupedArgs b = a;
-  const int64_t items = max_items(a);
-  b.sgroups = a.sw0 != nullptr ? (a.M + kShRows - 1) / kShRows : 0;
+  const int64_t items = max_items(a, kGuRows);
+  b.sgroups = a.sw0 != nullptr ? (a.M + kGuShRows - 1) / kGuShRows : 0;
   const long long blocks =
       (long long)b.sgroups * (a.sw0 != nullptr ? a.sN / kGuCols : 0) + (long long)items * (a.N / kGuCols);
   if (blocks <= 0) return hipSuccess;
@@ -572,8 +581,8 @@ hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
 template <bool ROWS, bool TILED>
 hipError_t launch_dn(const GroupedArgs& a, hipStream_t s) {
   GroupedArgs b = a;
-  const int64_t items = max_items(a);
-  b.sgroups = a.sw0 != nullptr ? (a.M + kShRows - 1) / kShRows : 0;
+  const int64_t items = max_items(a, kDnRows);
+  b.sgroups = a.sw0 != nullptr ? (a.M + kDnShRows - 1) / kDnShRows : 0;
   const long long blocks = (long long)b.sgroups * (a.sw0 != nullptr ? (a.sN + kDnShCols - 1) / kDnShCols : 0) +
                            (long long)items * ((a.N + kDnCols - 1) / kDnCols);
   if (blocks <= 0) return hipSuccess;
