@@ -89,14 +89,14 @@ int grouped_passes(int64_t M) {
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, int fmt, bool tiled, hipStream_t s) {
-  if (grouped_wide(fmt, a, true)) return launch_wide_gate_up(a, tiled, s);
+  if (grouped_wide(fmt, a, true)) return launch_wide_gate_up(fmt, a, tiled, s);
   const int rowcap = grouped_step_rows(a.M);
   if (fmt == kFmtFP4) return launch_gate_up_fp4(a, rowcap, tiled, s);
   return fmt == kFmtFP8 ? launch_gate_up_fp8(a, rowcap, tiled, s) : launch_gate_up_bf16(a, rowcap, tiled, s);
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, int fmt, bool tiled, hipStream_t s) {
-  if (grouped_wide(fmt, a, false)) return launch_wide_down(a, tiled, s);
+  if (grouped_wide(fmt, a, false)) return launch_wide_down(fmt, a, tiled, s);
   const int rowcap = grouped_step_rows(a.M);
   if (fmt == kFmtFP4) return launch_down_fp4(a, rowcap, tiled, s);
   return fmt == kFmtFP8 ? launch_down_fp8(a, rowcap, tiled, s) : launch_down_bf16(a, rowcap, tiled, s);

@@ -146,14 +146,14 @@ int grouped_rows_per_pass(int64_t M);
 int grouped_step_rows(int64_t M);
 int grouped_passes(int64_t M);
 
-// Wide-pass kernels (wide.hip): every row an expert holds, up to 64 at a
-// time, per (expert, column group), so each expert's weights are streamed
-// once per column group; the same bits as the 16-row pass kernels.  Taken for
-// FP8 weights with the tables of the align launch when an expert can hold
-// more than 16 rows (M > 16).
+// Wide-pass kernels (wide.hip): every row an expert holds, 32 at a time, per
+// (expert pass, column group), so each expert's weights are streamed once per
+// column group per 32 rows; the same bits as the 16-row pass kernels.  Taken
+// for FP8 and MXFP4 weights with the tables of the align launch when an
+// expert can hold more than 16 rows (M > 16) and holds 4 on average.
 bool grouped_wide(int fmt, const GroupedArgs& a, bool gate_up);
-hipError_t launch_wide_gate_up(const GroupedArgs& a, bool tiled, hipStream_t s);
-hipError_t launch_wide_down(const GroupedArgs& a, bool tiled, hipStream_t s);
+hipError_t launch_wide_gate_up(int fmt, const GroupedArgs& a, bool tiled, hipStream_t s);
+hipError_t launch_wide_down(int fmt, const GroupedArgs& a, bool tiled, hipStream_t s);
 
 // fmt: the weight element format, kFmtBF16 / kFmtFP8 / kFmtFP4
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, int fmt, bool tiled, hipStream_t s);

@@ -2,17 +2,20 @@
 // a time, in one workgroup per (expert pass, column group), so an expert's
 // weights are streamed once per column group per 32 rows instead of once per
 // 16-row pass.  For layers whose experts hold many rows (verify and prefill
-// widths); FP8 weights (block or row scales), tiled or row-major.
+// widths); FP8 weights (block or row scales) or MXFP4, tiled or row-major.
 //
 // What is computed is the grouped projection of the pass kernels
 // (grouped_impl.h; metrale fp8_moe_grouped.rs: the gate+up and down launchers;
 // nbxtensor moe_decode_vec.py: the SwiGLU epilogue), with the same arithmetic
 // for every output element:
-//   gate+up: per 128-deep chunk c (one FP8 scale block), t = the chunk's 4 MFMA
-//            steps from zero, acc = fma(scale_c, t, acc), c ascending;
+//   gate+up: FP8: per 128-deep chunk c (one scale block), t = the chunk's 4
+//            MFMA steps from zero, acc = fma(scale_c, t, acc), c ascending;
+//            MXFP4: the codes decoded with their 32-deep block's power-of-two
+//            scale (exact in bf16), every MFMA step straight into acc;
 //            act = silu(g) * u
 //   down:    per 64-deep half h, t = its 2 MFMA steps over bf16 hi then lo of
-//            act, from zero; acc = acc + scale * t, both rounded, h ascending
+//            act, from zero; acc = acc + scale * t (FP8; MXFP4: acc + t), each
+//            operation rounded, h ascending
 // so a row has the same bits whichever kernel (or layer path) runs it.
 //
 // gfx950 design.  4 waves.  Each wave streams its own weight rows (16 gate
@@ -77,6 +80,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 
 // Which pass routed item j is: the active experts in ascending order, each
 // contributing ceil(count / RP) passes.  Every thread takes a run of active
@@ -131,7 +141,7 @@ __device__ __forceinline__ float block_scale(const float (&sr)[kSL], int c) {
 // codes where they are used (registers for 4 workgroups per compute unit);
 // every sum still runs its 4 steps in order.
 template <bool ROWS>
-__device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t* __restrict__ xb, int nrt, int q,
+__device__ __forceinline__ void gu_chunk(const u32x4 (&w)[2][2], const uint16_t* __restrict__ xb, int nrt, int q,
                                          int r16, float sg, float su, const f32x4 (&rs)[2],
                                          f32x4 (&acc)[2][kGuRows / 16]) {
 #pragma unroll
@@ -144,7 +154,7 @@ __device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t*
             as_bf16x8(*reinterpret_cast<const uint4*>(xb + (rt * 16 + r16) * kXStride + k_of_step<true>(s, q)));
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const uint4 v = w[st][s >> 1];
+          const u32x4 v = w[st][s >> 1];
           t[st] = mfma((s & 1) ? fp8x8_to_bf16(v.z, v.w) : fp8x8_to_bf16(v.x, v.y), b, t[st]);
         }
       }
@@ -157,12 +167,47 @@ __device__ __forceinline__ void gu_chunk(const uint4 (&w)[2][2], const uint16_t*
   }
 }
 
+// MXFP4: one 128-deep chunk, gate and up codes (half 0 in .x .y, half 1 in
+// .z .w) with the rows' scale dwords (one E8M0 byte per 32-deep block), over
+// NRT row tiles.  Each step's codes are decoded once for all row tiles; every
+// sum takes the steps in order.
+template <int NRT>
+__device__ __forceinline__ void gu_chunk_fp4_tiles(const u32x4 (&w)[2], const uint32_t (&sc)[2],
+                                                   const uint16_t* __restrict__ xb, int q, int r16,
+                                                   f32x4 (&acc)[2][kGuRows / 16]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    bf16x8 a[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) a[st] = fp4x8_to_bf16(w[st][s], e8m0_at(sc[st], 16 * (s >> 1) + 8 * (q >> 1)));
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const bf16x8 b =
+          as_bf16x8(*reinterpret_cast<const uint4*>(xb + (rt * 16 + r16) * kXStride + k_of_step<true>(s, q)));
+#pragma unroll
+      for (int st = 0; st < 2; ++st) acc[st][rt] = mfma(a[st], b, acc[st][rt]);
+    }
+  }
+}
+// the pass's row tiles (1 or 2) chosen once per chunk, so no branch splits a step
+__device__ __forceinline__ void gu_chunk_fp4(const u32x4 (&w)[2], const uint32_t (&sc)[2],
+                                             const uint16_t* __restrict__ xb, int nrt, int q, int r16,
+                                             f32x4 (&acc)[2][kGuRows / 16]) {
+  static_assert(kGuRows == 32, "one or two row tiles");
+  if (nrt > 1)
+    gu_chunk_fp4_tiles<2>(w, sc, xb, q, r16, acc);
+  else
+    gu_chunk_fp4_tiles<1>(w, sc, xb, q, r16, acc);
+}
+
 // Grid (1-D): the shared expert's (64-token pass, 64-column group) units, then
 // the routed (pass item, 64-column group) units with the column group fastest,
 // so the routing's real passes come first and the items past them (the grid
 // covers the most passes any routing of n slots can need) come last and exit.
-template <bool ROWS, bool TILED>
+template <int FMT, bool ROWS, bool TILED>
 __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p) {
+  constexpr bool FP4 = FMT == kFmtFP4;
+  static_assert(!(FP4 && ROWS), "MXFP4 has block scales only");
   constexpr int kRows = kGuRows, kShRows = kGuShRows, kRT = kRows / 16, kPieces = pieces_of<kRows>();
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [2][kRows][kXStride]
   __shared__ int s_src[kRows];
@@ -195,18 +240,25 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   const int nch = K / kKC;
   const int wcol = g * kGuCols + wave * kWaveCols;
 
-  const size_t wstride = (size_t)N * K;
+  const size_t wstride = FP4 ? (size_t)N * K / 2 : (size_t)N * K;  // bytes of one matrix
   const char* W0 = routed ? static_cast<const char*>(p.w0) + (size_t)e * wstride : static_cast<const char*>(p.sw0);
   const char* W1 = routed ? static_cast<const char*>(p.w1) + (size_t)e * wstride : static_cast<const char*>(p.sw1);
-  const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
-  const float* S0 = routed ? static_cast<const float*>(p.s0) + (size_t)e * sstride : static_cast<const float*>(p.ss0);
-  const float* S1 = routed ? static_cast<const float*>(p.s1) + (size_t)e * sstride : static_cast<const float*>(p.ss1);
-  // the expert's gate and up [N, K] FP8 matrices as buffers; tiled: the
-  // wave's 16-column tile is one run of 2 KB chunk fragments, this lane's 16
-  // bytes at 16 * lane of each 1 KB half; row-major: the lane's row
+  const size_t sstride = FP4 ? (size_t)N * (K / kMxBlock) : ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
+  const size_t sbytes = FP4 ? sstride : sstride * 4;
+  const char* S0 = routed ? static_cast<const char*>(p.s0) + (size_t)e * sbytes : static_cast<const char*>(p.ss0);
+  const char* S1 = routed ? static_cast<const char*>(p.s1) + (size_t)e * sbytes : static_cast<const char*>(p.ss1);
+  // the expert's gate and up [N, K] matrices as buffers; tiled: the wave's
+  // 16-column tile is one run of chunk fragments (FP8: 2 KB, this lane's 16
+  // bytes at 16 * lane of each 1 KB half; MXFP4: 1 KB, 8 bytes at 8 * lane of
+  // each 512-byte half); row-major: the lane's row
   const __amdgpu_buffer_rsrc_t wrs0 = rsrc(W0, (uint32_t)wstride), wrs1 = rsrc(W1, (uint32_t)wstride);
-  const uint32_t lo = (uint32_t)(TILED ? (size_t)(wcol / kWaveCols) * K * kWaveCols + lane * 16
-                                       : (size_t)(wcol + r16) * K + q * 16);
+  const uint32_t lo =
+      FP4 ? (uint32_t)(TILED ? (size_t)(wcol / kWaveCols) * (K / 2) * kWaveCols + lane * 8
+                             : (size_t)(wcol + r16) * (K / 2) + q * 8)
+          : (uint32_t)(TILED ? (size_t)(wcol / kWaveCols) * K * kWaveCols + lane * 16 : (size_t)(wcol + r16) * K + q * 16);
+  // MXFP4: the E8M0 scale bytes [N, K / 32] as buffers, this lane's row
+  const __amdgpu_buffer_rsrc_t srs0 = rsrc(S0, (uint32_t)sbytes), srs1 = rsrc(S1, (uint32_t)sbytes);
+  const uint32_t slo = (uint32_t)((size_t)(wcol + r16) * (K / kMxBlock));
 
   // the row sources: the token of each row
   if (tid < nr) s_src[tid] = routed ? p.sorted_token_ids[row_base + r0 + tid] / p.top_k : row_base + tid;
@@ -217,8 +269,12 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   f32x4 rs[2];
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    const float* sp = st == 0 ? S0 : S1;
-    if constexpr (ROWS) {
+    const float* sp = reinterpret_cast<const float*>(st == 0 ? S0 : S1);
+    if constexpr (FP4) {
+#pragma unroll
+      for (int i = 0; i < kSL; ++i) sreg[st][i] = 0.f;
+      rs[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else if constexpr (ROWS) {
       rs[st] = *reinterpret_cast<const f32x4*>(sp + wcol + 4 * q);
 #pragma unroll
       for (int i = 0; i < kSL; ++i) sreg[st][i] = 0.f;
@@ -243,7 +299,9 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
     xo[u] = u * 16 + prow < nr ? (uint32_t)(((size_t)s_src[u * 16 + prow] * K + ppc * 8) * 2) : kNoFetch;
   uint16_t* xdst = xs + prow * kXStride + ppc * 8;
 
-  uint4 wb[kGuRing][2][2];
+  u32x4 wb[kGuRing][2][2];    // FP8: [slot][gate, up][16-byte piece]
+  u32x4 wq[kGuRing][2];       // MXFP4: [slot][gate, up] codes of the chunk
+  uint32_t wsc[kGuRing][2];   // MXFP4: [slot][gate, up] scale dword of the chunk
   u32x4 xr[2][kPieces];
   f32x4 acc[2][kRT];
 #pragma unroll
@@ -253,13 +311,25 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   const int nrt = (nr + 15) >> 4;
 
   // chunks past the depth (the last round's padding) fetch nothing: zeros
-#define WIDE_LOAD_W(c, W)                                                                             \
+#define WIDE_LOAD_W(c, SLOT)                                                                          \
   {                                                                                                   \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                  \
-      const uint32_t off =                                                                            \
-          (c) < nch ? lo + (TILED ? (c) * (kKC * kWaveCols) + j * 1024 : (c) * kKC + j * 64) : kNoFetch; \
-      (W)[0][j] = __builtin_bit_cast(uint4, bload(wrs0, off));                                       \
-      (W)[1][j] = __builtin_bit_cast(uint4, bload(wrs1, off));                                       \
+    if constexpr (FP4) {                                                                              \
+      const uint32_t off = (c) < nch ? lo + (c) * (TILED ? 1024 : kKC / 2) : kNoFetch;               \
+      const uint32_t hoff = TILED ? 512 : 32;                                                         \
+      const uint32_t so = (c) < nch ? slo + 4 * (c) : kNoFetch;                                       \
+      const u32x2 g0 = bload8(wrs0, off), g1 = bload8(wrs0, off + hoff);                             \
+      const u32x2 u0 = bload8(wrs1, off), u1 = bload8(wrs1, off + hoff);                             \
+      wq[SLOT][0] = u32x4{g0.x, g0.y, g1.x, g1.y};                                                   \
+      wq[SLOT][1] = u32x4{u0.x, u0.y, u1.x, u1.y};                                                   \
+      wsc[SLOT][0] = bload4(srs0, so);                                                                \
+      wsc[SLOT][1] = bload4(srs1, so);                                                                \
+    } else {                                                                                          \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
+        const uint32_t off =                                                                          \
+            (c) < nch ? lo + (TILED ? (c) * (kKC * kWaveCols) + j * 1024 : (c) * kKC + j * 64) : kNoFetch; \
+        wb[SLOT][0][j] = bload(wrs0, off);                                                            \
+        wb[SLOT][1][j] = bload(wrs1, off);                                                            \
+      }                                                                                               \
     }                                                                                                 \
   }
 #define WIDE_LOAD_X(c, R)                                                                                         \
@@ -275,26 +345,30 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
 
   // prologue: x and weights of chunks 0 and 1 requested, x(0) staged
   WIDE_LOAD_X(0, xr[0]);
-  WIDE_LOAD_W(0, wb[0]);
+  WIDE_LOAD_W(0, 0);
   WIDE_LOAD_X(1, xr[1]);
-  WIDE_LOAD_W(1, wb[1]);
+  WIDE_LOAD_W(1, 1);
   WIDE_STORE_X(0, xr[0]);
   __syncthreads();
   // step c: request x and weights of chunk c + 2, multiply chunk c (ring slot
   // c % 3, LDS slot c % 2), stage x(c + 1), barrier.  Six steps written out,
   // so every ring index is a constant and no step is conditional (a load under
   // a branch costs a full wait for every load in flight); the depth is padded
-  // to whole rounds of 6 with chunks that fetch nothing (zeros, block scale
-  // 0), which leave every sum as it is.
+  // to whole rounds of 6 with chunks that fetch nothing (zero codes, x and
+  // scales), which leave every sum as it is (a sum that starts at +0 and adds
+  // rounded products is never -0, so adding zeros keeps its bits).
   const int nsteps = (nch + 5) / 6 * 6;
 #define WIDE_GU_STEP(JJ)                                                                                   \
   {                                                                                                        \
     const int c = c0 + (JJ);                                                                               \
     WIDE_LOAD_X(c + 2, xr[(JJ) % 2]);                                                                      \
-    WIDE_LOAD_W(c + 2, wb[((JJ) + 2) % 3]);                                                                \
+    WIDE_LOAD_W(c + 2, ((JJ) + 2) % 3);                                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
-    gu_chunk<ROWS>(wb[(JJ) % 3], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, block_scale(sreg[0], c), \
-                   block_scale(sreg[1], c), rs, acc);                                                      \
+    if constexpr (FP4)                                                                                     \
+      gu_chunk_fp4(wq[(JJ) % 3], wsc[(JJ) % 3], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, acc);     \
+    else                                                                                                   \
+      gu_chunk<ROWS>(wb[(JJ) % 3], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, block_scale(sreg[0], c), \
+                     block_scale(sreg[1], c), rs, acc);                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
     WIDE_STORE_X(((JJ) + 1) % 2, xr[((JJ) + 1) % 2]);                                                      \
     __syncthreads();                                                                                       \
@@ -377,14 +451,56 @@ __device__ __forceinline__ void dn_half(const u32x4 (&w)[kDnTiles], const uint16
   }
 }
 
+// MXFP4: one 64-deep half (hodd: the chunk's second), the wave's tiles' codes
+// (8 bytes each) and the scale dwords of their rows for the chunk
+__device__ __forceinline__ void dn_half_fp4(const u32x2 (&w)[kDnTiles], const uint32_t (&sc)[kDnTiles],
+                                            const uint16_t* __restrict__ ab, int nrt, int q, int r16, int ntl, int hodd,
+                                            f32x4 (&acc)[kDnTiles][kDnRows / 16]) {
+  bf16x8 a[kDnTiles][2];
+#pragma unroll
+  for (int tt = 0; tt < kDnTiles; ++tt) {
+    // this lane's 16 k of the half lie in 32-deep block 2 hodd + q / 2
+    const float bs = e8m0_at(sc[tt], 16 * hodd + 8 * (q >> 1));
+    a[tt][0] = fp4x8_to_bf16(w[tt].x, bs);
+    a[tt][1] = fp4x8_to_bf16(w[tt].y, bs);
+  }
+  constexpr int plane = kDnRows * kAStride;
+#pragma unroll
+  for (int rt = 0; rt < kDnRows / 16; ++rt) {
+    if (rt < nrt) {
+      bf16x8 b[2][2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          b[x][s] = as_bf16x8(
+              *reinterpret_cast<const uint4*>(ab + x * plane + (rt * 16 + r16) * kAStride + q * 16 + s * 8));
+#pragma unroll
+      for (int tt = 0; tt < kDnTiles; ++tt) {
+        if (tt < ntl) {
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int x = 0; x < 2; ++x) t = mfma(a[tt][s], b[x][s], t);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][rt][i] = add_rn(acc[tt][rt][i], t[i]);
+        }
+      }
+    }
+  }
+}
+
 // Grid (1-D): the shared expert's (32-token pass, 64-row group of H) units,
 // then the routed (pass item, 256-row group) units, the group fastest.  A
 // routed wave owns output tiles 4 (4g + w) .. +3, a shared wave tile 4g + w
 // (tiles past N: none of its work).  The halves run in rounds of 4 (the ring
 // length); a half past the depth multiplies zeros (its loads lie past their
 // buffers and fetch nothing; scale 0), which leaves every sum as it is.
-template <bool ROWS, bool TILED>
+template <int FMT, bool ROWS, bool TILED>
 __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
+  constexpr bool FP4 = FMT == kFmtFP4;
+  static_assert(!(FP4 && ROWS), "MXFP4 has block scales only");
   constexpr int kRows = kDnRows, kShRows = kDnShRows, kRT = kRows / 16, kPieces = pieces_of<kRows>();
   extern __shared__ __attribute__((aligned(16))) uint16_t as[];  // [2 slots][hi, lo][kRows][kAStride]
   __shared__ int s_item[4 + 2 * kWaves];
@@ -419,26 +535,41 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   const int tile0 = (g * kWaves + wave) * tpw;                     // first output tile of this wave
   const int ntl = min(tpw, max(0, N / kWaveCols - tile0));         // its tiles inside N
 
-  const size_t wstride = (size_t)N * K;
+  const size_t wstride = FP4 ? (size_t)N * K / 2 : (size_t)N * K;  // bytes of one matrix
   const char* W = routed ? static_cast<const char*>(p.w0) + (size_t)e * wstride : static_cast<const char*>(p.sw0);
-  const size_t sstride = ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
-  const float* S = routed ? static_cast<const float*>(p.s0) + (size_t)e * sstride : static_cast<const float*>(p.ss0);
-  // the expert's [N, K] FP8 matrix as a buffer; per tile: tiled, one run of
-  // 2 KB chunk fragments (1 KB per half, this lane's 16 bytes at 16 * lane);
-  // row-major, the lane's row.  A tile past the wave's count fetches nothing.
+  const size_t sstride = FP4 ? (size_t)N * (K / kMxBlock) : ROWS ? (size_t)N : (size_t)(N / kFp8Block) * (K / kFp8Block);
+  const size_t sbytes = FP4 ? sstride : sstride * 4;
+  const char* SB = routed ? static_cast<const char*>(p.s0) + (size_t)e * sbytes : static_cast<const char*>(p.ss0);
+  const float* S = reinterpret_cast<const float*>(SB);
+  // the expert's [N, K] matrix as a buffer; per tile: tiled, one run of chunk
+  // fragments (FP8: 2 KB, 1 KB per half, this lane's 16 bytes at 16 * lane;
+  // MXFP4: 1 KB, 512 bytes per half, 8 bytes at 8 * lane); row-major, the
+  // lane's row.  A tile past the wave's count fetches nothing.  MXFP4: the
+  // scale bytes [N, K / 32] as a buffer, this lane's row per tile.
   const __amdgpu_buffer_rsrc_t wrs = rsrc(W, (uint32_t)wstride);
-  uint32_t wo[kDnTiles];
+  const __amdgpu_buffer_rsrc_t srs = rsrc(SB, (uint32_t)sbytes);
+  uint32_t wo[kDnTiles], so[kDnTiles];
 #pragma unroll
   for (int tt = 0; tt < kDnTiles; ++tt) {
     const int t = tile0 + tt;
-    wo[tt] = tt < ntl ? (uint32_t)(TILED ? (size_t)t * K * kWaveCols + lane * 16 : (size_t)(t * kWaveCols + r16) * K + q * 16)
-                      : kNoFetch;
+    if constexpr (FP4)
+      wo[tt] = tt < ntl ? (uint32_t)(TILED ? (size_t)t * (K / 2) * kWaveCols + lane * 8
+                                           : (size_t)(t * kWaveCols + r16) * (K / 2) + q * 8)
+                        : kNoFetch;
+    else
+      wo[tt] = tt < ntl ? (uint32_t)(TILED ? (size_t)t * K * kWaveCols + lane * 16
+                                           : (size_t)(t * kWaveCols + r16) * K + q * 16)
+                        : kNoFetch;
+    so[tt] = tt < ntl ? (uint32_t)((size_t)(t * kWaveCols + r16) * (K / kMxBlock)) : kNoFetch;
   }
   float sreg[kSL];
   // ROWS: lane l of each wave puts the scale of row l % 16 of its tile l / 16 in LDS
   __shared__ float s_rs[ROWS ? kWaves * kDnTiles * kWaveCols : 1];
   float* const rsl = s_rs + (ROWS ? wave * kDnTiles * kWaveCols : 0);
-  if constexpr (ROWS) {
+  if constexpr (FP4) {
+#pragma unroll
+    for (int i = 0; i < kSL; ++i) sreg[i] = 0.f;
+  } else if constexpr (ROWS) {
     const int tt = lane >> 4;
     rsl[lane] = tt < ntl ? S[(tile0 + tt) * kWaveCols + (lane & 15)] : 0.f;
 #pragma unroll
@@ -464,7 +595,9 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   uint16_t* adst = as + prow * kAStride + ppc * 4;
   constexpr int plane = kRows * kAStride;
 
-  u32x4 wb[kDnRing][kDnTiles];
+  u32x4 wb[kDnRing][kDnTiles];        // FP8: [slot][tile] 16 bytes of the half
+  u32x2 wq[kDnRing][kDnTiles];        // MXFP4: [slot][tile] 8 bytes of the half
+  uint32_t wsc[kDnRing][kDnTiles];    // MXFP4: scale dwords, in the slot of a chunk's first half
   u32x4 xr[kDnSets][kPieces];
   f32x4 acc[kDnTiles][kRT];
 #pragma unroll
@@ -474,12 +607,24 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   const int nrt = (nr + 15) >> 4;
   const int nsteps = (nh + 3) / 4 * 4;  // whole rounds of 4
 
-  // halves past the depth: offsets past the buffers (zeros, nothing fetched)
-#define WIDE_LOAD_W(h, W)                                                                                   \
+  // halves past the depth: offsets past the buffers (zeros, nothing fetched).
+  // MXFP4: a chunk's scale dwords come with its first half (EVEN: h is even).
+#define WIDE_LOAD_W(h, SLOT, EVEN)                                                                          \
   {                                                                                                         \
-    const uint32_t off = (h) < nh ? (TILED ? ((h) >> 1) * (kKC * kWaveCols) + ((h) & 1) * 1024 : (h) * 64)   \
-                                  : kNoFetch;                                                               \
-    _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt)(W)[tt] = bload(wrs, wo[tt] + off);           \
+    if constexpr (FP4) {                                                                                    \
+      const uint32_t off =                                                                                  \
+          (h) < nh ? (TILED ? ((h) >> 1) * 1024 + ((h) & 1) * 512 : ((h) >> 1) * (kKC / 2) + ((h) & 1) * 32) \
+                   : kNoFetch;                                                                              \
+      _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) wq[SLOT][tt] = bload8(wrs, wo[tt] + off);    \
+      if (EVEN) {                                                                                           \
+        const uint32_t sof = (h) < nh ? ((h) >> 1) * 4 : kNoFetch;                                          \
+        _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) wsc[SLOT][tt] = bload4(srs, so[tt] + sof);  \
+      }                                                                                                     \
+    } else {                                                                                                \
+      const uint32_t off = (h) < nh ? (TILED ? ((h) >> 1) * (kKC * kWaveCols) + ((h) & 1) * 1024 : (h) * 64) \
+                                    : kNoFetch;                                                             \
+      _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) wb[SLOT][tt] = bload(wrs, wo[tt] + off);     \
+    }                                                                                                       \
   }
 #define WIDE_LOAD_A(h, R)                                                                                   \
   {                                                                                                         \
@@ -506,24 +651,31 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
 
   // prologue: act of halves 0, 1 and weights of 0, 1, 2 requested, act(0) staged
   WIDE_LOAD_A(0, xr[0]);
-  WIDE_LOAD_W(0, wb[0]);
+  WIDE_LOAD_W(0, 0, true);
   WIDE_LOAD_A(1, xr[1]);
-  WIDE_LOAD_W(1, wb[1]);
-  WIDE_LOAD_W(2, wb[2]);
+  WIDE_LOAD_W(1, 1, false);
+  WIDE_LOAD_W(2, 2, true);
   WIDE_STORE_A(0, xr[0]);
   __syncthreads();
   // step h: request the weights of h + 3 and the act of h + 2 (set h % 2 held
   // act(h), staged a step ago), multiply half h (ring slot h % 4, LDS slot
   // h % 2), stage act(h + 1) (requested a step ago), barrier.  Four steps
   // written out, so every ring index is a constant and no step is conditional.
+  // MXFP4: half h's scale dwords sit in its chunk's first slot (JJ & 2), which
+  // an odd step's load (of the even half h + 3) reuses: taken out first.
 #define WIDE_DN_STEP(JJ)                                                                                    \
   {                                                                                                         \
     const int h = h0 + (JJ);                                                                                \
-    WIDE_LOAD_W(h + 3, wb[((JJ) + 3) % 4]);                                                                 \
+    uint32_t sck[kDnTiles];                                                                                 \
+    _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) sck[tt] = FP4 ? wsc[(JJ) & 2][tt] : 0u;       \
+    WIDE_LOAD_W(h + 3, ((JJ) + 3) % 4, ((JJ) & 1) == 1);                                                    \
     WIDE_LOAD_A(h + 2, xr[(JJ) % 2]);                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
-    dn_half<ROWS>(wb[(JJ) % 4], as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, block_scale(sreg, h >> 1), rsl, \
-                  acc);                                                                                     \
+    if constexpr (FP4)                                                                                      \
+      dn_half_fp4(wq[(JJ) % 4], sck, as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, (JJ) & 1, acc);       \
+    else                                                                                                    \
+      dn_half<ROWS>(wb[(JJ) % 4], as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, block_scale(sreg, h >> 1), \
+                    rsl, acc);                                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
     WIDE_STORE_A(((JJ) + 1) % 2, xr[((JJ) + 1) % 2]);                                                       \
     __syncthreads();                                                                                        \
@@ -564,7 +716,7 @@ inline int64_t max_items(const GroupedArgs& a, int RP) {
   return (n + (int64_t)a.cap * (RP - 1)) / RP;
 }
 
-template <bool ROWS, bool TILED>
+template <int FMT, bool ROWS, bool TILED>
 hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
   GroupedArgs b = a;
   const int64_t items = max_items(a, kGuRows);
@@ -574,11 +726,11 @@ hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
   b.items = (int)items;
-  hipLaunchKernelGGL((wide_gate_up_kernel<ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kGuLds, s, b);
+  hipLaunchKernelGGL((wide_gate_up_kernel<FMT, ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kGuLds, s, b);
   return hipGetLastError();
 }
 
-template <bool ROWS, bool TILED>
+template <int FMT, bool ROWS, bool TILED>
 hipError_t launch_dn(const GroupedArgs& a, hipStream_t s) {
   GroupedArgs b = a;
   const int64_t items = max_items(a, kDnRows);
@@ -588,38 +740,45 @@ hipError_t launch_dn(const GroupedArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
   b.items = (int)items;
-  hipLaunchKernelGGL((wide_down_kernel<ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kDnLds, s, b);
+  hipLaunchKernelGGL((wide_down_kernel<FMT, ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kDnLds, s, b);
   return hipGetLastError();
 }
 
 }  // namespace wide_detail
 
 bool grouped_wide(int fmt, const GroupedArgs& a, bool gate_up) {
-  // FP8 only, tables from the align launch (not the fused align), experts that
-  // can hold more rows than one 16-row pass (M > 16) and hold 4 or more on
-  // average (n >= 4E: a sparser routing leaves most passes a few rows, which
-  // the 16-row kernels stream as fast), depth within the scale registers and
-  // (both kernels pad the depth to whole rounds themselves)
-  // (and every buffer the kernels address under 2^31 bytes)
+  // FP8 or MXFP4, tables from the align launch (not the fused align), experts
+  // that can hold more rows than one 16-row pass (M > 16) and hold 4 or more
+  // on average (n >= 4E: a sparser routing leaves most passes a few rows,
+  // which the 16-row kernels stream as fast), FP8 depth within the scale
+  // registers, gate+up widths in whole 64-column groups (MXFP4 allows any
+  // multiple of 16), and every buffer the kernels address under 2^31 bytes.
+  // Both kernels pad the depth to whole rounds themselves.
   constexpr int64_t kLim = (int64_t)1 << 31;
+  const bool fp4 = fmt == kFmtFP4;
   auto ok = [&](int N, int K) {
-    return K % mma::kKC == 0 && K / kFp8Block <= wide_detail::kMaxScaleBlocks && (int64_t)N * K < kLim &&
+    return K % mma::kKC == 0 && (fp4 || K / kFp8Block <= wide_detail::kMaxScaleBlocks) &&
+           (!gate_up || N % wide_detail::kGuCols == 0) && (int64_t)N * K < kLim &&
            (!gate_up || (int64_t)a.M * K * 2 < kLim);
   };
-  return fmt == kFmtFP8 && a.ids == nullptr && a.M > 16 && (int64_t)a.M * a.top_k >= 4 * (int64_t)a.E &&
+  return (fmt == kFmtFP8 || fp4) && a.ids == nullptr && a.M > 16 && (int64_t)a.M * a.top_k >= 4 * (int64_t)a.E &&
          ok(a.N, a.K) && (a.sw0 == nullptr || ok(a.sN, a.sK));
 }
 
-hipError_t launch_wide_gate_up(const GroupedArgs& a, bool tiled, hipStream_t s) {
+hipError_t launch_wide_gate_up(int fmt, const GroupedArgs& a, bool tiled, hipStream_t s) {
   using namespace wide_detail;
-  if (a.scale_rows) return tiled ? launch_gu<true, true>(a, s) : launch_gu<true, false>(a, s);
-  return tiled ? launch_gu<false, true>(a, s) : launch_gu<false, false>(a, s);
+  if (fmt == kFmtFP4) return tiled ? launch_gu<kFmtFP4, false, true>(a, s) : launch_gu<kFmtFP4, false, false>(a, s);
+  if (a.scale_rows)
+    return tiled ? launch_gu<kFmtFP8, true, true>(a, s) : launch_gu<kFmtFP8, true, false>(a, s);
+  return tiled ? launch_gu<kFmtFP8, false, true>(a, s) : launch_gu<kFmtFP8, false, false>(a, s);
 }
 
-hipError_t launch_wide_down(const GroupedArgs& a, bool tiled, hipStream_t s) {
+hipError_t launch_wide_down(int fmt, const GroupedArgs& a, bool tiled, hipStream_t s) {
   using namespace wide_detail;
-  if (a.scale_rows) return tiled ? launch_dn<true, true>(a, s) : launch_dn<true, false>(a, s);
-  return tiled ? launch_dn<false, true>(a, s) : launch_dn<false, false>(a, s);
+  if (fmt == kFmtFP4) return tiled ? launch_dn<kFmtFP4, false, true>(a, s) : launch_dn<kFmtFP4, false, false>(a, s);
+  if (a.scale_rows)
+    return tiled ? launch_dn<kFmtFP8, true, true>(a, s) : launch_dn<kFmtFP8, true, false>(a, s);
+  return tiled ? launch_dn<kFmtFP8, false, true>(a, s) : launch_dn<kFmtFP8, false, false>(a, s);
 }
 
 }  // namespace moe

@@ -1,11 +1,11 @@
-"""The wide-pass grouped kernels on the GPU (FP8 layers whose experts hold many
-rows): parity with the float64 oracle, and the same bits as the 16-row pass
-kernels (a run on the first 16 tokens takes those; its rows must equal the
-wide run's), on shapes that exercise the cases of the wide kernels: experts
-with several 32-row passes, every slot on a few experts, out-of-range ids, a
-shared expert whose tokens end mid-pass and whose depth ends mid-round,
-per-row scales, an output width that ends inside a 256-row group, and a
-depth of 3 chunks that the gate+up pads to a round of 6."""
+"""The wide-pass grouped kernels on the GPU (FP8 and MXFP4 layers whose experts
+hold many rows): parity with the float64 oracle, and the same bits as the
+16-row pass kernels (a run on the first 16 tokens takes those; its rows must
+equal the wide run's), on shapes that exercise the cases of the wide kernels:
+experts with several 32-row passes, every slot on a few experts, out-of-range
+ids, a shared expert whose tokens end mid-pass and whose depth ends mid-round,
+per-row scales, an output width that ends inside a 256-row group, and a depth
+of 3 chunks that the gate+up pads to a round of 6."""
 
 import numpy as np
 import pytest
@@ -36,6 +36,13 @@ CONFIGS = {
     # hidden 384: gate+up depth of 3 chunks (padded to a round of 6), down's
     # second 256-row group half full
     "mixed": workloads.MoeConfig("wide_mixed", 48, 384, 4, 2, 256, 0, 16, "fp8", "softmax", seed=63),
+    # MXFP4: experts of up to 96 rows
+    "mx_heavy": workloads.MoeConfig("wide_mx_heavy", 96, 512, 8, 4, 256, 0, 16, "mxfp4", "softmax_bias",
+                                    bias_std=3.0, seed=64),
+    # MXFP4, hidden 384 (gate+up depth 3 chunks, down's second 256-row group
+    # half full), routed down depth 128 (2 halves, padded to 4), a shared
+    # expert of 384 (6 halves) over 40 tokens (passes of 32 + 8)
+    "mx_shared": workloads.MoeConfig("wide_mx_shared", 40, 384, 8, 2, 128, 384, 16, "mxfp4", "softmax", seed=65),
 }
 
 _MODELS = {}
@@ -95,11 +102,12 @@ def test_wide_parity_and_pass_kernel_bits(moe, key):
             assert torch.equal(part.view(torch.int16), full[:m].view(torch.int16)), (m, layer.path(m))
 
 
-def test_wide_every_slot_on_few_experts(moe):
+@pytest.mark.parametrize("key", ["heavy", "mx_heavy"])
+def test_wide_every_slot_on_few_experts(moe, key):
     """Every token names experts 0..3 (96 rows each: three passes per expert),
     then a routing with out-of-range ids and a token whose slots are all
     dropped: oracle parity and pass-kernel bits."""
-    model = model_for("heavy")
+    model = model_for(key)
     cfg = model.cfg
     (x, ids0, w), (xt, _, wt) = device_inputs(cfg)
     few = np.tile(np.arange(4, dtype=np.int64), (cfg.M, 1))
