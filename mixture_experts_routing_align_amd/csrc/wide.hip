@@ -88,6 +88,24 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
+// MXFP4: copy n consecutive scale dwords (a workgroup's weight rows, K / 128
+// dwords each) from src to LDS, every load of a round issued before its
+// stores.  No barrier.
+constexpr int kStageJ = 8, kStageRound = kStageJ * kThreads;
+__device__ __forceinline__ void stage_scales(uint32_t* __restrict__ dst, const void* src, int n) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(src, (uint32_t)n * 4);
+  for (int b0 = 0; b0 < n; b0 += kStageRound) {
+    uint32_t v[kStageJ];
+#pragma unroll
+    for (int j = 0; j < kStageJ; ++j) v[j] = bload4(r, (uint32_t)(b0 + j * kThreads + (int)threadIdx.x) * 4);
+#pragma unroll
+    for (int j = 0; j < kStageJ; ++j) {
+      const int i = b0 + j * kThreads + (int)threadIdx.x;
+      if (i < n) dst[i] = v[j];
+    }
+  }
+}
+
 // Which pass routed item j is: the active experts in ascending order, each
 // contributing ceil(count / RP) passes.  Every thread takes a run of active
 // indices, a block scan of their pass counts places the runs, and the thread
@@ -256,9 +274,18 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
       FP4 ? (uint32_t)(TILED ? (size_t)(wcol / kWaveCols) * (K / 2) * kWaveCols + lane * 8
                              : (size_t)(wcol + r16) * (K / 2) + q * 8)
           : (uint32_t)(TILED ? (size_t)(wcol / kWaveCols) * K * kWaveCols + lane * 16 : (size_t)(wcol + r16) * K + q * 16);
-  // MXFP4: the E8M0 scale bytes [N, K / 32] as buffers, this lane's row
-  const __amdgpu_buffer_rsrc_t srs0 = rsrc(S0, (uint32_t)sbytes), srs1 = rsrc(S1, (uint32_t)sbytes);
-  const uint32_t slo = (uint32_t)((size_t)(wcol + r16) * (K / kMxBlock));
+  // MXFP4: the E8M0 scale bytes ([N, K / 32], one dword per row and chunk)
+  // of the workgroup's 64 gate and 64 up rows, staged in LDS once behind the x
+  // slots; each step reads the lane's row dword of the next chunk from there
+  const int kd = K / kKC;
+  uint32_t* const s_sc = reinterpret_cast<uint32_t*>(xs + 2 * kRows * kXStride);
+  if constexpr (FP4) {
+    const int n = kGuCols * kd;
+    stage_scales(s_sc, S0 + (size_t)g * n * 4, n);
+    stage_scales(s_sc + n, S1 + (size_t)g * n * 4, n);
+  }
+  const uint32_t* const sc_row0 = s_sc + (wave * kWaveCols + r16) * kd;
+  const uint32_t* const sc_row1 = sc_row0 + kGuCols * kd;
 
   // the row sources: the token of each row
   if (tid < nr) s_src[tid] = routed ? p.sorted_token_ids[row_base + r0 + tid] / p.top_k : row_base + tid;
@@ -301,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
 
   u32x4 wb[kGuRing][2][2];    // FP8: [slot][gate, up][16-byte piece]
   u32x4 wq[kGuRing][2];       // MXFP4: [slot][gate, up] codes of the chunk
-  uint32_t wsc[kGuRing][2];   // MXFP4: [slot][gate, up] scale dword of the chunk
+  uint32_t wsc[2][2];         // MXFP4: [chunk parity][gate, up] scale dwords, read a step ahead
   u32x4 xr[2][kPieces];
   f32x4 acc[2][kRT];
 #pragma unroll
@@ -316,13 +343,10 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
     if constexpr (FP4) {                                                                              \
       const uint32_t off = (c) < nch ? lo + (c) * (TILED ? 1024 : kKC / 2) : kNoFetch;               \
       const uint32_t hoff = TILED ? 512 : 32;                                                         \
-      const uint32_t so = (c) < nch ? slo + 4 * (c) : kNoFetch;                                       \
       const u32x2 g0 = bload8(wrs0, off), g1 = bload8(wrs0, off + hoff);                             \
       const u32x2 u0 = bload8(wrs1, off), u1 = bload8(wrs1, off + hoff);                             \
       wq[SLOT][0] = u32x4{g0.x, g0.y, g1.x, g1.y};                                                   \
       wq[SLOT][1] = u32x4{u0.x, u0.y, u1.x, u1.y};                                                   \
-      wsc[SLOT][0] = bload4(srs0, so);                                                                \
-      wsc[SLOT][1] = bload4(srs1, so);                                                                \
     } else {                                                                                          \
       _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
         const uint32_t off =                                                                          \
@@ -350,6 +374,10 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   WIDE_LOAD_W(1, 1);
   WIDE_STORE_X(0, xr[0]);
   __syncthreads();
+  if constexpr (FP4) {
+    wsc[0][0] = sc_row0[0];
+    wsc[0][1] = sc_row1[0];
+  }
   // step c: request x and weights of chunk c + 2, multiply chunk c (ring slot
   // c % 3, LDS slot c % 2), stage x(c + 1), barrier.  Six steps written out,
   // so every ring index is a constant and no step is conditional (a load under
@@ -363,9 +391,14 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
     const int c = c0 + (JJ);                                                                               \
     WIDE_LOAD_X(c + 2, xr[(JJ) % 2]);                                                                      \
     WIDE_LOAD_W(c + 2, ((JJ) + 2) % 3);                                                                    \
+    if constexpr (FP4) {                                                                                   \
+      const int cn = min(c + 1, nch - 1);                                                                  \
+      wsc[((JJ) + 1) % 2][0] = c + 1 < nch ? sc_row0[cn] : 0u;                                             \
+      wsc[((JJ) + 1) % 2][1] = c + 1 < nch ? sc_row1[cn] : 0u;                                             \
+    }                                                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
     if constexpr (FP4)                                                                                     \
-      gu_chunk_fp4(wq[(JJ) % 3], wsc[(JJ) % 3], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, acc);     \
+      gu_chunk_fp4(wq[(JJ) % 3], wsc[(JJ) % 2], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, acc);     \
     else                                                                                                   \
       gu_chunk<ROWS>(wb[(JJ) % 3], xs + ((JJ) % 2) * (kRows * kXStride), nrt, q, r16, block_scale(sreg[0], c), \
                      block_scale(sreg[1], c), rs, acc);                                                    \
@@ -544,11 +577,9 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   // the expert's [N, K] matrix as a buffer; per tile: tiled, one run of chunk
   // fragments (FP8: 2 KB, 1 KB per half, this lane's 16 bytes at 16 * lane;
   // MXFP4: 1 KB, 512 bytes per half, 8 bytes at 8 * lane); row-major, the
-  // lane's row.  A tile past the wave's count fetches nothing.  MXFP4: the
-  // scale bytes [N, K / 32] as a buffer, this lane's row per tile.
+  // lane's row.  A tile past the wave's count fetches nothing.
   const __amdgpu_buffer_rsrc_t wrs = rsrc(W, (uint32_t)wstride);
-  const __amdgpu_buffer_rsrc_t srs = rsrc(SB, (uint32_t)sbytes);
-  uint32_t wo[kDnTiles], so[kDnTiles];
+  uint32_t wo[kDnTiles];
 #pragma unroll
   for (int tt = 0; tt < kDnTiles; ++tt) {
     const int t = tile0 + tt;
@@ -560,7 +591,6 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
       wo[tt] = tt < ntl ? (uint32_t)(TILED ? (size_t)t * K * kWaveCols + lane * 16
                                            : (size_t)(t * kWaveCols + r16) * K + q * 16)
                         : kNoFetch;
-    so[tt] = tt < ntl ? (uint32_t)((size_t)(t * kWaveCols + r16) * (K / kMxBlock)) : kNoFetch;
   }
   float sreg[kSL];
   // ROWS: lane l of each wave puts the scale of row l % 16 of its tile l / 16 in LDS
@@ -582,6 +612,18 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
     for (int i = 0; i < kSL; ++i) sreg[i] = lane + 64 * i < kb ? sw[lane + 64 * i] : 0.f;
   }
 
+  // MXFP4: the scale dwords ([N, K / 32] bytes, one dword per row and chunk)
+  // of the workgroup's rows (its waves' tiles: consecutive rows of N), staged
+  // in LDS once behind the act slots; the lane reads its row's dword of each
+  // tile from there (a tile past N reads the wave's first row: not stored)
+  const int kd = K / kKC;
+  uint32_t* const s_sc = reinterpret_cast<uint32_t*>(as + 2 * 2 * kRows * kAStride);
+  if constexpr (FP4) {
+    const int row0 = g * kWaves * tpw * kWaveCols;
+    stage_scales(s_sc, SB + (size_t)row0 * kd * 4, min(kWaves * tpw * kWaveCols, N - row0) * kd);
+  }
+  const uint32_t* const sc_lane = s_sc + (wave * tpw * kWaveCols + r16) * kd;
+
   // the pass's act rows (consecutive: sorted positions, or tokens) as a buffer
   // of exactly nr rows; rows u*16 + prow, 4 floats at 4 * ppc of each half
   // (rows past nr lie past the buffer: no fetch, zeros)
@@ -597,7 +639,7 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
 
   u32x4 wb[kDnRing][kDnTiles];        // FP8: [slot][tile] 16 bytes of the half
   u32x2 wq[kDnRing][kDnTiles];        // MXFP4: [slot][tile] 8 bytes of the half
-  uint32_t wsc[kDnRing][kDnTiles];    // MXFP4: scale dwords, in the slot of a chunk's first half
+  uint32_t wsc[2][kDnTiles];          // MXFP4: [half parity][tile] scale dwords, read a step ahead
   u32x4 xr[kDnSets][kPieces];
   f32x4 acc[kDnTiles][kRT];
 #pragma unroll
@@ -607,19 +649,14 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   const int nrt = (nr + 15) >> 4;
   const int nsteps = (nh + 3) / 4 * 4;  // whole rounds of 4
 
-  // halves past the depth: offsets past the buffers (zeros, nothing fetched).
-  // MXFP4: a chunk's scale dwords come with its first half (EVEN: h is even).
-#define WIDE_LOAD_W(h, SLOT, EVEN)                                                                          \
+  // halves past the depth: offsets past the buffers (zeros, nothing fetched)
+#define WIDE_LOAD_W(h, SLOT)                                                                                \
   {                                                                                                         \
     if constexpr (FP4) {                                                                                    \
       const uint32_t off =                                                                                  \
           (h) < nh ? (TILED ? ((h) >> 1) * 1024 + ((h) & 1) * 512 : ((h) >> 1) * (kKC / 2) + ((h) & 1) * 32) \
                    : kNoFetch;                                                                              \
       _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) wq[SLOT][tt] = bload8(wrs, wo[tt] + off);    \
-      if (EVEN) {                                                                                           \
-        const uint32_t sof = (h) < nh ? ((h) >> 1) * 4 : kNoFetch;                                          \
-        _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) wsc[SLOT][tt] = bload4(srs, so[tt] + sof);  \
-      }                                                                                                     \
     } else {                                                                                                \
       const uint32_t off = (h) < nh ? (TILED ? ((h) >> 1) * (kKC * kWaveCols) + ((h) & 1) * 1024 : (h) * 64) \
                                     : kNoFetch;                                                             \
@@ -651,28 +688,35 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
 
   // prologue: act of halves 0, 1 and weights of 0, 1, 2 requested, act(0) staged
   WIDE_LOAD_A(0, xr[0]);
-  WIDE_LOAD_W(0, 0, true);
+  WIDE_LOAD_W(0, 0);
   WIDE_LOAD_A(1, xr[1]);
-  WIDE_LOAD_W(1, 1, false);
-  WIDE_LOAD_W(2, 2, true);
+  WIDE_LOAD_W(1, 1);
+  WIDE_LOAD_W(2, 2);
   WIDE_STORE_A(0, xr[0]);
   __syncthreads();
+  if constexpr (FP4) {
+#pragma unroll
+    for (int tt = 0; tt < kDnTiles; ++tt) wsc[0][tt] = sc_lane[tt < ntl ? tt * kWaveCols * kd : 0];
+  }
   // step h: request the weights of h + 3 and the act of h + 2 (set h % 2 held
   // act(h), staged a step ago), multiply half h (ring slot h % 4, LDS slot
   // h % 2), stage act(h + 1) (requested a step ago), barrier.  Four steps
   // written out, so every ring index is a constant and no step is conditional.
-  // MXFP4: half h's scale dwords sit in its chunk's first slot (JJ & 2), which
-  // an odd step's load (of the even half h + 3) reuses: taken out first.
+  // MXFP4: the scale dwords of half h + 1 (its chunk's, per tile) are read from
+  // LDS a step ahead.
 #define WIDE_DN_STEP(JJ)                                                                                    \
   {                                                                                                         \
     const int h = h0 + (JJ);                                                                                \
-    uint32_t sck[kDnTiles];                                                                                 \
-    _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) sck[tt] = FP4 ? wsc[(JJ) & 2][tt] : 0u;       \
-    WIDE_LOAD_W(h + 3, ((JJ) + 3) % 4, ((JJ) & 1) == 1);                                                    \
+    WIDE_LOAD_W(h + 3, ((JJ) + 3) % 4);                                                                     \
     WIDE_LOAD_A(h + 2, xr[(JJ) % 2]);                                                                       \
+    if constexpr (FP4) {                                                                                    \
+      const int cn = min((h + 1) >> 1, kd - 1);                                                             \
+      _Pragma("unroll") for (int tt = 0; tt < kDnTiles; ++tt) wsc[((JJ) + 1) % 2][tt] =                    \
+          h + 1 < nh ? sc_lane[(tt < ntl ? tt * kWaveCols * kd : 0) + cn] : 0u;                             \
+    }                                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                                      \
     if constexpr (FP4)                                                                                      \
-      dn_half_fp4(wq[(JJ) % 4], sck, as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, (JJ) & 1, acc);       \
+      dn_half_fp4(wq[(JJ) % 4], wsc[(JJ) % 2], as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, (JJ) & 1, acc); \
     else                                                                                                    \
       dn_half<ROWS>(wb[(JJ) % 4], as + ((JJ) % 2) * (2 * plane), nrt, q, r16, ntl, block_scale(sreg, h >> 1), \
                     rsl, acc);                                                                              \
@@ -709,6 +753,17 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
   }
 }
 
+// dynamic LDS of a launch: the staged activation slots, and (MXFP4) the scale
+// dwords of a workgroup's weight rows behind them
+inline size_t gu_lds(int fmt, const GroupedArgs& a) {
+  const int kd = max(a.K, a.sw0 != nullptr ? a.sK : 0) / kKC;
+  return kGuLds + (fmt == kFmtFP4 ? (size_t)2 * kGuCols * kd * 4 : 0);
+}
+inline size_t dn_lds(int fmt, const GroupedArgs& a) {
+  const size_t routed = (size_t)kDnCols * (a.K / kKC), shared = a.sw0 != nullptr ? (size_t)kDnShCols * (a.sK / kKC) : 0;
+  return kDnLds + (fmt == kFmtFP4 ? max(routed, shared) * 4 : 0);
+}
+
 // the most RP-row passes n slots can need: sum over experts of
 // ceil(count / RP) <= (n + active * (RP - 1)) / RP
 inline int64_t max_items(const GroupedArgs& a, int RP) {
@@ -726,7 +781,8 @@ hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
   b.items = (int)items;
-  hipLaunchKernelGGL((wide_gate_up_kernel<FMT, ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kGuLds, s, b);
+  hipLaunchKernelGGL((wide_gate_up_kernel<FMT, ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), gu_lds(FMT, a), s,
+                     b);
   return hipGetLastError();
 }
 
@@ -740,7 +796,8 @@ hipError_t launch_dn(const GroupedArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
   b.items = (int)items;
-  hipLaunchKernelGGL((wide_down_kernel<FMT, ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), kDnLds, s, b);
+  hipLaunchKernelGGL((wide_down_kernel<FMT, ROWS, TILED>), dim3((unsigned)blocks), dim3(kThreads), dn_lds(FMT, a), s,
+                     b);
   return hipGetLastError();
 }
 
@@ -752,8 +809,9 @@ bool grouped_wide(int fmt, const GroupedArgs& a, bool gate_up) {
   // on average (n >= 4E: a sparser routing leaves most passes a few rows,
   // which the 16-row kernels stream as fast), FP8 depth within the scale
   // registers, gate+up widths in whole 64-column groups (MXFP4 allows any
-  // multiple of 16), and every buffer the kernels address under 2^31 bytes.
-  // Both kernels pad the depth to whole rounds themselves.
+  // multiple of 16), MXFP4 scales of a workgroup's rows within 64 KB of LDS
+  // with the staged rows, and every buffer the kernels address under 2^31
+  // bytes.  Both kernels pad the depth to whole rounds themselves.
   constexpr int64_t kLim = (int64_t)1 << 31;
   const bool fp4 = fmt == kFmtFP4;
   auto ok = [&](int N, int K) {
@@ -761,8 +819,9 @@ bool grouped_wide(int fmt, const GroupedArgs& a, bool gate_up) {
            (!gate_up || N % wide_detail::kGuCols == 0) && (int64_t)N * K < kLim &&
            (!gate_up || (int64_t)a.M * K * 2 < kLim);
   };
+  const size_t lds = gate_up ? wide_detail::gu_lds(fmt, a) : wide_detail::dn_lds(fmt, a);
   return (fmt == kFmtFP8 || fp4) && a.ids == nullptr && a.M > 16 && (int64_t)a.M * a.top_k >= 4 * (int64_t)a.E &&
-         ok(a.N, a.K) && (a.sw0 == nullptr || ok(a.sN, a.sK));
+         ok(a.N, a.K) && (a.sw0 == nullptr || ok(a.sN, a.sK)) && lds + 1024 <= 65536;
 }
 
 hipError_t launch_wide_gate_up(int fmt, const GroupedArgs& a, bool tiled, hipStream_t s) {
