@@ -4,7 +4,8 @@
 // What it computes (nbxtensor 0.0.1 wheel page, moe_align.py: module docstring
 // and the stage-1/2/3 kernel docstrings; metrale fp8_moe_grouped.rs:
 // moe_fp8_grouped_sort): see align_device.h.  One launch, no atomics:
-//   pass 1   per-wave per-expert counts from wave ballots (leaders only write);
+//   pass 1   per-wave per-expert counts from wave ballots (leaders only write),
+//            every id requested up front and kept in registers;
 //   scan     per-wave bases, padded exclusive offsets, ascending active list;
 //   pass 2   stable scatter of every slot and token_to_perm;
 //   rest     counts, offsets, active list, total, padding sentinels, block owners.
@@ -23,6 +24,13 @@ constexpr int kAlignThreads = kAlignWaves * 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kAlignBlocksMinSlots = 4096;  // from here on the alignment runs over several blocks
 
+// Below kAlignBlocksMinSlots each wave walks at most kWaveChunks chunks of 64
+// slots: all of them are requested at once (before the count rows are
+// cleared), and their ids and same-expert masks stay in registers from the
+// count pass to the scatter pass.
+constexpr int kWaveChunks = kAlignBlocksMinSlots / kAlignThreads;
+static_assert(kWaveChunks * kAlignThreads == kAlignBlocksMinSlots, "whole chunks per wave");
+
 template <typename IdT>
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(const IdT* __restrict__ ids, int n, int E, int BS,
                                                               int max_total, int cap, int nbits, AlignOut o) {
@@ -32,10 +40,45 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(const IdT* __restr
   __shared__ int s_active[kMaxExperts];
   __shared__ int s_wa[kAlignWaves], s_wb[kAlignWaves], s_scal[2];
   const align_dev::ExpertLds s{cnt, s_count, s_off, s_active, s_wa, s_wb, s_scal};
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int beg, end;
+  align_dev::wave_range<kAlignWaves>(n, w, beg, end);
 
-  align_dev::count_pass<kAlignWaves>(ids, n, E, nbits, cnt);
+  int id[kWaveChunks];
+  bool valid[kWaveChunks];
+  uint64_t m[kWaveChunks];
+#pragma unroll
+  for (int j = 0; j < kWaveChunks; ++j) id[j] = align_dev::load_id(ids, beg + 64 * j + lane, end, E, valid[j]);
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) cnt[i] = 0;
+  __syncthreads();
+
+  // pass 1: per-wave counts, chunks in order, leaders only
+  int* my = cnt + w * E;
+#pragma unroll
+  for (int j = 0; j < kWaveChunks; ++j) {
+    m[j] = 0;
+    if (beg + 64 * j < end) {
+      m[j] = align_dev::same_expert_mask(id[j], valid[j], nbits);
+      if (valid[j] && align_dev::is_leader(m[j], lane)) my[id[j]] += __popcll(m[j]);
+    }
+  }
+  __syncthreads();
   align_dev::expert_scan<kAlignWaves>(s, E, BS);
-  align_dev::scatter_pass<kAlignWaves>(ids, n, E, nbits, cnt, s_off, o.sorted_token_ids, o.token_to_perm);
+
+  // pass 2: the stable scatter from the kept ids and masks, in the same order
+#pragma unroll
+  for (int j = 0; j < kWaveChunks; ++j) {
+    const int i = beg + 64 * j + lane;
+    if (valid[j]) {
+      const int pos = s_off[id[j]] + my[id[j]] + __popcll(m[j] & align_dev::lanes_below(lane));
+      o.sorted_token_ids[pos] = i;
+      o.token_to_perm[i] = pos;
+    } else if (i < end) {
+      o.token_to_perm[i] = -1;
+    }
+    // every lane has read its base above (a wave's LDS operations run in order)
+    if (valid[j] && align_dev::is_leader(m[j], lane)) my[id[j]] += __popcll(m[j]);
+  }
   align_dev::write_rest<kAlignWaves>(s, n, E, BS, max_total, cap, o);
 }
 

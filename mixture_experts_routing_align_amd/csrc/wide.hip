@@ -51,7 +51,8 @@ constexpr int kGuRows = 32, kGuShRows = 32;              // gate+up
 constexpr int kDnRows = 32, kDnShRows = 32;              // down
 static_assert(kGuShRows <= kGuRows && kDnShRows <= kDnRows, "a shared pass fits the routed pass registers");
 constexpr int kGuCols = kWaves * kWaveCols;              // gate+up columns per workgroup
-constexpr int kDnTiles = 4;                              // down: 16-row output tiles per wave
+constexpr int kDnTiles = 4;                              // down: 16-row output tiles per wave (at most 4)
+constexpr int kDnOcc = 3;                                // down: workgroups per compute unit
 constexpr int kDnCols = kWaves * kDnTiles * kWaveCols;   // down output rows (of H) per routed workgroup
 constexpr int kDnShCols = kWaves * kWaveCols;            // per shared-expert workgroup (one tile per wave)
 constexpr int kGuRing = 3;                               // gate+up: weight steps in the register ring (2 ahead)
@@ -531,7 +532,7 @@ __device__ __forceinline__ void dn_half_fp4(const u32x2 (&w)[kDnTiles], const ui
 // length); a half past the depth multiplies zeros (its loads lie past their
 // buffers and fetch nothing; scale 0), which leaves every sum as it is.
 template <int FMT, bool ROWS, bool TILED>
-__global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
+__global__ __launch_bounds__(kThreads, kDnOcc) void wide_down_kernel(GroupedArgs p) {
   constexpr bool FP4 = FMT == kFmtFP4;
   static_assert(!(FP4 && ROWS), "MXFP4 has block scales only");
   constexpr int kRows = kDnRows, kShRows = kDnShRows, kRT = kRows / 16, kPieces = pieces_of<kRows>();
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 3) void wide_down_kernel(GroupedArgs p) {
     for (int i = 0; i < kSL; ++i) sreg[i] = 0.f;
   } else if constexpr (ROWS) {
     const int tt = lane >> 4;
-    rsl[lane] = tt < ntl ? S[(tile0 + tt) * kWaveCols + (lane & 15)] : 0.f;
+    if (tt < kDnTiles) rsl[lane] = tt < ntl ? S[(tile0 + tt) * kWaveCols + (lane & 15)] : 0.f;
 #pragma unroll
     for (int i = 0; i < kSL; ++i) sreg[i] = 0.f;
   } else {
