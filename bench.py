@@ -15,10 +15,12 @@ remainder) for exactly K steps, bracketed by device syncs.
 
 Printed (one JSON line): layer rows/s (the value), weight-stream GB/s and its
 fraction of the 8 TB/s HBM peak, per-kernel times from HIP events, the
-roofline of the dominant kernel (the single-pass layer kernel: align, gate+up
-+SiLU and the down slices), the align latency on the prefill-scale align
+roofline of the dominant kernel (on the steps path, which the library takes
+at this width, the gate+up kernel with the align fused in; on the single pass
+the layer kernel: align, gate+up+SiLU and the down slices), the align latency
+on the prefill-scale align
 workload (n = 32768 int64 ids, 256 experts, BS 64), the router latency, the
-plain streaming-read ceiling for the same bytes, the verify-width layer
+plain streaming-read ceiling for the dominant kernel's bytes, the verify-width layer
 (M=128 with a shared expert; --other-configs) as context, and the float64
 CPU oracle timed on the host as a reference baseline (24 seeded decode
 routings).
@@ -39,7 +41,6 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer rows/s + weight-stream HBM GB/s (% of peak) at M=8; align latency us"
 HBM_PEAK_GBPS = 8000.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "layer_partials_decode_pmc.txt")
 
 
 def log(msg):
@@ -102,25 +103,35 @@ def time_graphs(multi, singles, steps, warmup):
     return time.perf_counter() - t0
 
 
-KERNEL_SOURCES = ("layer_fused.hip", "mma_common.h", "align_device.h", "moe_internal.h")
+# The dominant kernel of each layer path at decode width: the sources it is
+# built from (their digest ties a counter summary to them) and the committed
+# rocprofv3 counter summary of its HBM traffic.
+DOMINANT = {
+    "single_pass": {"sources": ("layer_fused.hip", "mma_common.h", "align_device.h", "moe_internal.h"),
+                    "pmc": "layer_partials_decode_pmc.txt"},
+    "steps": {"sources": ("grouped_impl.h", "grouped_gu_fp8.hip", "grouped.hip", "mma_common.h", "align_device.h",
+                          "moe_internal.h"),
+              "pmc": "grouped_gate_up_decode_pmc.txt"},
+}
 
 
-def source_digest():
-    """Digest of the sources the dominant kernel (the single-pass layer kernel) is built from."""
+def source_digest(path="single_pass"):
+    """Digest of the sources the path's dominant kernel is built from."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in DOMINANT[path]["sources"]:
         with open(os.path.join(ROOT, "mixture_experts_routing_align_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(digest):
+def traffic_from_profile(digest, path="single_pass"):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
-    if not os.path.exists(PROFILE_PMC):
+    pmc = os.path.join(ROOT, "profiles", DOMINANT[path]["pmc"])
+    if not os.path.exists(pmc):
         return None
     fields = {}
-    for line in open(PROFILE_PMC):
+    for line in open(pmc):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
@@ -320,14 +331,38 @@ def main():
     def k_blend(i):
         moe.moe_layer_blend_partials(layers[i], ids_d[i], w_d[i], outs[i], wss[i], stream=stream)
 
+    # the steps path: the launches moe_layer_forward makes at this width (the
+    # align fused into gate+up: at most MOE_FUSED_ALIGN_MAX_SLOTS slots and one
+    # pass per expert), each on the layer's own workspace
+    views = [layers[i].workspace_views(wss[i], cfg.M) for i in range(G)]
+
+    def tables(i):
+        return moe.AlignTables(*[views[i][f] for f in moe.TABLE_FIELDS])
+
+    def k_align_gate_up(i):
+        L = layers[i]
+        moe.moe_align_gate_up_silu(ids_d[i], xt, L.gate, L.up, cfg.E, cfg.BS, views[i]["act"], tables=tables(i),
+                                   stream=stream)
+
+    def k_down(i):
+        moe.moe_grouped_down(views[i]["act"], layers[i].down, tables(i), views[i]["expert_out"], cfg.M, cfg.top_k,
+                             cfg.BS, stream=stream)
+
+    def k_blend_steps(i):
+        moe.moe_blend(outs[i], views[i]["expert_out"], w_d[i], views[i]["token_to_perm"], stream=stream)
+
     if path == moe.MOE_LAYER_PATH_SINGLE_PASS:
         launches = (("layer_partials", k_partials), ("blend_partials", k_blend))
         dominant = "layer_partials"
         dominant_kernel = "layer_kernel<fp8> (moe_layer_partials: align + gate+up+SiLU + down slices)"
+        dominant_bytes = [b["total"] for b in bytes_per]
     else:
-        launches = (("layer_steps", step),)
-        dominant = "layer_steps"
-        dominant_kernel = "the steps path's launches together (align, gate+up, down, blend)"
+        assert cfg.M * cfg.top_k <= moe.MOE_FUSED_ALIGN_MAX_SLOTS and cfg.M <= 16, "the layer would align apart"
+        launches = (("align_gate_up", k_align_gate_up), ("down", k_down), ("blend", k_blend_steps))
+        dominant = "align_gate_up"
+        dominant_kernel = "grouped_kernel<fp8 gate+up, fused align> (moe_align_gate_up_silu: align + gate+up+SiLU)"
+        dominant_bytes = [b["gate_up"] for b in bytes_per]
+    pname = PATH_NAMES[path]
     kernels_us = {}
     for name, fn in launches:
         g = graph_of(lambda fn=fn: [fn(i) for _ in range(R) for i in range(G)], stream)
@@ -340,8 +375,8 @@ def main():
             ev1.record(stream)
         ev1.synchronize()
         kernels_us[name] = ev0.elapsed_time(ev1) * 1e3 / (3 * R * G)
-    layer_bytes = float(np.mean([b["total"] for b in bytes_per]))
-    part_gbps = layer_bytes / (kernels_us[dominant] * 1e-6) / 1e9
+    dom_bytes = float(np.mean(dominant_bytes))
+    part_gbps = dom_bytes / (kernels_us[dominant] * 1e-6) / 1e9
 
     # align latency on the prefill-scale align workload, graph-replayed
     log("align latency (n=32768, E=256, BS=64)")
@@ -403,11 +438,11 @@ def main():
     router_us = per_call_us(rg)
 
     # plain streaming-read ceiling in the same run: one launch of the library's
-    # read-only kernel over as many bytes as one layer streams (G disjoint
-    # buffers in rotation, like the weight copies), best of a few grid sizes;
-    # and the steady rate of one 4 GiB read
+    # read-only kernel over as many bytes as the dominant kernel streams (G
+    # disjoint buffers in rotation, like the weight copies), best of a few grid
+    # sizes; and the steady rate of one 4 GiB read
     log("streaming-read ceiling")
-    nb = int(layer_bytes) // 16 * 16
+    nb = int(dom_bytes) // 16 * 16
     bufs = [torch.ones(nb // 4, dtype=torch.int32, device=dev) for _ in range(G)]
     ceiling = {}
     for blocks in (1024, 2048, 4096, 8192):
@@ -450,8 +485,8 @@ def main():
         "dominant_frac_of_same_bytes": same_bytes_us / kernels_us[dominant],
     }
 
-    digest = source_digest()
-    traffic = traffic_from_profile(digest)
+    digest = source_digest(pname)
+    traffic = traffic_from_profile(digest, pname)
     result = {
         "metric": METRIC,
         "value": rows_per_s,
@@ -488,7 +523,7 @@ def main():
             "unit": "GB/s",
             "frac": part_gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": layer_bytes,
+            "algorithmic_bytes_per_launch": dom_bytes,
             "source_digest": digest,
         },
         "align_us": align_us,

@@ -277,9 +277,13 @@ int moe_blend(void* out_bf16, const float* expert_out, const float* topk_weights
  * `path` field; MOE_LAYER_PATH_AUTO (0) lets the library choose from the
  * descriptor's shapes (never from the routing, so a captured graph stays valid
  * for any routing): the narrow path for at most MOE_NARROW_AUTO_SLOTS slots
- * where it fits, else the single pass where it fits, else the steps.  (The FP8
- * page picks its decode kernel pair the same way, from the shape and a kill
- * switch read once: metrale forward_nvfp4_grouped_decode.rs,
+ * where it fits; else the single pass where it fits, except where the steps
+ * measured faster on MI355X (MXFP4 and per-row FP8 scales at every width;
+ * block-scaled FP8 where the slots exceed 6 times the rows of one pass of the
+ * 4- and 8-row pass classes, e.g. 4, 7 and 8 tokens at top-8); else the
+ * steps.  Every path gives the same bits, so the choice changes only time.
+ * (The FP8 page picks its decode kernel pair the same way, from the shape and
+ * a kill switch read once: metrale forward_nvfp4_grouped_decode.rs,
  * nvfp4_grouped_tc_enabled.)
  *  - MOE_LAYER_PATH_STEPS: align (fused into gate+up for at most
  *    MOE_FUSED_ALIGN_MAX_SLOTS slots when every expert fits one pass; from

@@ -210,6 +210,21 @@ int forced_path() {
 // default the narrow path for a few tokens, else the single-pass layer where
 // it fits (tiled weights at decode width), else the steps.  A forced path that
 // does not fit is refused.
+// Where the single pass fits, AUTO still takes the steps path where that
+// measured faster on the decode layer (2048 x 768, 128 experts, top-8; both
+// give the same bits, so only time decides): MXFP4 at every width (the single
+// pass at best even, and 1.7-1.9x slower from 9 tokens), per-row FP8 scales
+// (faster at 4-5 and 7-12 tokens, 1.2 us slower at 6), and block-scaled FP8
+// when the slots exceed 6 times the rows of one pass in the 4- and 8-row pass
+// classes (4, 7 and 8 tokens: 1.2, 1.8 and 3.1 us faster; at 5-6 tokens and
+// in the 16-row class the single pass is as fast or faster).
+bool auto_prefers_steps(moe_weight_dtype wdt, int64_t M, int64_t n) {
+  if (is_fp4(wdt) || is_rows(wdt)) return true;
+  if (!is_fp8(wdt)) return false;
+  const int rowcap = moe::grouped_rows_per_pass(M);
+  return rowcap <= 8 && n > 6 * (int64_t)rowcap;
+}
+
 int layer_path(const char* fn, const moe_layer_desc* d) {
   static_assert(MOE_NARROW_LAYER_MAX_SLOTS == moe::kNarrowLayerMaxSlots, "narrow slot limit");
   const int64_t n = d->M * d->top_k;
@@ -230,7 +245,7 @@ int layer_path(const char* fn, const moe_layer_desc* d) {
                 fn, MOE_NARROW_LAYER_MAX_SLOTS, (long long)n);
   if (want != MOE_LAYER_PATH_AUTO) return want;
   if (narrow_fits && n <= MOE_NARROW_AUTO_SLOTS) return MOE_LAYER_PATH_NARROW;
-  return fits ? MOE_LAYER_PATH_SINGLE_PASS : MOE_LAYER_PATH_STEPS;
+  return fits && !auto_prefers_steps(d->wdt, d->M, n) ? MOE_LAYER_PATH_SINGLE_PASS : MOE_LAYER_PATH_STEPS;
 }
 
 // MOE_LOG=1 (read once per process): one line on stderr the first time the

@@ -161,6 +161,21 @@ def _tiled(d):
     return d
 
 
+def _rows_per_pass(M):
+    r = 4
+    while r < M and r < 128:
+        r *= 2
+    return r
+
+
+def _auto_single(M, n, fp8):
+    """Where the single pass fits, AUTO's documented choice for tiled FP8
+    (block scales) and BF16 weights: FP8 takes the steps when the slots exceed
+    6 times the rows of one pass in the 4- and 8-row classes."""
+    r = _rows_per_pass(M)
+    return not (fp8 and r <= 8 and n > 6 * r)
+
+
 @pytest.mark.parametrize("tiled", [False, True])
 def test_workspace_layout(lib, tiled):
     R = _ffi.MOE_LAYER_WORKSPACE_REGIONS
@@ -177,7 +192,9 @@ def test_workspace_layout(lib, tiled):
         mt = oracle.max_total(n, a["E"], a["BS"])
         path = lib.moe_layer_path(ctypes.byref(d))
         # the single pass runs tiled weights at decode width (at most 256 slots)
-        assert path == (_ffi.MOE_LAYER_PATH_SINGLE_PASS if tiled and n <= 256 else _ffi.MOE_LAYER_PATH_STEPS)
+        # where AUTO does not prefer the steps
+        single_auto = tiled and n <= 256 and _auto_single(a["M"], n, kw.get("wdt", 1) == 1)
+        assert path == (_ffi.MOE_LAYER_PATH_SINGLE_PASS if single_auto else _ffi.MOE_LAYER_PATH_STEPS), kw
         single = path == _ffi.MOE_LAYER_PATH_SINGLE_PASS
         M, H, I, S = a["M"], a["H"], a["I"], a["S"]
         sizes = [mt * 4, mt // a["BS"] * 4, (a["E"] + 1) * 4, a["E"] * 4, n * 4, min(n, a["E"]) * 4, 4, 4,
@@ -236,7 +253,8 @@ def test_fused_align_gate_up_refusals(lib):
 
 def test_single_pass_stage_refusals(lib):
     """The stage calls refuse a descriptor that takes the steps path (row-major
-    weights, or more than 256 slots) and check the workspace like the layer."""
+    weights, more than 256 slots, or AUTO's choice of the steps) and check the
+    workspace like the layer."""
     d = _desc()                                   # row-major FP8: steps path
     need = lib.moe_layer_workspace_bytes(ctypes.byref(d))
     assert lib.moe_layer_partials(ctypes.byref(d), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
@@ -246,7 +264,11 @@ def test_single_pass_stage_refusals(lib):
     big = _tiled(_desc(M=128))                    # 1024 slots
     need = lib.moe_layer_workspace_bytes(ctypes.byref(big))
     assert lib.moe_layer_partials(ctypes.byref(big), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
-    t = _tiled(_desc())                           # decode shape, tiled: single pass
+    auto8 = _tiled(_desc())                       # decode shape, tiled: AUTO takes the steps
+    need = lib.moe_layer_workspace_bytes(ctypes.byref(auto8))
+    assert lib.moe_layer_partials(ctypes.byref(auto8), FAKE, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_SHAPE
+    t = _tiled(_desc())                           # the same, forced onto the single pass
+    t.path = _ffi.MOE_LAYER_PATH_SINGLE_PASS
     need = lib.moe_layer_workspace_bytes(ctypes.byref(t))
     assert lib.moe_layer_partials(ctypes.byref(t), FAKE, FAKE, 0x100000, need - 1, None) == _ffi.MOE_ERR_WORKSPACE
     assert lib.moe_layer_partials(ctypes.byref(t), None, FAKE, 0x100000, need, None) == _ffi.MOE_ERR_NULL
@@ -262,7 +284,7 @@ def test_path_control(lib):
     every valid descriptor, SINGLE_PASS is refused where it does not fit; the
     workspace follows the chosen path."""
     P = _ffi
-    t = _tiled(_desc())                                 # decode, tiled: AUTO takes the single pass
+    t = _tiled(_desc(M=6))                              # 6 tokens, tiled: AUTO takes the single pass
     assert lib.moe_layer_path(ctypes.byref(t)) == P.MOE_LAYER_PATH_SINGLE_PASS
     auto_bytes = lib.moe_layer_workspace_bytes(ctypes.byref(t))
     t.path = P.MOE_LAYER_PATH_STEPS
@@ -292,6 +314,28 @@ def test_path_control(lib):
     assert "path" in _err(lib)
 
 
+def test_auto_path_by_shape_class(lib):
+    """Where the single pass fits, AUTO takes the steps where they measured
+    faster: block-scaled FP8 past 6 slots per pass row in the 4- and 8-row
+    classes (4, 7, 8 tokens at top-8), MXFP4 and per-row FP8 scales at every
+    width; BF16 always the single pass.  A forced single pass still runs."""
+    P = _ffi
+    for M, want in ((4, P.MOE_LAYER_PATH_STEPS), (5, P.MOE_LAYER_PATH_SINGLE_PASS),
+                    (6, P.MOE_LAYER_PATH_SINGLE_PASS), (7, P.MOE_LAYER_PATH_STEPS), (8, P.MOE_LAYER_PATH_STEPS),
+                    (9, P.MOE_LAYER_PATH_SINGLE_PASS), (12, P.MOE_LAYER_PATH_SINGLE_PASS),
+                    (16, P.MOE_LAYER_PATH_SINGLE_PASS), (33, P.MOE_LAYER_PATH_STEPS)):
+        assert lib.moe_layer_path(ctypes.byref(_tiled(_desc(M=M)))) == want, M
+    for wdt in (P.MOE_W_MXFP4_TILED, P.MOE_W_FP8_E4M3_ROWS_TILED):
+        for M in (4, 5, 6, 8, 9, 16):
+            d = _desc(M=M)
+            d.wdt = wdt
+            assert lib.moe_layer_path(ctypes.byref(d)) == P.MOE_LAYER_PATH_STEPS, (wdt, M)
+            d.path = P.MOE_LAYER_PATH_SINGLE_PASS
+            assert lib.moe_layer_path(ctypes.byref(d)) == P.MOE_LAYER_PATH_SINGLE_PASS, (wdt, M)
+    for M in (4, 8, 16):
+        assert lib.moe_layer_path(ctypes.byref(_tiled(_desc(M=M, wdt=0)))) == P.MOE_LAYER_PATH_SINGLE_PASS, M
+
+
 def test_narrow_path_control(lib):
     """AUTO takes the narrow path for tiled FP8 weights and at most
     MOE_NARROW_AUTO_SLOTS slots; forcing it elsewhere (BF16, row-major, more
@@ -299,13 +343,13 @@ def test_narrow_path_control(lib):
     by slot and no expert_out, sh_out or partials."""
     P = _ffi
     for M, want in ((1, P.MOE_LAYER_PATH_NARROW), (2, P.MOE_LAYER_PATH_NARROW), (3, P.MOE_LAYER_PATH_NARROW),
-                    (4, P.MOE_LAYER_PATH_SINGLE_PASS), (8, P.MOE_LAYER_PATH_SINGLE_PASS)):
+                    (4, P.MOE_LAYER_PATH_STEPS), (5, P.MOE_LAYER_PATH_SINGLE_PASS), (8, P.MOE_LAYER_PATH_STEPS)):
         assert lib.moe_layer_path(ctypes.byref(_tiled(_desc(M=M)))) == want, M
     four = _tiled(_desc(M=4))                           # 32 slots of 768-wide act: past the LDS budget
     four.path = P.MOE_LAYER_PATH_NARROW
     assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_ERR_SHAPE
     four = _tiled(_desc(M=4, H=1024, I=256))            # 32 slots of a smaller layer: narrow when asked for
-    assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_LAYER_PATH_SINGLE_PASS
+    assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_LAYER_PATH_STEPS
     four.path = P.MOE_LAYER_PATH_NARROW
     assert lib.moe_layer_path(ctypes.byref(four)) == P.MOE_LAYER_PATH_NARROW
     five = _tiled(_desc(M=5, H=1024, I=256))
@@ -333,7 +377,7 @@ sys.path.insert(0, {root!r})
 from mixture_experts_routing_align_amd import _ffi
 from tests.test_abi import _desc, _tiled
 lib = _ffi.load()
-t = _tiled(_desc())
+t = _tiled(_desc(M=6))
 auto = lib.moe_layer_path(ctypes.byref(t))
 t.path = _ffi.MOE_LAYER_PATH_SINGLE_PASS
 explicit = lib.moe_layer_path(ctypes.byref(t))
@@ -469,6 +513,7 @@ def test_misaligned_pointers_refused(lib):
     wodd.down = _ffi.MoeWeight(odd, FAKE)
     refused(lib.moe_layer_forward(ctypes.byref(wodd), FAKE, FAKE, FAKE, FAKE, 0x100000, need, None), "down weights")
     single = _tiled(_desc())
+    single.path = _ffi.MOE_LAYER_PATH_SINGLE_PASS
     need1 = lib.moe_layer_workspace_bytes(ctypes.byref(single))
     assert lib.moe_layer_path(ctypes.byref(single)) == _ffi.MOE_LAYER_PATH_SINGLE_PASS
     refused(lib.moe_layer_partials(ctypes.byref(single), odd, FAKE, 0x100000, need1, None), "x")

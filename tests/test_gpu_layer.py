@@ -154,14 +154,17 @@ def test_layer_int32_ids_same_bits(moe):
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
 def test_single_pass_layer_parity(moe, name):
-    """Tiled weights at decode width take the single-pass path: tables bit-exact,
-    output and each slot's expert output (the sum of its slices) within tolerance."""
+    """Tiled weights at decode width on the single-pass path (AUTO's choice for
+    the BF16 tiny layer; forced for the FP8 decode layer, where AUTO takes the
+    steps): tables bit-exact, output and each slot's expert output (the sum of
+    its slices) within tolerance."""
     model = model_for(name)
     cfg = model.cfg
     (x, ids, w), (xt, it, wt) = device_inputs(cfg)
-    assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    single = moe.MOE_LAYER_PATH_SINGLE_PASS
+    assert model.tiled_layer().path(cfg.M) == (single if name == "tiny" else moe.MOE_LAYER_PATH_STEPS)
     log(f"single-pass parity: config {name}")
-    out, views = _run_layer(moe, model, xt, it, wt, tiled=True)
+    out, views = _run_layer(moe, model, xt, it, wt, tiled=True, path=single)
     assert "act" not in views and "part" in views
     ref = oracle_layer(model, x, ids, w)
     compare_tables(views, ref["tables"])
@@ -179,7 +182,7 @@ def test_single_pass_stages_equal_forward(moe):
     """moe_layer_partials then moe_layer_blend_partials give moe_layer_forward's bits."""
     model = model_for("decode")
     _, (xt, it, wt) = device_inputs(model.cfg)
-    layer = model.tiled_layer()
+    layer = model.tiled_layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS)
     a = layer.forward(xt, it, wt)
     ws = layer.alloc_workspace(xt.shape[0])
     moe.moe_layer_partials(layer, xt, it, ws)
@@ -360,13 +363,16 @@ def test_blend_parity_and_invariants(moe):
 
 # ------------------------------------------------------------ graph replay --
 
-@pytest.mark.parametrize("tiled", [False, True])
-def test_graph_replay_follows_new_routing(moe, tiled):
+@pytest.mark.parametrize("kind", ["rowmajor", "tiled", "single"])
+def test_graph_replay_follows_new_routing(moe, kind):
     """Capture the layer once; overwrite ids/weights in place between replays;
-    every replay must match the oracle for the routing it saw."""
+    every replay must match the oracle for the routing it saw.  Row-major and
+    tiled weights under AUTO (both the steps at this width), and tiled weights
+    forced onto the single pass."""
     model = model_for("decode")
     cfg = model.cfg
-    layer = model.tiled_layer() if tiled else model.layer()
+    layer = {"rowmajor": model.layer(), "tiled": model.tiled_layer(),
+             "single": model.tiled_layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS)}[kind]
     (x, ids0, w0), (xt, it, wt) = device_inputs(cfg)
     ws = layer.alloc_workspace(cfg.M)
     out = torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device="cuda")
@@ -577,7 +583,8 @@ def test_row_scales_single_pass(moe, name):
 def test_row_scales_full_size(moe, name):
     """The decode and verify layers at full size with per-row FP8 scales:
     row-major weights (the steps path) against the oracle, tables bit-exact,
-    and tiled weights (decode: the single pass) with the same bits."""
+    and tiled weights (AUTO: the steps; decode also forced onto the single
+    pass) with the same bits."""
     cfg = workloads.CONFIGS[name].replace(wdt="fp8_rows", name=name + "_rows")
     log(f"row-scale full size: {cfg}")
     model = DeviceModel(cfg, threads=16)
@@ -589,5 +596,8 @@ def test_row_scales_full_size(moe, name):
     log(f"  out: max err {err:.3e} bound {bound:.3e}")
     assert ok, (err, bound)
     tiled, _ = _run_layer(moe, model, xt, it, wt, tiled=True)
-    assert (model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS) == (name == "decode")
+    assert model.tiled_layer().path(cfg.M) == moe.MOE_LAYER_PATH_STEPS
     assert torch.equal(tiled.view(torch.int16), out.view(torch.int16))
+    if name == "decode":
+        single, _ = _run_layer(moe, model, xt, it, wt, tiled=True, path=moe.MOE_LAYER_PATH_SINGLE_PASS)
+        assert torch.equal(single.view(torch.int16), out.view(torch.int16))

@@ -128,18 +128,26 @@ def _run(moe, layer, xt, it, wt):
     return out, layer.workspace_views(ws, xt.shape[0])
 
 
+def _single_fits(moe, model, M):
+    try:
+        return model.tiled_layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS).path(M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    except moe.MoeError:
+        return False
+
+
 @pytest.mark.parametrize("key", list(MX))
 def test_mxfp4_layer_parity(moe, key):
-    """Row-major (the steps path) and tiled weights (the single pass where the
-    shape fits): tables bit-exact, output within the bound of the oracle, and
-    the two runs equal bit for bit."""
+    """Row-major weights (the steps path), tiled weights under AUTO (the steps
+    for MXFP4) and tiled weights forced onto the single pass where the shape
+    fits: tables bit-exact, output within the bound of the oracle, and the runs
+    equal bit for bit."""
     model = model_for(key)
     cfg = model.cfg
     (x, ids, w), (xt, it, wt) = device_inputs(cfg)
     log(f"MXFP4 layer parity: {cfg}")
     layer = model.layer()
     tiled = model.tiled_layer()
-    log(f"  paths: row-major {layer.path(cfg.M)}, tiled {tiled.path(cfg.M)}")
+    assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_STEPS
     a, views = _run(moe, layer, xt, it, wt)
     b, tviews = _run(moe, tiled, xt, it, wt)
     ref = oracle_layer(model, x, ids, w)
@@ -149,6 +157,11 @@ def test_mxfp4_layer_parity(moe, key):
     log(f"  out: max err {err:.3e} bound {bound:.3e}")
     assert ok, (err, bound)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    if _single_fits(moe, model, cfg.M):
+        c, sviews = _run(moe, tiled.with_path(moe.MOE_LAYER_PATH_SINGLE_PASS), xt, it, wt)
+        compare_tables(sviews, ref["tables"])
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+        log("  single pass: the same bits")
     pos = sorted(ref["act_pos"])
     act = views["act"][pos].cpu().double().numpy()
     ok, err, bound = tolerance_ok(act, np.stack([ref["act_pos"][p] for p in pos]))
@@ -158,16 +171,16 @@ def test_mxfp4_layer_parity(moe, key):
     assert ok, ("expert_out", err, bound)
 
 
-def test_mxfp4_decode_takes_single_pass_and_matches_steps(moe):
-    """The decode layer with tiled MXFP4 weights runs the single pass; forced
-    onto the steps path it gives the same bits, and so do the four separate
-    calls."""
+def test_mxfp4_decode_steps_match_single_pass(moe):
+    """The decode layer with tiled MXFP4 weights runs the steps under AUTO;
+    forced onto the single pass it gives the same bits, and so do the four
+    separate calls."""
     model = model_for("decode")
     _, (xt, it, wt) = device_inputs(model.cfg)
     tiled = model.tiled_layer()
-    assert tiled.path(model.cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
-    a = tiled.forward(xt, it, wt)
-    b = tiled.with_path(moe.MOE_LAYER_PATH_STEPS).forward(xt, it, wt)
+    assert tiled.path(model.cfg.M) == moe.MOE_LAYER_PATH_STEPS
+    a = tiled.with_path(moe.MOE_LAYER_PATH_SINGLE_PASS).forward(xt, it, wt)
+    b = tiled.forward(xt, it, wt)
     c, _ = separate_steps(moe, tiled, xt, it, wt)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
@@ -178,10 +191,14 @@ def test_mxfp4_decode_takes_single_pass_and_matches_steps(moe):
                                     ("wide", [1, 17, 64, 128, 129])])
 def test_mxfp4_row_invariance(moe, key, ms):
     """Rows of a run on the first m tokens equal the full run's rows bit for
-    bit, tiled weights (decode: the single pass) and row-major."""
+    bit: tiled weights (AUTO), row-major, and (decode) tiled weights forced
+    onto the single pass."""
     model = model_for(key)
     _, (xt, it, wt) = device_inputs(model.cfg)
-    for layer in (model.tiled_layer(), model.layer()):
+    layers = [model.tiled_layer(), model.layer()]
+    if key == "decode":
+        layers.append(model.tiled_layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS))
+    for layer in layers:
         full = layer.forward(xt, it, wt)
         for m in ms:
             part = layer.forward(xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous())

@@ -116,7 +116,7 @@ def test_narrow_32_slots_two_row_tiles(moe):
     cfg = model.cfg
     (x, ids0, w), (xt, it0, wt) = device_inputs(cfg)
     tiled = model.tiled_layer()
-    assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_STEPS  # AUTO at 4 tokens of top-8
     narrow = tiled.with_path(moe.MOE_LAYER_PATH_NARROW)
     single = tiled.with_path(moe.MOE_LAYER_PATH_SINGLE_PASS)
     one = np.full((cfg.M, cfg.top_k), 5, dtype=np.int64)

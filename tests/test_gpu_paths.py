@@ -24,21 +24,32 @@ def moe():
 
 
 def test_forced_paths_same_bits(moe):
-    """The decode layer with tiled weights, AUTO (the single pass) and forced
-    onto the steps path: the same output bits; a row-major layer cannot be
-    forced onto the single pass."""
+    """The decode layer with tiled weights: AUTO (the steps at 8 tokens), forced
+    onto the steps and forced onto the single pass give the same output bits,
+    and so does 6 tokens under AUTO (the single pass) and forced onto the
+    steps; a row-major layer cannot be forced onto the single pass."""
     cfg = workloads.CONFIGS["decode"]
     model = DeviceModel(cfg, threads=16)
     _, (xt, it, wt) = device_inputs(cfg)
     tiled = model.tiled_layer()
-    assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    assert tiled.path(cfg.M) == moe.MOE_LAYER_PATH_STEPS
+    assert tiled.path(6) == moe.MOE_LAYER_PATH_SINGLE_PASS
     steps = tiled.with_path(moe.MOE_LAYER_PATH_STEPS)
+    single = tiled.with_path(moe.MOE_LAYER_PATH_SINGLE_PASS)
     assert steps.path(cfg.M) == moe.MOE_LAYER_PATH_STEPS
-    log("decode layer: single pass against the forced steps path")
+    assert single.path(cfg.M) == moe.MOE_LAYER_PATH_SINGLE_PASS
+    log("decode layer: AUTO, the forced steps path and the forced single pass")
     a = tiled.forward(xt, it, wt)
     b = steps.forward(xt, it, wt)
+    c = single.forward(xt, it, wt)
+    x6, i6, w6 = xt[:6].contiguous(), it[:6].contiguous(), wt[:6].contiguous()
+    d = tiled.forward(x6, i6, w6)
+    e = steps.forward(x6, i6, w6)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    assert torch.equal(d.view(torch.int16), e.view(torch.int16))
+    assert torch.equal(d.view(torch.int16), a[:6].view(torch.int16))
     with pytest.raises(moe.MoeError):
         model.layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS).forward(xt, it, wt)
 

@@ -31,16 +31,17 @@ def _noalloc(moe, layer, xt, it, wt):
     return out
 
 
-@pytest.mark.parametrize("name,tiled,ms", [("verify", False, (128, 37)), ("decode", True, (8, 3)),
-                                           ("tiny", False, (4, 1))])
-def test_noalloc_equals_forward(moe, name, tiled, ms):
+@pytest.mark.parametrize("name,kind,ms", [("verify", "rowmajor", (128, 37)), ("decode", "tiled", (8, 3)),
+                                          ("decode", "single", (8, 5)), ("tiny", "rowmajor", (4, 1))])
+def test_noalloc_equals_forward(moe, name, kind, ms):
     cfg = workloads.CONFIGS[name]
     model = DeviceModel(cfg, threads=16)
-    layer = model.tiled_layer() if tiled else model.layer()
+    layer = {"rowmajor": model.layer(), "tiled": model.tiled_layer(),
+             "single": model.tiled_layer().with_path(moe.MOE_LAYER_PATH_SINGLE_PASS)}[kind]
     _, (xt, it, wt) = device_inputs(cfg)
     assert layer.workspace_bytes(cfg.M) <= moe._ffi.MOE_NOALLOC_WORKSPACE_BYTES
     for m in ms:  # two calls in a row, the second on fewer tokens
-        log(f"no-alloc layer: {name} tiled={tiled} M={m}")
+        log(f"no-alloc layer: {name} {kind} M={m} path {layer.path(m)}")
         x, i, w = xt[:m].contiguous(), it[:m].contiguous(), wt[:m].contiguous()
         a = _noalloc(moe, layer, x, i, w)
         b = layer.forward(x, i, w)
