@@ -147,6 +147,59 @@ __device__ __forceinline__ Pass locate_pass(const GroupedArgs& p, int j, int* s_
   return Pass{s_item[0], s_item[1], s_item[2], s_item[3]};
 }
 
+// The routed gate+up grid by XCD lane: column c = a * ng + g (a: index in the
+// active list, g: column group) belongs to lane c % 8, and lane l's units are
+// its columns in ascending order, each column's passes one after another.
+// Workgroup b of the routed part takes unit b / 8 of lane b % 8: workgroups
+// are dealt to the XCDs round-robin by id, so every pass of one (expert,
+// column group) runs on one XCD, next to the others in dispatch order, and
+// reads the expert's weights through one L2; a lane's units past its count
+// come after its real ones.  The thread whose run of active experts holds
+// unit k publishes (expert, first row, count, offset, column group); e = -1:
+// lane l has fewer units.  Contains barriers.
+struct LaneUnit {
+  int e, r0, count, offset, g;
+};
+template <int RP>
+__device__ __forceinline__ LaneUnit locate_lane_unit(const GroupedArgs& p, int lane, int k, int ng, int* s_item) {
+  constexpr int kPer = (MOE_MAX_EXPERTS + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  const int per = (p.cap + kThreads - 1) / kThreads;
+  const int a0 = min(p.cap, tid * per);
+  // the first column group of active expert a in this lane, and how many it has there
+  auto g_first = [&](int a) { return (lane - (a * ng) % 8 + 8) % 8; };
+  auto n_cols = [&](int a) {
+    const int g0 = g_first(a);
+    return g0 < ng ? (ng - 1 - g0) / 8 + 1 : 0;
+  };
+  int ex[kPer], cn[kPer], units = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) ex[i] = (i < per && a0 + i < p.cap) ? p.active_experts[a0 + i] : -1;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    cn[i] = ex[i] >= 0 ? p.expert_counts[ex[i]] : 0;
+    units += (cn[i] + RP - 1) / RP * n_cols(a0 + i);
+  }
+  if (tid == 0) s_item[0] = -1;
+  int base, unused_ex, total, unused_tot;
+  align_dev::block_scan2<kWaves>(units, 0, s_item + 8, s_item + 8 + kWaves, base, unused_ex, total, unused_tot);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int np = (cn[i] + RP - 1) / RP, u = np * n_cols(a0 + i);
+    if (k >= base && k < base + u) {
+      const int rel = k - base;
+      s_item[0] = ex[i];
+      s_item[1] = rel % np * RP;
+      s_item[2] = cn[i];
+      s_item[3] = p.expert_offsets[ex[i]];
+      s_item[4] = g_first(a0 + i) + 8 * (rel / np);
+    }
+    base += u;
+  }
+  __syncthreads();
+  return LaneUnit{s_item[0], s_item[1], s_item[2], s_item[3], s_item[4]};
+}
+
 // the FP8 block scale of chunk c from the lane-indexed registers
 __device__ __forceinline__ float block_scale(const float (&sr)[kSL], int c) {
   const float v = (kSL == 1 || c < 64) ? sr[0] : sr[kSL - 1];
@@ -219,10 +272,10 @@ __device__ __forceinline__ void gu_chunk_fp4(const u32x4 (&w)[2], const uint32_t
     gu_chunk_fp4_tiles<1>(w, sc, xb, q, r16, acc);
 }
 
-// Grid (1-D): the shared expert's (64-token pass, 64-column group) units, then
-// the routed (pass item, 64-column group) units with the column group fastest,
-// so the routing's real passes come first and the items past them (the grid
-// covers the most passes any routing of n slots can need) come last and exit.
+// Grid (1-D): the shared expert's (32-token pass, 64-column group) units, then
+// the routed (pass, 64-column group) units in XCD lanes (locate_lane_unit); the
+// grid covers 8 lanes of ceil(groups / 8) times the most passes any routing of
+// n slots can need, and the units past a lane's count exit.
 template <int FMT, bool ROWS, bool TILED>
 __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p) {
   constexpr bool FP4 = FMT == kFmtFP4;
@@ -230,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   constexpr int kRows = kGuRows, kShRows = kGuShRows, kRT = kRows / 16, kPieces = pieces_of<kRows>();
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [2][kRows][kXStride]
   __shared__ int s_src[kRows];
-  __shared__ int s_item[4 + 2 * kWaves];
+  __shared__ int s_item[8 + 2 * kWaves];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -242,14 +295,13 @@ __global__ __launch_bounds__(kThreads, 4) void wide_gate_up_kernel(GroupedArgs p
   int g, e = 0, r0 = 0, nr, row_base;
   if (routed) {
     const int r = (int)blockIdx.x - nshared;
-    const int ng = p.N / kGuCols;
-    const Pass ps = locate_pass<kRows>(p, r / ng, s_item);
-    if (ps.e < 0) return;
-    g = r % ng;
-    e = ps.e;
-    r0 = ps.r0;
-    nr = min(kRows, ps.count - r0);
-    row_base = ps.offset;
+    const LaneUnit u = locate_lane_unit<kRows>(p, r % 8, r / 8, p.N / kGuCols, s_item);
+    if (u.e < 0) return;
+    g = u.g;
+    e = u.e;
+    r0 = u.r0;
+    nr = min(kRows, u.count - r0);
+    row_base = u.offset;
   } else {
     g = (int)blockIdx.x % sng;
     row_base = (int)blockIdx.x / sng * kShRows;
@@ -778,7 +830,7 @@ hipError_t launch_gu(const GroupedArgs& a, hipStream_t s) {
   const int64_t items = max_items(a, kGuRows);
   b.sgroups = a.sw0 != nullptr ? (a.M + kGuShRows - 1) / kGuShRows : 0;
   const long long blocks =
-      (long long)b.sgroups * (a.sw0 != nullptr ? a.sN / kGuCols : 0) + (long long)items * (a.N / kGuCols);
+      (long long)b.sgroups * (a.sw0 != nullptr ? a.sN / kGuCols : 0) + (long long)items * ((a.N / kGuCols + 7) / 8 * 8);
   if (blocks <= 0) return hipSuccess;
   if (blocks > INT_MAX || items > INT_MAX) return hipErrorInvalidValue;
   b.items = (int)items;
