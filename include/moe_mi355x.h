@@ -166,7 +166,10 @@ size_t moe_align_workspace_bytes(int64_t M, int32_t top_k, int32_t E);
  * own bases from all blocks' counts.  The tables are bit-identical to
  * moe_align's (the same stable order; still no atomics), and the workspace
  * holds nothing after the call that the caller needs.  Below 4096 slots this
- * is moe_align (one workgroup).  Errors as for moe_align, plus MOE_ERR_NULL
+ * is moe_align (one workgroup), and so it is where E * G^2 (G blocks of 1024
+ * slots) passes 256 * 512^2: every scatter block reads all blocks' counts,
+ * which past that costs more than the three launches' single scan (measured
+ * on MI355X at 256 experts: faster up to 512 blocks, slower from 576).  Errors as for moe_align, plus MOE_ERR_NULL
  * (workspace NULL when needed), MOE_ERR_WORKSPACE (too small), MOE_ERR_SHAPE
  * (misaligned). */
 int moe_align_ws(const void* topk_ids, moe_index_dtype idt, int64_t M, int32_t top_k,

@@ -531,10 +531,17 @@ hipError_t launch_align(const void* ids, bool ids64, int n, int E, int BS, int m
 
 size_t align_workspace_bytes(int n, int E) { return (size_t)align_blocks(n) * E * sizeof(int32_t); }
 
+// The workspace form's scan+scatter blocks each read every block's counts
+// (E * G^2 loads in all), which outgrows the three launches' one scan: on
+// MI355X at E = 256 the workspace form is faster up to 512 blocks (31.9 against
+// 35.8 us) and slower from 576 (43.0 against 39.8 us).  Past that much work the
+// three launches run instead (the same tables).
+constexpr int64_t kAlignWsMaxWork = (int64_t)256 * 512 * 512;
+
 hipError_t launch_align_ws(const void* ids, bool ids64, int n, int E, int BS, int max_total, int cap, int32_t* ws,
                            const AlignOut& o, hipStream_t s) {
   const int G = align_blocks(n);
-  if (G == 0) return launch_align(ids, ids64, n, E, BS, max_total, cap, o, s);
+  if (G == 0 || (int64_t)E * G * G > kAlignWsMaxWork) return launch_align(ids, ids64, n, E, BS, max_total, cap, o, s);
   const int nbits = align_dev::id_bits(E);
   if (ids64)
     hipLaunchKernelGGL(align_count_blocks<int64_t>, dim3(G), dim3(kBlockThreads), 0, s,

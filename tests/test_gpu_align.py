@@ -73,6 +73,16 @@ def test_align_adversarial(case, ws):
     compare_tables(_gpu_align(ids, E, BS, ws=ws), oracle.align(ids, E, BS))
 
 
+def test_align_ws_past_its_cap():
+    """1024 experts over 257 blocks of 1024 slots: E * G^2 passes the workspace
+    form's limit, so moe_align_ws runs the three launches; its tables are the
+    oracle's (and at 256 blocks, the workspace form's own)."""
+    for rows in (32896, 32768):  # 257 and 256 blocks of 1024 slots at top-8
+        ids = np.random.default_rng(7).integers(-1, 1025, size=(rows, 8)).astype(np.int64)
+        log(f"align ws at its limit: {rows * 8} slots, 1024 experts")
+        compare_tables(_gpu_align(ids, 1024, 4, ws=True), oracle.align(ids, 1024, 4))
+
+
 def test_align_int64_ids_beyond_int32():
     """int64 ids that would alias a valid expert if truncated to 32 bits are dropped."""
     ids = np.array([[2 ** 32 + 1, 1], [3, -(2 ** 40)], [2 ** 33, 0]], dtype=np.int64)
