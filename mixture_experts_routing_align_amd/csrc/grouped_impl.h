@@ -70,6 +70,11 @@ constexpr int kStaged = 0, kResident = 1, kRoutedResident = 2;  // activation st
 __host__ __device__ constexpr size_t fused_align_lds(int E, int n) {
   return ((size_t)kWaves * E + E + (E + 1) + E + 2 * kWaves + 2 + n) * sizeof(int);
 }
+// LDS bytes of the MXFP4 scale area: per weight stream, the scale dwords (one
+// per row and 128-deep chunk) of ctw 64-row tiles at depth K
+__host__ __device__ constexpr size_t mx_scale_area(int streams, int ctw, int K) {
+  return (size_t)streams * ctw * kTileCols * (K / kKC) * sizeof(uint32_t);
+}
 
 // FMT: the weight format (kFmtBF16, kFmtFP8, kFmtFP4).
 // ROWS (FP8 only): one float32 scale per weight row, [E, N], instead of one per
@@ -234,6 +239,36 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   const int nv = (t_end - t_begin) * nch;  // (tile, chunk) steps of one pass
   const int kpad = TILED ? round_up(K, kKC) : K;
   const int kblocks = K / kFp8Block;
+  // MXFP4: the scale dwords of this workgroup's weight rows (its tiles' rows,
+  // consecutive rows of N) per stream, in LDS behind the alignment region;
+  // staged with the first activation rows, read where a chunk is multiplied
+  const int kd = K / kKC;
+  uint32_t* const s_sc = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(xs) + xs_bytes +
+                                                     (FUSED ? fused_align_lds(p.E, p.n) : 0));
+  auto stage_mx_scales = [&]() {
+    if constexpr (FP4) {
+      const int row0 = t_begin * kTileCols;
+      const int n = (min(N, t_end * kTileCols) - row0) * kd;
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(st == 0 ? B0 : B1) + (size_t)row0 * kd;
+        uint32_t* dst = s_sc + st * ctw * kTileCols * kd;
+        for (int b0 = 0; b0 < n; b0 += 8 * kThreads) {
+          uint32_t v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = b0 + u * kThreads + tid;
+            v[u] = i < n ? src[i] : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = b0 + u * kThreads + tid;
+            if (i < n) dst[i] = v[u];
+          }
+        }
+      }
+    }
+  };
 
   // a wave whose 16 columns lie past N reads the tile's first columns (valid
   // memory), multiplies nothing and stores nothing
@@ -255,18 +290,12 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
   int lt = t_begin, lc = 0;
   const char* lp0 = nullptr;
   const char* lp1 = nullptr;
-  const uint8_t* lb0 = nullptr;  // MXFP4: this lane's row of scale bytes
-  const uint8_t* lb1 = nullptr;
   auto set_load_tile = [&](int t) {
     bool on;
     const int wcol = wave_col(t, on);
     const size_t lo = lane_offset(wcol);
     lp0 = W0 + lo;
     if (GATE_UP) lp1 = W1 + lo;
-    if (FP4) {
-      lb0 = B0 + (size_t)(wcol + r16) * (K / kMxBlock);
-      if (GATE_UP) lb1 = B1 + (size_t)(wcol + r16) * (K / kMxBlock);
-    }
   };
   // unconditional loads of the cursor's chunk, then advance the cursor (past the
   // last step it stays on the last chunk, which is then loaded again): the
@@ -280,12 +309,12 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       const uint2 a0 = *reinterpret_cast<const uint2*>(lp0 + off);
       const uint2 a1 = *reinterpret_cast<const uint2*>(lp0 + off + hoff);
       wr[0][0] = uint4{a0.x, a0.y, a1.x, a1.y};
-      sr[0] = *reinterpret_cast<const uint32_t*>(lb0 + 4 * lc);
+      sr[0] = 0u;  // the scales come from LDS where the chunk is multiplied
       if (GATE_UP) {
         const uint2 b0 = *reinterpret_cast<const uint2*>(lp1 + off);
         const uint2 b1 = *reinterpret_cast<const uint2*>(lp1 + off + hoff);
         wr[NS - 1][0] = uint4{b0.x, b0.y, b1.x, b1.y};
-        sr[NS - 1] = *reinterpret_cast<const uint32_t*>(lb1 + 4 * lc);
+        sr[NS - 1] = 0u;
       }
     }
 #pragma unroll
@@ -530,7 +559,18 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
     bool con;
     int cwcol = wave_col(ct, con);
     auto step = [&](const uint4 (&wc)[NS][WL], const uint32_t (&scb)[NS], int slot, int kb) {
-      if (con) compute(wc, scb, slot, kb, cc);
+      if (con) {
+        if constexpr (FP4) {
+          // the lane's row of the tile: its scale dword of chunk cc, per stream
+          const int row = (ct - t_begin) * kTileCols + wave * kWaveCols + r16;
+          uint32_t scl[NS];
+#pragma unroll
+          for (int st = 0; st < NS; ++st) scl[st] = s_sc[(st * ctw * kTileCols + row) * kd + cc];
+          compute(wc, scl, slot, kb, cc);
+        } else {
+          compute(wc, scb, slot, kb, cc);
+        }
+      }
       if (cc + 1 < nch) {
         ++cc;
       } else {
@@ -544,6 +584,7 @@ __global__ __launch_bounds__(kThreads) void grouped_kernel(GroupedArgs p, int ro
       }
     };
 
+    stage_mx_scales();  // visible after the barrier that ends the row staging
     if (resident) {
       // every row of this pass, the whole depth
       const int total = nr * pieces;
@@ -626,9 +667,18 @@ inline int device_cus() {
 template <int FMT, bool ROWS, bool GATE_UP, int RT, int RES, bool TILED, bool FUSED, typename IdT>
 hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int tiles, hipStream_t s) {
   auto kern = grouped_kernel<FMT, ROWS, GATE_UP, RT, RES, TILED, FUSED, IdT>;
-  const size_t lds = xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0);
+  // MXFP4: the scale area for ctw tiles at the deeper of the routed and shared depths
+  const int kmax = (a.sw0 != nullptr && a.sK > a.K) ? a.sK : a.K;
+  auto lds_for = [&](int ctw_) {
+    return xs_bytes + (FUSED ? fused_align_lds(a.E, a.n) : 0) +
+           (FMT == kFmtFP4 ? mx_scale_area(GATE_UP ? 2 : 1, ctw_, kmax) : 0);
+  };
+  constexpr size_t kLdsMax = 160 * 1024;
+  const int max_ctw = lds_for(kMaxTilesPerGroup) <= kLdsMax ? kMaxTilesPerGroup : 1;
+  size_t lds = lds_for(1);
+  if (lds > kLdsMax) return hipErrorInvalidValue;  // MXFP4 scales of a 64-row tile past the LDS (depth > 16k)
   static std::atomic<size_t> allowed[kMaxCachedDevices];
-  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds, allowed);
+  hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kern), lds_for(max_ctw), allowed);
   if (e != hipSuccess) return e;
   // column tiles per workgroup: the fewest that let every workgroup of the
   // worst case (every item busy) be resident at once, but at most
@@ -642,7 +692,8 @@ hipError_t launch_one(const GroupedArgs& a, int rowcap, size_t xs_bytes, int til
   // (the shared and routed items may have different column counts: `tiles` is the larger)
   const int items = a.sgroups + a.items;
   int ctw = 1;
-  while (ctw < tiles && ctw < kMaxTilesPerGroup && (long long)items * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
+  while (ctw < tiles && ctw < max_ctw && (long long)items * ((tiles + ctw - 1) / ctw) > slots) ++ctw;
+  lds = lds_for(ctw);
   const long long groups_r = ((a.N + kTileCols - 1) / kTileCols + ctw - 1) / ctw;
   const long long groups_s = a.sgroups ? ((a.sN + kTileCols - 1) / kTileCols + ctw - 1) / ctw : 0;
   const long long blocks = a.sgroups * groups_s + a.items * groups_r;
@@ -666,6 +717,8 @@ template <int FMT, bool ROWS, bool GATE_UP, int RT, bool TILED>
 hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   constexpr int NX = GATE_UP ? 1 : 2;
   const int kmax = (a.sw0 != nullptr && a.sK > a.K) ? a.sK : a.K;
+  // (MXFP4: the workgroup's scale area counts against the resident budget)
+  const size_t mx = FMT == kFmtFP4 ? mx_scale_area(GATE_UP ? 2 : 1, kMaxTilesPerGroup, kmax) : 0;
   const size_t resident = (size_t)NX * rowcap * (kmax + kPad) * 2;
   const size_t routed_resident = (size_t)NX * rowcap * (a.K + kPad) * 2;
   const size_t chunked = (size_t)2 * NX * rowcap * (kKC + kPad) * 2;
@@ -677,11 +730,11 @@ hipError_t launch_rt(const GroupedArgs& a, int rowcap, hipStream_t s) {
   // ceil(count / rowcap) <= (n + active * (rowcap - 1)) / rowcap
   const int64_t n = (int64_t)a.M * a.top_k;
   b.items = (int)((n + (int64_t)a.cap * (rowcap - 1)) / rowcap);
-  if (resident <= kResidentLdsBudget)
+  if (resident + mx <= kResidentLdsBudget)
     return launch_fused_or_not<FMT, ROWS, GATE_UP, RT, kResident, TILED>(b, rowcap, resident, tiles, s);
   // only the shared expert's depth is too deep: its items stage 128 deep at a
   // time while the routed items keep their rows resident
-  if (routed_resident <= kResidentLdsBudget)
+  if (routed_resident + mx <= kResidentLdsBudget)
     return launch_fused_or_not<FMT, ROWS, GATE_UP, RT, kRoutedResident, TILED>(
         b, rowcap, std::max(routed_resident, chunked), tiles, s);
   return launch_fused_or_not<FMT, ROWS, GATE_UP, RT, kStaged, TILED>(b, rowcap, chunked, tiles, s);
