@@ -43,6 +43,12 @@ CONFIGS = {
     # half full), routed down depth 128 (2 halves, padded to 4), a shared
     # expert of 384 (6 halves) over 40 tokens (passes of 32 + 8)
     "mx_shared": workloads.MoeConfig("wide_mx_shared", 40, 384, 8, 2, 128, 384, 16, "mxfp4", "softmax", seed=65),
+    # intermediate 1152: 18 gate+up column groups, so the XCD lanes hold 2 or 3
+    # columns of an expert; down depth 9 chunks (18 halves, padded to 20)
+    "many_groups": workloads.MoeConfig("wide_many_groups", 64, 256, 16, 4, 1152, 0, 16, "fp8", "softmax_bias",
+                                       bias_std=2.0, seed=67),
+    "mx_many_groups": workloads.MoeConfig("wide_mx_many_groups", 64, 256, 16, 4, 1152, 0, 16, "mxfp4",
+                                          "softmax_bias", bias_std=2.0, seed=68),
 }
 
 _MODELS = {}
