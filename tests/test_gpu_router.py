@@ -65,7 +65,12 @@ def test_router_configs(name):
     _check(workloads.x_bf16(cfg), workloads.router_weight_bf16(cfg), cfg.top_k)
 
 
-@pytest.mark.parametrize("M,H,E,k", [(37, 104, 70, 5), (1, 8, 1, 1), (17, 520, 1024, 64), (33, 64, 16, 16)])
+# (the selection holds ceil(E / 64), rounded up to a power of two, logits per
+# lane: 1 for E = 1, 16, 48; 2 for 70; 4 for 256; 8 for 300; 16 for 1024;
+# (20, 2040, 48, 6): 16 rounds of H, the last one ragged; (5, 1000, 256, 8): 8
+# rounds, the last ragged, over 16 expert tiles)
+@pytest.mark.parametrize("M,H,E,k", [(37, 104, 70, 5), (1, 8, 1, 1), (17, 520, 1024, 64), (33, 64, 16, 16),
+                                     (20, 2040, 48, 6), (5, 1000, 256, 8), (9, 256, 300, 10)])
 def test_router_odd_shapes(M, H, E, k):
     cfg = workloads.MoeConfig("router_odd", M, H, E, k, 0, 0, 16, "bf16", "softmax", seed=M * 1000 + E)
     log(f"router odd shape M={M} H={H} E={E} top_k={k}")
@@ -141,3 +146,4 @@ def test_router_row_invariance_and_graph_replay():
         e_ids, e_w, e_l = moe.moe_router_topk(x[start:start + 16].contiguous(), w, cfg.top_k)
         torch.cuda.synchronize()
         assert torch.equal(g_ids, e_ids) and torch.equal(g_w, e_w) and torch.equal(g_l, e_l), start
+
