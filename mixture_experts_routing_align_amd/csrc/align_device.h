@@ -76,21 +76,26 @@ __device__ void count_pass(const IdT* __restrict__ ids, int n, int E, int nbits,
   __syncthreads();
 }
 
+// Inclusive scan over the wave's lanes on the DPP lane crossbar (no LDS round
+// trip): shifts by 1, 2, 4 and 8 within each row of 16 lanes (a lane with no
+// source adds 0), then the broadcasts of lane 15 into rows 1 and 3 and of lane
+// 31 into rows 2 and 3 carry the row totals across.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive scan of (a, b) over the block's threads in thread order; also
 // returns the totals.  Uses wa/wb [NW] of LDS; contains barriers.
 template <int NW>
 __device__ void block_scan2(int a, int b, int* wa, int* wb, int& ex_a, int& ex_b, int& tot_a, int& tot_b) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int ta = __shfl_up(ia, d, 64);
-    const int tb = __shfl_up(ib, d, 64);
-    if (lane >= d) {
-      ia += ta;
-      ib += tb;
-    }
-  }
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   __syncthreads();  // wa/wb free
   if (lane == 63) {
     wa[w] = ia;
@@ -133,11 +138,15 @@ __device__ void expert_scan(const ExpertLds& s, int E, int BS) {
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int sum_pad = 0, sum_act = 0;
   for (int e = e0; e < e1; ++e) {
+    // every wave's count requested before any base is stored
+    int c[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) c[k] = s.cnt[k * E + e];
     int run = 0;
+#pragma unroll
     for (int k = 0; k < NW; ++k) {
-      const int c = s.cnt[k * E + e];
       s.cnt[k * E + e] = run;
-      run += c;
+      run += c[k];
     }
     s.count[e] = run;
     sum_pad += (run + BS - 1) / BS * BS;
