@@ -42,7 +42,7 @@ using namespace mma;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 16;                            // experts (and tokens) per wave tile
-constexpr int kLanesMax = MOE_MAX_EXPERTS / 64;      // logits per lane in the selection
+constexpr int kLanesMax = MOE_MAX_EXPERTS / 64;      // most logits per lane in the selection
 constexpr int kKWaves = 16;                          // waves sharing one logits tile, split over H
 
 // grid (ceil(E / 16), ceil(M / 16)) x kKWaves waves: every wave of a
